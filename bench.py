@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Radial attention forward pass on one MI355X: effective TFLOP/s on active blocks.
+
+    python bench.py [--steps K] [--warmup W] [--workload wan|hunyuan|long4x|small|tiny]
+
+A step is one call of the block-sparse forward kernel over the whole workload
+(every batch, head and query block), with Q/K/V already resident in HBM. The static mask
+is built once before timing, and its host build time is reported on its own. After W
+untimed warm-up steps, exactly K steps are timed with HIP events on the stream the
+kernel runs on, between device synchronisations. The same kernel with the all-active
+mask gives the dense baseline. The CPU oracle is timed beside it on a bounded sample.
+Rank 0 prints one JSON line.
+
+Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
+(batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_radial_amd", "csrc", "radial_attn_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes(workload_name: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters.
+
+    Null when no counters exist for this workload or the kernel source changed since.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256") != kernel_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall
+
+
+def cpu_baseline(wl, q, k, v, mask, seconds: float):
+    """Time the fp64 CPU oracle on head 0, query blocks in a seeded order, until about
+    `seconds` of work has run. Report the same active-tile flop rate as the GPU."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import radial_oracle as ro
+
+    t0 = time.perf_counter()
+    ro.block_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+    mask_s = time.perf_counter() - t0
+
+    rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
+    qh, kh, vh = (x[0, 0].double().cpu().numpy() for x in (q, k, v))
+    order = np.random.default_rng(0).permutation(wl.nb)
+    done = []
+    t0 = time.perf_counter()
+    for qb in order:
+        ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)])
+        done.append(int(qb))
+        if time.perf_counter() - t0 >= seconds:
+            break
+    elapsed = time.perf_counter() - t0
+    tiles = int(sum(rp[b + 1] - rp[b] for b in done))
+    flops = 4 * wl.head_dim * 128 * 128 * tiles
+    threads = [d.get("num_threads", 0) for d in threadpool_info()
+               if d.get("user_api") == "blas"]
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": max(threads) if threads else 1,
+        "kind": "oracle",
+        "sample": f"head 0 of {wl.heads}, {len(done)} of {wl.nb} query blocks "
+                  f"({tiles} active tiles) in {elapsed:.1f} s, fp64 numpy; "
+                  f"oracle block-mask build {mask_s:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_radial_amd as radial
+    from block_sparse_attention_radial_amd.inputs import WORKLOADS, draw_qkv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    radial.lib()
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+
+    t0 = time.perf_counter()
+    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+    mask_ms = (time.perf_counter() - t0) * 1e3
+    mdev = mask.to(dev)
+    q, k, v = draw_qkv(wl, seed=0, device=dev)
+    o = torch.empty_like(q)
+    bh = wl.batch * wl.heads
+    flops = 4 * wl.head_dim * 128 * 128 * mask.nnz * bh
+    log(f"workload {wl.name}: n={wl.n} nb={mask.nb} nnz={mask.nnz} "
+        f"({mask.nnz / mask.nb ** 2:.3f} of blocks), mask build {mask_ms:.2f} ms")
+
+    ms, wall = time_launches(lambda: radial.attn_fwd(q, k, v, mdev, out=o),
+                             args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"sparse: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
+
+    dense = None
+    if not args.no_dense:
+        dmask = radial.dense_mask(wl.n, device=dev)
+        dsteps = max(3, args.steps // 2)
+        dms, _ = time_launches(lambda: radial.attn_fwd(q, k, v, dmask, out=o),
+                               dsteps, min(args.warmup, 2))
+        dflops = 4 * wl.head_dim * 128 * 128 * dmask.nnz * bh
+        dense = {"ms": dms, "tflops": dflops / (dms * 1e-3) / 1e12, "steps": dsteps,
+                 "speedup": dms / ms, "ideal_speedup": dmask.nnz / mask.nnz}
+        log(f"dense:  {dms:.3f} ms/step, {dense['tflops']:.1f} TFLOP/s; "
+            f"speedup {dense['speedup']:.2f}x (block-count ceiling {dense['ideal_speedup']:.2f}x)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
+
+    traffic = traffic_bytes(wl.name)
+    line = {
+        "metric": "active-block attention TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 1 GPU",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v in bf16 at the workload's shape",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "heads": wl.heads,
+            "head_dim": wl.head_dim, "frames": wl.frames,
+            "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
+            "block": 128, "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2,
+        },
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "speedup_vs_dense": None if dense is None else round(dense["speedup"], 3),
+        "dense": None if dense is None else {k_: round(v_, 4) for k_, v_ in dense.items()},
+        "mask_build_ms": round(mask_ms, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

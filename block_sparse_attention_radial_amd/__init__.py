@@ -1,0 +1,14 @@
+"""Radial Attention forward pass for MI355X (gfx950).
+
+    from block_sparse_attention_radial_amd import build_mask, attn_fwd
+    mask = build_mask(frames, tokens_per_frame, w0).to("cuda")
+    o = attn_fwd(q, k, v, mask)            # q, k, v: bf16 [B, H, n, D] on the GPU
+
+The mask builder and the kernels live in libradial.so (C ABI: include/radial_attn.h),
+built in-tree by `python -m block_sparse_attention_radial_amd.build`.
+"""
+from .api import (BLOCK, Mask, RadialError, attn_fwd, build_mask, dense_mask, error_string,
+                  lib, mask_dims)
+
+__all__ = ["BLOCK", "Mask", "RadialError", "attn_fwd", "build_mask", "dense_mask",
+           "error_string", "lib", "mask_dims"]

@@ -1,0 +1,170 @@
+"""Python binding of libradial.so (ctypes). Argument marshalling only.
+
+Every step of the forward pass runs in the library. torch supplies device memory and
+the current HIP stream. If the library has not been built, the calls raise: there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+BLOCK = 128
+
+RADIAL_OK = 0
+_ERRORS = {
+    -1: "INVALID_ARG", -2: "UNSUPPORTED_HEAD_DIM", -3: "CAPACITY", -4: "SHAPE_MISMATCH",
+    -5: "MISALIGNED", -6: "TOO_LARGE", -7: "HIP",
+}
+
+# Every symbol that include/radial_attn.h declares, with its ctypes signature.
+_SIGNATURES = {
+    "radial_mask_dims": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "radial_build_mask": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
+    "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
+        ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 4 + [ctypes.c_int64] * 3
+        + [ctypes.c_void_p]),
+    "radial_error_string": (ctypes.c_char_p, [ctypes.c_int32]),
+}
+
+_lib = None
+
+
+class RadialError(RuntimeError):
+    """A non-zero return code from libradial.so."""
+
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {_ERRORS.get(code, code)} ({error_string(code)})")
+
+
+def library_path() -> str:
+    return os.environ.get("RADIAL_LIB", LIB_PATH)
+
+
+def lib():
+    """The loaded libradial.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with "
+                "`python -m block_sparse_attention_radial_amd.build` (or __graft_entry__.build())")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def error_string(code: int) -> str:
+    return lib().radial_error_string(code).decode()
+
+
+def _check(fn: str, code: int):
+    if code != RADIAL_OK:
+        raise RadialError(fn, code)
+
+
+@dataclass
+class Mask:
+    """Block mask in compressed-row form: int32 row_ptr[nb + 1], col_idx[nnz]."""
+
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    frames: int
+    tokens_per_frame: int
+    w0: int
+
+    @property
+    def n(self) -> int:
+        return self.frames * self.tokens_per_frame
+
+    @property
+    def nb(self) -> int:
+        return self.row_ptr.numel() - 1
+
+    @property
+    def nnz(self) -> int:
+        return self.col_idx.numel()
+
+    @property
+    def device(self) -> torch.device:
+        return self.row_ptr.device
+
+    def to(self, device) -> "Mask":
+        return Mask(self.row_ptr.to(device), self.col_idx.to(device), self.frames,
+                    self.tokens_per_frame, self.w0)
+
+
+def mask_dims(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK):
+    nb, nnz = ctypes.c_int32(), ctypes.c_int64()
+    _check("radial_mask_dims", lib().radial_mask_dims(
+        frames, tokens_per_frame, w0, block, ctypes.byref(nb), ctypes.byref(nnz)))
+    return nb.value, nnz.value
+
+
+def build_mask(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK) -> Mask:
+    """The static radial block mask for a frames x tokens_per_frame video (host tensors)."""
+    nb, nnz = mask_dims(frames, tokens_per_frame, w0, block)
+    row_ptr = torch.empty(nb + 1, dtype=torch.int32)
+    col_idx = torch.empty(max(nnz, 1), dtype=torch.int32)
+    _check("radial_build_mask", lib().radial_build_mask(
+        frames, tokens_per_frame, w0, block, row_ptr.data_ptr(), col_idx.data_ptr(), nnz))
+    return Mask(row_ptr, col_idx[:nnz], frames, tokens_per_frame, w0)
+
+
+def dense_mask(seqlen: int, device="cpu") -> Mask:
+    """All-active CSR (every query block sees every key block): the dense baseline."""
+    nb = (seqlen + BLOCK - 1) // BLOCK
+    row_ptr = torch.arange(0, nb * nb + 1, nb, dtype=torch.int32, device=device)
+    col_idx = torch.arange(nb, dtype=torch.int32, device=device).repeat(nb)
+    return Mask(row_ptr, col_idx, 1, seqlen, 2**31 - 1)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
+             scale: float | None = None, out: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None) -> torch.Tensor:
+    """Radial attention forward on q, k, v of shape [B, H, n, D] (bf16, on the GPU).
+
+    Any layout with a contiguous last axis and strides shared by q, k, v and out works,
+    e.g. a [B, n, H, D] buffer viewed as [B, H, n, D]. `lse` (optional, fp32 [B, H, n],
+    contiguous) receives the natural-log log-sum-exp of every row. The call is
+    asynchronous on torch's current stream.
+    """
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share the shape [B, H, n, D]")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if mask.row_ptr.device != q.device or mask.col_idx.device != q.device:
+        raise ValueError("the mask must be on the same device as q (Mask.to(device))")
+    if q.stride() != k.stride() or q.stride() != v.stride() or q.stride(-1) != 1:
+        raise ValueError("q, k, v must share strides with a contiguous last axis")
+    B, H, n, D = q.shape
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.stride() != q.stride() or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape, strides and dtype")
+    if lse is not None and (lse.shape != (B, H, n) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor on q's device")
+    if scale is None:
+        scale = D ** -0.5
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check("radial_attn_fwd", lib().radial_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(),
+        mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb, float(scale),
+        B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
+    return out

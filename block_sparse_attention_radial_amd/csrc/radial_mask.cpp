@@ -1,0 +1,136 @@
+// Host-side block-mask builder for Radial Attention.
+//
+// The rule, after "Radial Attention: A Breakthrough in Efficient Long Video Generation",
+// How Radial Attention Works (the window shrinks with temporal distance, density halves
+// when the distance doubles, and the mask is applied in 128x128 blocks), and the
+// radial-attention-video SKILL.md page, Step 1 (frame-major token layout):
+//
+//     key allowed  <=>  |s_q - s_k| * 2^floor(log2(|f_q - f_k| + 1)) < W0
+//
+// The builder never looks at single elements. For a query frame f_q and a key frame
+// f_k at band k = floor(log2(|f_q - f_k| + 1)), the largest allowed spatial offset is
+// r_k = floor((W0 - 1) / 2^k), because |ds| * 2^k < W0 <=> |ds| * 2^k <= W0 - 1
+// (integers). A run of query positions [a, b] inside one frame therefore reaches the
+// key positions [a - r_k, b + r_k], clipped to [0, S). That range is contiguous, so it
+// maps to a contiguous range of key blocks. A query block is cut into at most
+// ceil(128 / S) + 1 frame pieces, each piece is swept over every key frame, and the
+// touched key blocks are collected. Cost is O(nb * (128 / S + 2) * F) plus the blocks
+// marked.
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/radial_attn.h"
+
+namespace {
+
+// floor(log2(x)) for x >= 1.
+inline int floor_log2(uint32_t x) { return 31 - __builtin_clz(x); }
+
+int32_t check_args(int32_t frames, int32_t tokens_per_frame, int32_t w0, int32_t block) {
+  if (frames <= 0 || tokens_per_frame <= 0 || w0 <= 0) return RADIAL_ERR_INVALID_ARG;
+  if (block != RADIAL_BLOCK) return RADIAL_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(frames) * tokens_per_frame > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  return RADIAL_OK;
+}
+
+// Calls emit(row, ascending_key_blocks) for every query block row, in order.
+template <typename Emit>
+void sweep(int32_t frames, int32_t S, int32_t w0, Emit&& emit) {
+  const int64_t n = static_cast<int64_t>(frames) * S;
+  const int32_t nb = static_cast<int32_t>((n + RADIAL_BLOCK - 1) / RADIAL_BLOCK);
+  // The radius at each frame distance, tabulated once.
+  std::vector<int32_t> radius(frames);
+  for (int32_t d = 0; d < frames; ++d)
+    radius[d] = (w0 - 1) >> floor_log2(static_cast<uint32_t>(d) + 1u);
+  std::vector<uint8_t> hit(nb, 0);
+  std::vector<int32_t> cols;
+  cols.reserve(nb);
+  for (int32_t row = 0; row < nb; ++row) {
+    const int64_t t0 = static_cast<int64_t>(row) * RADIAL_BLOCK;
+    const int64_t t1 = std::min<int64_t>(n, t0 + RADIAL_BLOCK);  // exclusive
+    int32_t lo_blk = nb, hi_blk = -1;
+    for (int64_t t = t0; t < t1;) {
+      const int32_t fq = static_cast<int32_t>(t / S);
+      const int64_t piece_end = std::min<int64_t>(t1, static_cast<int64_t>(fq + 1) * S);
+      const int32_t a = static_cast<int32_t>(t - static_cast<int64_t>(fq) * S);
+      const int32_t b = static_cast<int32_t>(piece_end - 1 - static_cast<int64_t>(fq) * S);
+      for (int32_t fk = 0; fk < frames; ++fk) {
+        const int32_t r = radius[fq > fk ? fq - fk : fk - fq];
+        const int64_t s_lo = std::max<int64_t>(0, static_cast<int64_t>(a) - r);
+        const int64_t s_hi = std::min<int64_t>(S - 1, static_cast<int64_t>(b) + r);
+        const int64_t base = static_cast<int64_t>(fk) * S;
+        const int32_t blk_lo = static_cast<int32_t>((base + s_lo) / RADIAL_BLOCK);
+        const int32_t blk_hi = static_cast<int32_t>((base + s_hi) / RADIAL_BLOCK);
+        for (int32_t kb = blk_lo; kb <= blk_hi; ++kb) hit[kb] = 1;
+        lo_blk = std::min(lo_blk, blk_lo);
+        hi_blk = std::max(hi_blk, blk_hi);
+      }
+      t = piece_end;
+    }
+    cols.clear();
+    for (int32_t kb = lo_blk; kb <= hi_blk; ++kb) {
+      if (hit[kb]) {
+        cols.push_back(kb);
+        hit[kb] = 0;
+      }
+    }
+    emit(row, cols);
+  }
+}
+
+}  // namespace
+
+extern "C" int32_t radial_mask_dims(int32_t frames, int32_t tokens_per_frame, int32_t w0,
+                                    int32_t block, int32_t* nb_out, int64_t* nnz_out) {
+  if (!nb_out || !nnz_out) return RADIAL_ERR_INVALID_ARG;
+  const int32_t st = check_args(frames, tokens_per_frame, w0, block);
+  if (st != RADIAL_OK) return st;
+  int64_t nnz = 0;
+  int32_t rows = 0;
+  sweep(frames, tokens_per_frame, w0, [&](int32_t, const std::vector<int32_t>& cols) {
+    nnz += static_cast<int64_t>(cols.size());
+    ++rows;
+  });
+  if (nnz > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  *nb_out = rows;
+  *nnz_out = nnz;
+  return RADIAL_OK;
+}
+
+extern "C" int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0,
+                                     int32_t block, int32_t* row_ptr, int32_t* col_idx,
+                                     int64_t nnz_capacity) {
+  if (!row_ptr || !col_idx || nnz_capacity < 0) return RADIAL_ERR_INVALID_ARG;
+  const int32_t st = check_args(frames, tokens_per_frame, w0, block);
+  if (st != RADIAL_OK) return st;
+  int64_t nnz = 0;
+  bool overflow = false;
+  row_ptr[0] = 0;
+  sweep(frames, tokens_per_frame, w0, [&](int32_t row, const std::vector<int32_t>& cols) {
+    const int64_t end = nnz + static_cast<int64_t>(cols.size());
+    if (end > nnz_capacity || end > INT32_MAX) overflow = true;
+    if (!overflow) std::memcpy(col_idx + nnz, cols.data(), cols.size() * sizeof(int32_t));
+    nnz = end;
+    row_ptr[row + 1] = static_cast<int32_t>(std::min<int64_t>(nnz, INT32_MAX));
+  });
+  if (nnz > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  if (overflow) return RADIAL_ERR_CAPACITY;
+  return RADIAL_OK;
+}
+
+extern "C" const char* radial_error_string(int32_t code) {
+  switch (code) {
+    case RADIAL_OK: return "ok";
+    case RADIAL_ERR_INVALID_ARG: return "invalid argument";
+    case RADIAL_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head_dim (64 or 128)";
+    case RADIAL_ERR_CAPACITY: return "col_idx capacity smaller than the active-block count";
+    case RADIAL_ERR_SHAPE_MISMATCH: return "nb does not equal ceil(seqlen / 128)";
+    case RADIAL_ERR_MISALIGNED: return "pointer or stride not 16-byte aligned";
+    case RADIAL_ERR_TOO_LARGE: return "size past the int32 index range";
+    case RADIAL_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown error code";
+  }
+}

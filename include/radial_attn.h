@@ -1,0 +1,122 @@
+/*
+ * radial_attn.h — C ABI of libradial.so: Radial Attention forward pass on gfx950.
+ *
+ * The operation, after these pages:
+ *  - "Radial Attention: O(n log n) Sparse Attention with Energy Decay for Long Video
+ *    Generation" (paper summary page), Outline. Softmax attention over a video token
+ *    sequence, where each query attends to spatially close keys and the window narrows
+ *    as the temporal distance grows.
+ *  - "Radial Attention: A Breakthrough in Efficient Long Video Generation", How Radial
+ *    Attention Works. The mask is static, compute density halves when temporal distance
+ *    doubles, and the mask is applied in 128x128 blocks.
+ *  - The radial-attention-video SKILL.md page, Step 1 and Step 2. Tokens are frame-major
+ *    (frame = t / S, spatial = t % S), masked scores are -inf before the softmax, and
+ *    out = softmax(Q K^T * scale) V with one mask for every batch and head.
+ *
+ * The rule this library implements, with W0 the base spatial window:
+ *     key k allowed for query q  <=>  |s_q - s_k| * 2^floor(log2(|f_q - f_k| + 1)) < W0
+ * A 128x128 block is active iff it contains at least one allowed (query, key) pair.
+ * Every real key of an active block takes part in that query block's softmax.
+ *
+ * Conventions for every call:
+ *  - The return value is 0 (RADIAL_OK) on success or a negative RADIAL_ERR_* code.
+ *    No call aborts, prints, or leaves global state behind.
+ *  - All buffers are owned by the caller. The library allocates no memory.
+ *  - Every check that can fail is done on the host before any HIP call.
+ */
+#ifndef RADIAL_ATTN_H
+#define RADIAL_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  RADIAL_OK = 0,
+  RADIAL_ERR_INVALID_ARG = -1,          /* a size <= 0, block != 128, null pointer, bad scale */
+  RADIAL_ERR_UNSUPPORTED_HEAD_DIM = -2, /* head_dim other than 64 or 128 */
+  RADIAL_ERR_CAPACITY = -3,             /* nnz_capacity smaller than the mask needs */
+  RADIAL_ERR_SHAPE_MISMATCH = -4,       /* nb != ceil(seqlen / 128) */
+  RADIAL_ERR_MISALIGNED = -5,           /* pointer or stride not a multiple of 16 bytes */
+  RADIAL_ERR_TOO_LARGE = -6,            /* a count past the int32 index range */
+  RADIAL_ERR_HIP = -7                   /* the HIP runtime reported an error at launch */
+};
+
+/* Block size of the mask in tokens, on both axes. */
+#define RADIAL_BLOCK 128
+
+/*
+ * radial_mask_dims — sizes of the block mask for a video of `frames` x `tokens_per_frame`
+ * tokens with base window `w0`. It writes the number of block rows
+ * nb = ceil(frames * tokens_per_frame / 128) to *nb_out, and the number of active
+ * blocks to *nnz_out. It runs on the host only.
+ *
+ * Errors: INVALID_ARG if frames, tokens_per_frame or w0 is <= 0, if block != 128, or if
+ * an output pointer is null. TOO_LARGE if the sequence length or the active-block count
+ * does not fit in int32.
+ */
+int32_t radial_mask_dims(int32_t frames, int32_t tokens_per_frame, int32_t w0, int32_t block,
+                         int32_t* nb_out, int64_t* nnz_out);
+
+/*
+ * radial_build_mask — fill the block mask in compressed-row form. This is host code and
+ * is deterministic.
+ *
+ * row_ptr: caller-owned host array of nb + 1 int32. row_ptr[0] = 0, and row r's active key
+ *          blocks are col_idx[row_ptr[r] .. row_ptr[r+1]).
+ * col_idx: caller-owned host array of at least nnz_capacity int32. Within each row the
+ *          indices are strictly ascending, so a mask has exactly one such form.
+ * Arguments and errors are as for radial_mask_dims, plus CAPACITY when nnz_capacity is
+ * smaller than the active-block count. On any error the arrays are left unspecified.
+ *
+ * The mask is static for given (frames, tokens_per_frame, w0). Build it once, copy it to
+ * the device, and reuse it for every batch, head and call.
+ */
+int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, int32_t block,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t nnz_capacity);
+
+/*
+ * radial_attn_fwd — block-sparse softmax attention forward pass on the GPU. The call is
+ * asynchronous on `stream`.
+ *
+ * q, k, v, o: device pointers to bf16 tensors of logical shape [batch, heads, seqlen,
+ *             head_dim]. Element (b, h, t, d) is at b*stride_b + h*stride_h +
+ *             t*stride_s + d, with strides counted in elements and shared by all four
+ *             tensors. The head_dim axis must be contiguous. [B,H,n,D] and [B,n,H,D]
+ *             both work without a copy. o is written for rows t < seqlen only.
+ * lse:        optional device pointer (may be null) to float32 [batch, heads, seqlen],
+ *             contiguous. It receives the natural-log log-sum-exp of each row's scaled
+ *             scores over that row's key set.
+ * row_ptr, col_idx: the block mask from radial_build_mask, copied to device memory.
+ *             nb = ceil(seqlen / 128). Column indices outside [0, nb) are skipped.
+ *             Every row must have at least one active block, which is always true of a
+ *             radial mask (the diagonal is allowed).
+ * scale:      softmax scale, finite and >= 0 (head_dim^-0.5 is the usual value).
+ * stream:     a hipStream_t, or null for the default stream.
+ *
+ * Keys at or past seqlen in the last block are excluded. Rows at or past seqlen are
+ * never read or written. Accumulation is fp32, and probabilities are rounded to bf16
+ * before the P*V product. Buffers must stay alive and unmodified until the stream work
+ * has finished.
+ *
+ * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim),
+ * UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH, MISALIGNED (q/k/v/o not 16-byte aligned, or a
+ * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*nb workgroups above
+ * 2^31 - 1), HIP (launch failure).
+ */
+int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,
+                        float scale, int32_t batch, int32_t heads, int32_t seqlen,
+                        int32_t head_dim, int64_t stride_b, int64_t stride_h,
+                        int64_t stride_s, void* stream);
+
+/* radial_error_string — a static, human-readable text for a return code. */
+const char* radial_error_string(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RADIAL_ATTN_H */

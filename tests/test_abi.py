@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: exported symbols, error codes, argument validation.
+
+radial_attn_fwd validates everything on the host before its first HIP call, so every
+error path is reachable here with fake (never dereferenced) pointer values.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_radial_amd as radial
+from block_sparse_attention_radial_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "radial_attn.h")
+
+OK, INVALID, HEADDIM, CAPACITY, SHAPE, MISALIGNED, TOO_LARGE, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(radial_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted(
+        ["radial_mask_dims", "radial_build_mask", "radial_attn_fwd", "radial_error_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = radial.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", api.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (radial_\w+)", out))
+    assert set(declared_symbols()) <= exported
+    assert set(api._SIGNATURES) == set(declared_symbols())
+
+
+def test_error_strings():
+    lib = radial.lib()
+    for code in (OK, INVALID, HEADDIM, CAPACITY, SHAPE, MISALIGNED, TOO_LARGE, HIP):
+        s = lib.radial_error_string(code).decode()
+        assert s and s != "unknown error code"
+    assert lib.radial_error_string(12345).decode() == "unknown error code"
+
+
+def dims(F, S, w0, block=128):
+    nb, nnz = ctypes.c_int32(-9), ctypes.c_int64(-9)
+    rc = radial.lib().radial_mask_dims(F, S, w0, block, ctypes.byref(nb), ctypes.byref(nnz))
+    return rc, nb.value, nnz.value
+
+
+def test_mask_dims_errors():
+    assert dims(0, 10, 5)[0] == INVALID
+    assert dims(4, 0, 5)[0] == INVALID
+    assert dims(4, 10, 0)[0] == INVALID
+    assert dims(4, 10, -3)[0] == INVALID
+    assert dims(4, 10, 5, block=64)[0] == INVALID
+    assert dims(1 << 16, 1 << 16, 5)[0] == TOO_LARGE
+    assert radial.lib().radial_mask_dims(4, 10, 5, 128, None, None) == INVALID
+    assert dims(4, 256, 256) == (OK, 8, 64)
+
+
+def test_build_mask_errors():
+    lib = radial.lib()
+    rp = (ctypes.c_int32 * 9)()
+    ci = (ctypes.c_int32 * 64)()
+    assert lib.radial_build_mask(4, 256, 256, 128, None, ci, 64) == INVALID
+    assert lib.radial_build_mask(4, 256, 256, 128, rp, None, 64) == INVALID
+    assert lib.radial_build_mask(4, 256, 256, 128, rp, ci, -1) == INVALID
+    assert lib.radial_build_mask(4, 256, 256, 128, rp, ci, 63) == CAPACITY
+    assert lib.radial_build_mask(4, 256, 256, 100, rp, ci, 64) == INVALID
+    assert lib.radial_build_mask(4, 256, 256, 128, rp, ci, 64) == OK
+    assert list(rp) == list(range(0, 72, 8))
+    with pytest.raises(radial.RadialError) as e:
+        radial.build_mask(3, 100, 0)
+    assert e.value.code == INVALID
+
+
+def fwd(**kw):
+    """Call radial_attn_fwd with valid-looking defaults, overridden by kw."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, row_ptr=0x50000,
+             col_idx=0x60000, nb=8, scale=0.125, batch=1, heads=2, seqlen=1000, head_dim=128,
+             stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_s=128, stream=None)
+    a.update(kw)
+    return radial.lib().radial_attn_fwd(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], a["row_ptr"], a["col_idx"], a["nb"],
+        a["scale"], a["batch"], a["heads"], a["seqlen"], a["head_dim"], a["stride_b"],
+        a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID), (dict(row_ptr=None), INVALID), (dict(col_idx=None), INVALID),
+    (dict(batch=0), INVALID), (dict(heads=-1), INVALID), (dict(seqlen=0), INVALID),
+    (dict(nb=0), INVALID), (dict(scale=-0.5), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(stride_s=64), INVALID),
+    (dict(head_dim=96), HEADDIM), (dict(head_dim=256), HEADDIM),
+    (dict(nb=9), SHAPE), (dict(nb=7), SHAPE),
+    (dict(q=0x10008), MISALIGNED), (dict(o=0x40002), MISALIGNED),
+    (dict(stride_s=132), MISALIGNED), (dict(stride_h=1000 * 128 + 4), MISALIGNED),
+    (dict(batch=1 << 12, heads=1 << 12, seqlen=1 << 20, nb=1 << 13,
+          stride_h=(1 << 20) * 128, stride_b=(1 << 32) * 128), TOO_LARGE),
+])
+def test_attn_fwd_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_python_wrapper_checks_before_the_library():
+    import torch
+    q = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16)
+    m = radial.dense_mask(256)
+    with pytest.raises(ValueError):
+        radial.attn_fwd(q, q, q, m)       # CPU tensors are refused
+    with pytest.raises(TypeError):
+        radial.attn_fwd(q.float(), q.float(), q.float(), m)
+    with pytest.raises(ValueError):
+        radial.attn_fwd(q, q[:, :, :128], q, m)
