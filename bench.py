@@ -73,8 +73,9 @@ def time_launches(fn, steps: int, warmup: int):
 
 
 def cpu_baseline(wl, q, k, v, mask, seconds: float):
-    """Time the fp64 CPU oracle on head 0, query blocks in a seeded order, until about
-    `seconds` of work has run. Report the same active-tile flop rate as the GPU."""
+    """Time the fp64 CPU oracle over heads 0, 1, ... (each head's query blocks in a seeded
+    order) until about `seconds` of work has run. Report the same active-tile flop rate
+    as the GPU."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -85,17 +86,22 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float):
     mask_s = time.perf_counter() - t0
 
     rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
-    qh, kh, vh = (x[0, 0].double().cpu().numpy() for x in (q, k, v))
     order = np.random.default_rng(0).permutation(wl.nb)
-    done = []
-    t0 = time.perf_counter()
-    for qb in order:
-        ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)])
-        done.append(int(qb))
-        if time.perf_counter() - t0 >= seconds:
+    blocks, tiles, heads, elapsed = 0, 0, 0, 0.0
+    for h in range(wl.batch * wl.heads):
+        b, hh = divmod(h, wl.heads)
+        qh, kh, vh = (x[b, hh].double().cpu().numpy() for x in (q, k, v))
+        heads += 1
+        t0 = time.perf_counter()
+        for qb in order:
+            ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)])
+            blocks += 1
+            tiles += int(rp[qb + 1] - rp[qb])
+            if elapsed + time.perf_counter() - t0 >= seconds:
+                break
+        elapsed += time.perf_counter() - t0
+        if elapsed >= seconds:
             break
-    elapsed = time.perf_counter() - t0
-    tiles = int(sum(rp[b + 1] - rp[b] for b in done))
     flops = 4 * wl.head_dim * 128 * 128 * tiles
     threads = [d.get("num_threads", 0) for d in threadpool_info()
                if d.get("user_api") == "blas"]
@@ -104,7 +110,7 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float):
         "unit": "TFLOP/s",
         "cores": max(threads) if threads else 1,
         "kind": "oracle",
-        "sample": f"head 0 of {wl.heads}, {len(done)} of {wl.nb} query blocks "
+        "sample": f"{blocks} query blocks over {heads} of {wl.batch * wl.heads} heads "
                   f"({tiles} active tiles) in {elapsed:.1f} s, fp64 numpy; "
                   f"oracle block-mask build {mask_s:.2f} s",
     }
@@ -119,6 +125,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times), to scale "
+                         "HBM traffic counters against a kernel of known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -135,6 +144,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB 5 times")
+        return
     radial.lib()
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
