@@ -8,29 +8,35 @@
 //     O[rows] = softmax(scale * Q[rows] K[keys]^T) V[keys]
 //   where keys are the real tokens of the key blocks listed in the CSR row qb.
 //
-// Work decomposition: one workgroup = 4 wave64 = one query block of 128 rows. Each wave
-// owns 32 query rows. Two workgroups share a CU, so each SIMD runs two waves: while one
-// wave is in its softmax (VALU) the other keeps the matrix core busy. The register
-// budget is therefore 256 per lane, with no accumulator spills.
+// Work decomposition. One workgroup of 8 wave64 owns one query block of 128 rows and
+// fills one CU. Its waves form two groups of four: group 0 takes the even positions of
+// the row's key-block list and group 1 the odd ones. Wave i of either group owns query
+// rows 32i .. 32i+31, so each SIMD runs one wave of each group over the same rows. Both
+// keep their own online-softmax state, and the two states are merged at the end.
 //
+// Ping-pong. A wave's work per key tile is an MFMA part (P*V of the previous tile, then
+// Q*K^T of this tile) and a VALU part (the softmax). The groups run one phase apart,
+// separated by workgroup barriers: while group 0 issues MFMAs, group 1 runs its softmax,
+// then the roles swap. The matrix core of every SIMD thus always has a wave feeding it.
+// The MFMA-phase wave raises its issue priority.
+//
+// Per tile:
 //  - S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16, with keys on M and queries on N. A
-//    lane then holds one query (lane % 32) and 64 of the tile's 128 keys. The row max
-//    and row sum are in-lane, plus one exchange between the half-waves
-//    (v_permlane32_swap).
-//  - O^T = V^T P^T uses the same MFMA with head_dim on M and queries on N. The S^T
-//    accumulator of a lane is, key for key, the B operand this product needs once the
-//    contraction runs over keys in accumulator order, so P goes from registers into the
-//    MFMA after one bf16 pack.
-//  - K and V tiles are both stored key-major in LDS ([key][d], no padding). Each 16-byte
-//    chunk of a row is XOR-swizzled by a function of the row, so the K reads
-//    (ds_read_b128, 8 rows per bank cycle) and the transposed V reads
-//    (ds_read_b64_tr_b16, 4 rows x 32 bytes per 16-lane group) hit distinct banks.
-//  - ds_read_b64_tr_b16 gives a lane 4 keys of one V column. Two of them form the V^T
-//    A operand of one MFMA, so no register transpose is needed.
-//  - Tiles go HBM/L2 -> registers -> LDS with buffer loads. The descriptor's range check
-//    returns zeros past the sequence end, so the ragged last block needs no branches.
-//    The next K tile is fetched while QK^T and the softmax run, and the next V tile
-//    while PV runs.
+//    lane holds one query (lane % 32) and 64 of the tile's 128 keys, so the row max and
+//    row sum are in-lane, plus one v_permlane32_swap between the half-waves.
+//  - O^T = V^T P^T runs on the same MFMA, with head_dim on M and queries on N. The S^T
+//    accumulator is, key for key, the B operand this product needs once the contraction
+//    runs over keys in accumulator order. So P goes from registers into the MFMA after
+//    one bf16 pack.
+//  - K and V tiles are stored key-major in LDS ([key][d], no padding). Chunk c (16
+//    bytes) of row r sits at position c ^ swz(r), which spreads every read pattern below
+//    over all 64 banks.
+//  - V^T operands come from ds_read_b64_tr_b16. One such read gives a lane 4 keys of one
+//    V column, and two of them form an MFMA operand.
+//  - Tiles are copied HBM/L2 -> LDS by buffer_load ... lds, with no staging registers.
+//    A group issues the copies for its next tiles during its softmax phase, when its
+//    buffers are idle. The descriptor's range check returns zeros past the sequence end,
+//    so the ragged last block needs no guarded loads.
 //  - Online softmax in base 2: c = scale * log2(e), p = 2^(c*s - m). The running max m
 //    moves only when a tile's max exceeds it by more than 2^8 for some row of the wave.
 //    Until then p <= 256, and O and l are not rescaled. The final O / l is exact for
@@ -55,9 +61,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBlock = 128;    // query rows per workgroup, keys per tile
-constexpr int kThreads = 256;  // 4 wave64
+constexpr int kBlock = 128;        // query rows per workgroup, keys per tile
+constexpr int kThreads = 512;      // 8 wave64: two groups of four
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: p stays <= 256 between rescales
@@ -67,16 +74,24 @@ constexpr int kBufferFlags = 0x00020000;
 template <int D>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;                        // 16-byte chunks per row
-  static constexpr int kLoads = kBlock * kChunks / kThreads;   // chunks per thread per tile
-  static constexpr int kLdsElems = kBlock * D;
-  static_assert(kLoads * kThreads == kBlock * kChunks, "staging must cover the tile");
+  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
+  static constexpr int kBytes = kBlock * kRowBytes;   // one K or V tile
+  static constexpr int kCopiesPerWave = kBytes / 1024 / 4;  // 1 KiB per copy instruction
+  static_assert(kCopiesPerWave * 4 * 1024 == kBytes, "a group's copies must cover the tile");
 };
 
-// Bank swizzle: chunk c of row r lives at chunk position c ^ swz(r). Within 8
-// consecutive rows swz takes all of 0..7 (K reads), and within rows 4h..4h+3 it takes
-// {0, 2, 4, 6} + h (V transposed reads, whose 16-lane groups touch 4 rows x 2 chunks).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Bank swizzle. The LDS has 64 four-byte banks, so a 256-byte span is one bank cycle:
+// ds_read_b128 serves 16 lanes a cycle and ds_read_b64(_tr) 32 lanes. swz is chosen so
+// that (1) the 16 consecutive rows one K read touches land on 16 distinct 16-byte bank
+// slots, (2) the 4 rows x 4 chunks one transposed V read touches per 32 lanes do too.
+// For 256-byte rows (D = 128) this is swz(r) = 4 (r mod 4) + (r / 4 mod 4). For
+// 128-byte rows (D = 64) two rows share a bank cycle, and swz(r) = 4 (r / 2 mod 2) +
+// (r / 4 mod 4).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
@@ -86,8 +101,13 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
-// Reduction over the two half-waves: for a symmetric op, op(lo, hi) of the pair
-// returned by v_permlane32_swap(x, x) is the same in every lane.
+// One 1 KiB tile-copy instruction: lane l's 16 bytes from byte_offset land at lds + 16 l.
+__device__ __forceinline__ void copy_1k(__amdgpu_buffer_rsrc_t r, char* lds, int byte_offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, byte_offset, 0, 0, 0);
+}
+
+// Reductions over the two half-waves: for a symmetric op, op(lo, hi) of the pair that
+// v_permlane32_swap(x, x) returns is the same in every lane.
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
@@ -99,226 +119,332 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Everything one wave needs across the phase loop, gathered so that the two groups can
+// run the same phase code over different (compile-time distinct) LDS buffers.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void radial_fwd_kernel(
+struct WaveState {
+  using T = Tile<D>;
+  // inputs
+  const char* kh;  // K of this (batch, head), as bytes
+  const char* vh;  // V of this (batch, head), as bytes
+  const int32_t* cols;  // this group's list positions: cols[2j] is its tile j
+  int nb, n, row_bytes, wi, lane, hl, mine;
+  float c;
+  // per-lane offsets
+  int copy_off[T::kCopiesPerWave];
+  int k_rd, k_sw, v_rd, v_sw0, v_sw1, v_ch;
+  // Q^T fragments (bf16 pairs; kept as dwords so the struct is a valid host type too)
+  u32x4 qf[D / 16];
+  // softmax state
+  f32x16 oacc[D / 32];
+  float m_run, l_run;
+};
+
+// Copy one K or V tile (128 rows) into a group buffer: this wave's quarter of it.
+template <int D>
+__device__ __forceinline__ void stage_tile(WaveState<D>& w, char* buf, const char* src, int kb) {
+  using T = Tile<D>;
+  const bool valid = static_cast<unsigned>(kb) < static_cast<unsigned>(w.nb);
+  const int key0 = valid ? kb * kBlock : 0;
+  const int rows = valid ? (w.n - key0 < kBlock ? w.n - key0 : kBlock) : 0;
+  const auto r = make_rsrc(src + static_cast<int64_t>(key0) * w.row_bytes,
+                           rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0);
+#pragma unroll
+  for (int t = 0; t < T::kCopiesPerWave; ++t)
+    copy_1k(r, buf + (w.wi * T::kCopiesPerWave + t) * 1024, w.copy_off[t]);
+}
+
+// MFMA phase j: O += P(j-1) V(j-1), then S(j) = Q K(j)^T. On entry `sacc` holds P(j-1)
+// packed as bf16 (see softmax_phase); on exit it holds S(j).
+template <int D>
+__device__ __forceinline__ void mfma_phase(WaveState<D>& w, const char* kbuf, const char* vbuf,
+                                           int j, f32x16 (&sacc)[4]) {
+  using T = Tile<D>;
+  __builtin_amdgcn_s_setprio(1);
+  if (j >= 1 && j - 1 < w.mine) {
+    const char* vb = vbuf + w.v_rd;
+    auto read_v = [&](int u, bf16x8 (&vf)[D / 32]) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const char* p0 = vb + 16 * u * T::kRowBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(p0 + (((4 * db + w.v_ch) ^ w.v_sw0) << 4)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(p0 + 8 * T::kRowBytes + (((4 * db + w.v_ch) ^ w.v_sw1) << 4)));
+        vf[db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                         __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    bf16x8 vf[2][D / 32];
+    read_v(0, vf[0]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // u = 2g + s2: 16 keys of the contraction
+      if (u + 1 < 8) read_v(u + 1, vf[(u + 1) & 1]);
+      const f32x4 packed = {sacc[u >> 1][4 * (u & 1) + 0], sacc[u >> 1][4 * (u & 1) + 1],
+                            sacc[u >> 1][4 * (u & 1) + 2], sacc[u >> 1][4 * (u & 1) + 3]};
+      const bf16x8 pu = __builtin_bit_cast(bf16x8, packed);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u & 1][db], pu, w.oacc[db], 0, 0, 0);
+    }
+  }
+  if (j < w.mine) {
+    const char* kbp = kbuf + w.k_rd;
+    auto read_k = [&](int s, bf16x8 (&kf)[4]) {
+      const int ch = ((2 * s + w.hl) ^ w.k_sw) << 4;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        kf[g] = *reinterpret_cast<const bf16x8*>(kbp + g * 32 * T::kRowBytes + ch);
+    };
+    bf16x8 kf[2][4];
+    read_k(0, kf[0]);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      if (s + 1 < D / 16) read_k(s + 1, kf[(s + 1) & 1]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)  // the first k-step takes an inline zero accumulator
+        sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kf[s & 1][g], __builtin_bit_cast(bf16x8, w.qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+    }
+  }
+}
+
+// Softmax phase j: copy V(j) and K(j+1) into the idle group buffers, then turn S(j)
+// into P(j) and fold it into the running max / sum (rescaling O when the max moves).
+// P(j) is written back over S(j): the 8 bf16 of P for (g, s2), made from
+// sacc[g][8 s2 .. 8 s2 + 7], are packed into the dwords sacc[g][4 s2 .. 4 s2 + 3]. The
+// compiler then keeps S and P in the same 64 registers.
+template <int D>
+__device__ __forceinline__ void softmax_phase(WaveState<D>& w, char* kbuf, char* vbuf, int j,
+                                              f32x16 (&sacc)[4]) {
+  if (j >= w.mine) return;
+  __builtin_amdgcn_s_setprio(0);
+  const int kb = w.cols[2 * j];
+  stage_tile(w, vbuf, w.vh, kb);
+  if (j + 1 < w.mine) stage_tile(w, kbuf, w.kh, w.cols[2 * j + 2]);
+
+  if (static_cast<unsigned>(kb) >= static_cast<unsigned>(w.nb)) {
+    // Out-of-range column: the tile contributes nothing (P = 0).
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sacc[g] = f32x16{};
+    return;
+  }
+  const int key_lim = w.n - kb * kBlock;  // keys at or past this index are padding
+  if (key_lim < kBlock) {
+    // Key of accumulator entry (g, i) is 32g + 8(i/4) + (i%4) + 4hl: compare the
+    // constant part against one per-lane limit.
+    const int lim = key_lim - 4 * w.hl;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * g + 8 * (i >> 2) + (i & 3) >= lim) sacc[g][i] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[g][i]);
+  const float m_tile = halves_max(mx) * w.c;
+  if (__builtin_amdgcn_ballot_w64(m_tile > w.m_run + kRescaleThreshold) != 0) {
+    const float m_new = fmaxf(w.m_run, m_tile);
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);
+    w.m_run = m_new;
+    w.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) w.oacc[i] *= alpha;
+  }
+  const float neg_m = -w.m_run;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int g = u >> 1, s2 = u & 1;
+    f32x8 p8;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      p8[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + jj], w.c, neg_m));
+    const bf16x8 pu = __builtin_convertvector(p8, bf16x8);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bf16x2 pair = {pu[2 * jj], pu[2 * jj + 1]};
+      w.l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, w.l_run, false);
+    }
+    const f32x4 packed = __builtin_bit_cast(f32x4, pu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sacc[g][4 * s2 + e] = packed[e];
+  }
+}
+
+// The phase loop of one group. Phase ph of the workgroup is this group's phase
+// ph - G: even = MFMA phase, odd = softmax phase. Both groups pass the same number of
+// barriers (one per workgroup phase).
+template <int D, int G>
+__device__ __forceinline__ void run_group(WaveState<D>& w, char* kbuf, char* vbuf, int phases) {
+  f32x16 sacc[4];  // S(j) after an MFMA phase, P(j) after a softmax phase
+  int ph = 0;
+  if (G == 1) {
+    if (w.mine > 0) stage_tile(w, kbuf, w.kh, w.cols[0]);
+    __syncthreads();
+    ph = 1;
+  }
+  for (int j = 0; ph < phases; ++j) {
+    mfma_phase(w, kbuf, vbuf, j, sacc);
+    __syncthreads();
+    if (++ph >= phases) break;
+    softmax_phase(w, kbuf, vbuf, j, sacc);
+    __syncthreads();
+    ++ph;
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, int nb, int heads, int n, float c,
     int64_t stride_b, int64_t stride_h, int stride_s) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[T::kLdsElems];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[T::kLdsElems];
+  // K and V buffers of each group at fixed offsets; the merge at the end reuses them.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes];
+  char* const k0 = smem;
+  char* const v0 = smem + T::kBytes;
+  char* const k1 = smem + 2 * T::kBytes;
+  char* const v1 = smem + 3 * T::kBytes;
 
-  // Workgroups are handed to the 8 XCDs round-robin (XCD = id % 8). Give every XCD a
-  // contiguous run of (head, query block) items, so neighbouring query blocks of one
-  // head, which read mostly the same K/V tiles, share that XCD's L2.
-  const int grid = gridDim.x;
+  // Work mapping. Workgroup ids go to the 8 XCDs round-robin (XCD = id % 8) and are
+  // dispatched in id order. Ids [bh * nb, (bh + 1) * nb) all belong to head bh, so the
+  // whole chip works on one or two heads at a time and their K/V stays in the shared
+  // Infinity Cache. Inside a head, the ids that land on XCD x take one contiguous run of
+  // query blocks, in order, so neighbouring query blocks (which read mostly the same
+  // K/V tiles) share that XCD's L2.
   const int pid = blockIdx.x;
-  const int xcd = pid & 7, local = pid >> 3;
-  const int per = grid >> 3, rem = grid & 7;
-  const int item =
-      (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  const int bh = item / nb;
-  const int qb = item - bh * nb;
+  const int bh = pid / nb;
+  const int first_id = bh * nb;
+  const int xcd = pid & 7;
+  int seg = 0;  // query blocks of this head taken by XCDs 0 .. xcd-1
+  for (int y = 0; y < xcd; ++y)
+    seg += ((first_id + nb - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
+  const int first_here = first_id + ((xcd - first_id) & 7);  // first id of this head on xcd
+  const int qb = seg + ((pid - first_here) >> 3);
   const int b = bh / heads, h = bh - b * heads;
   const int64_t base = b * stride_b + h * stride_h;
-  const int row_bytes = stride_s * 2;  // bytes between consecutive tokens
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int lq = lane & 31;  // query column owned by this lane
-  const int hl = lane >> 5;  // half-wave
+  // The wave index is the same in every lane; saying so lets it live in a scalar
+  // register (it feeds M0, the LDS base of the tile copies).
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: even list positions, 1: odd
+
+  WaveState<D> w;
+  w.kh = reinterpret_cast<const char*>(k + base);
+  w.vh = reinterpret_cast<const char*>(v + base);
+  w.nb = nb;
+  w.n = n;
+  w.c = c;
+  w.row_bytes = stride_s * 2;
+  w.wi = wave & 3;  // query rows 32 wi .. 32 wi + 31
+  w.lane = tid & 63;
+  const int lq = w.lane & 31;  // query column owned by this lane
+  w.hl = w.lane >> 5;          // half-wave
 
   // ---- Q^T as the MFMA B operand: d = 16s + 8hl .. +7 of this lane's query ----
-  bf16x8 qf[D / 16];
   {
     const int q0 = qb * kBlock;
     const int rows = min(kBlock, n - q0);
     const auto rq = make_rsrc(q + base + static_cast<int64_t>(q0) * stride_s,
-                              (rows - 1) * row_bytes + T::kRowBytes);
-    const int off = (wave * 32 + lq) * row_bytes + hl * 16;
+                              (rows - 1) * w.row_bytes + T::kRowBytes);
+    const int off = (w.wi * 32 + lq) * w.row_bytes + w.hl * 16;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off + s * 32));
+    for (int s = 0; s < D / 16; ++s)
+      w.qf[s] = buffer_load16(rq, off + s * 32);
   }
 
-  // ---- staging: thread's chunks of a tile, fixed offsets for every tile ----
-  int g_off[T::kLoads];    // byte offset in global memory from the tile's first row
-  int l_off[T::kLoads];    // byte offset in LDS (swizzled)
+  // ---- tile copies: this wave's quarter of a tile, 1 KiB per instruction ----
+  // Copy t of wave wi fills bytes [(wi * kCopiesPerWave + t) KiB, +1 KiB) of a buffer;
+  // lane l writes 16 bytes at l * 16, i.e. chunk position p of row r, and so loads
+  // global chunk p ^ swz(r) of that row.
 #pragma unroll
-  for (int r = 0; r < T::kLoads; ++r) {
-    const int idx = tid + r * kThreads;
-    const int row = idx / T::kChunks, ch = idx % T::kChunks;
-    g_off[r] = row * row_bytes + ch * 16;
-    l_off[r] = row * T::kRowBytes + ((ch ^ swz(row)) << 4);
+  for (int t = 0; t < T::kCopiesPerWave; ++t) {
+    const int ci = (w.wi * T::kCopiesPerWave + t) * 64 + w.lane;
+    const int row = ci / T::kChunks, p = ci % T::kChunks;
+    w.copy_off[t] = row * w.row_bytes + ((p ^ swz<D>(row)) << 4);
   }
-  u32x4 stg[T::kLoads];
-  const __bf16* kh = k + base;
-  const __bf16* vh = v + base;
-  auto fetch = [&](const __bf16* src, int kb) {
-    const bool valid = static_cast<unsigned>(kb) < static_cast<unsigned>(nb);
-    const int key0 = valid ? kb * kBlock : 0;
-    const int rows = valid ? min(kBlock, n - key0) : 0;
-    const auto r = make_rsrc(src + static_cast<int64_t>(key0) * stride_s,
-                             rows > 0 ? (rows - 1) * row_bytes + T::kRowBytes : 0);
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) stg[i] = buffer_load16(r, g_off[i]);
-  };
-  auto stash = [&](__bf16* dst) {
-    char* d = reinterpret_cast<char*>(dst);
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) *reinterpret_cast<u32x4*>(d + l_off[i]) = stg[i];
-  };
 
   // ---- per-lane LDS read offsets for the MFMA operands (bytes) ----
   // K (A operand of S^T): row 32g + lq, chunk 2s + hl.
-  const int k_rd = lq * T::kRowBytes;
-  const int k_sw = swz(lq);
-  // V^T (A operand of O^T) via ds_read_b64_tr_b16: in 16-lane group gi, source lane s
-  // points at key 4hl + s/4 (+ tile offsets) and d = 32db + 16(gi&1) + 4(s&3).
-  const int gi = (lane >> 4) & 3, sl = lane & 15;
-  const int v_key = 4 * hl + (sl >> 2);
-  const int v_rd = v_key * T::kRowBytes + 8 * (sl & 1);
-  const int v_sw = swz(v_key);
-  const int v_ch = 2 * (gi & 1) + ((sl & 3) >> 1);
+  w.k_rd = lq * T::kRowBytes;
+  w.k_sw = swz<D>(lq);
+  // V^T (A operand of O^T) via ds_read_b64_tr_b16: in 16-lane group gi, source lane sl
+  // points at key 4hl + sl/4 (+ 8 for the second read of a pair, + tile offsets) and
+  // d = 32db + 16(gi&1) + 4(sl&3).
+  const int gi = (w.lane >> 4) & 3, sl = w.lane & 15;
+  const int v_key = 4 * w.hl + (sl >> 2);
+  w.v_rd = v_key * T::kRowBytes + 8 * (sl & 1);
+  w.v_sw0 = swz<D>(v_key);
+  w.v_sw1 = swz<D>(v_key + 8);
+  w.v_ch = 2 * (gi & 1) + ((sl & 3) >> 1);
 
-  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // max of c * s used for p, base-2 units
-  float l_run = 0.f;        // sum of bf16(p) over this lane's keys
+  for (int i = 0; i < D / 32; ++i) w.oacc[i] = f32x16{};
+  w.m_run = -INFINITY;  // max of c * s used for p, base-2 units
+  w.l_run = 0.f;        // sum of bf16(p) over this lane's keys
 
   const int start = row_ptr[qb];
-  const int end = row_ptr[qb + 1];
-  if (start < end) {
-    fetch(kh, col_idx[start]);
-    stash(k_lds);
-    fetch(vh, col_idx[start]);
-    stash(v_lds);
+  const int count = row_ptr[qb + 1] - start;
+  w.mine = (count - grp + 1) >> 1;  // tiles of this group
+  w.cols = col_idx + start + grp;
+
+  if (grp == 0 && w.mine > 0) stage_tile(w, k0, w.kh, w.cols[0]);
+  __syncthreads();
+  const int phases = count + 2;
+  if (grp == 0)
+    run_group<D, 0>(w, k0, v0, phases);
+  else
+    run_group<D, 1>(w, k1, v1, phases);
+
+  // ---- merge the two groups' states; group 1 hands its state to group 0 via LDS ----
+  // Layout: [wave][r][lane] floats, r = 0..D/2-1 for O^T, then m, then l.
+  constexpr int kState = D / 2 + 2;
+  float* const xfer = reinterpret_cast<float*>(smem) + w.wi * kState * 64 + w.lane;
+  static_assert(4 * kState * 64 * 4 <= 4 * T::kBytes, "merge area must fit the buffers");
+  if (grp == 1) {
+#pragma unroll
+    for (int r = 0; r < D / 2; ++r) xfer[r * 64] = w.oacc[r >> 4][r & 15];
+    xfer[(D / 2) * 64] = w.m_run;
+    xfer[(D / 2 + 1) * 64] = w.l_run;
   }
   __syncthreads();
+  if (grp == 1) return;
 
-  const char* k_bytes = reinterpret_cast<const char*>(k_lds);
-  const char* v_bytes = reinterpret_cast<const char*>(v_lds);
-
-  for (int it = start; it < end; ++it) {
-    const int kb = col_idx[it];
-    const bool has_next = it + 1 < end;
-    const int kb_next = has_next ? col_idx[it + 1] : 0;
-    const bool valid = static_cast<unsigned>(kb) < static_cast<unsigned>(nb);
-    if (has_next) fetch(kh, kb_next);
-
-    bf16x8 pf[8];  // P^T as B operands: [4 * g + ... ] packed per (g, s2)
-    if (valid) {
-      // ---- S^T = K Q^T ----
-      f32x16 sacc[4];
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int ch = ((2 * s + hl) ^ k_sw) << 4;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_bytes + k_rd + g * 32 * T::kRowBytes + ch);
-          // The first k-step takes an inline zero accumulator.
-          sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s == 0 ? f32x16{} : sacc[g],
-                                                            0, 0, 0);
-        }
-      }
-
-      // ---- padding keys of the ragged last block ----
-      const int key_lim = n - kb * kBlock;  // keys at or past this index are padding
-      if (key_lim < kBlock) {
-        // Key of accumulator entry (g, i) is 32g + 8(i/4) + (i%4) + 4hl: compare the
-        // constant part against one per-lane limit.
-        const int lim = key_lim - 4 * hl;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * g + 8 * (i >> 2) + (i & 3) >= lim) sacc[g][i] = -INFINITY;
-      }
-
-      // ---- online softmax ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[g][i]);
-      const float m_tile = halves_max(mx) * c;
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-      }
-      const float neg_m = -m_run;
-      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          f32x8 p8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            p8[j] = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + j], c, neg_m));
-          pf[2 * g + s2] = __builtin_convertvector(p8, bf16x8);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pair = {pf[2 * g + s2][2 * j], pf[2 * g + s2][2 * j + 1]};
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
-          }
-        }
-    }
-
-    __syncthreads();  // every wave is done reading K(it)
-    if (has_next) {
-      stash(k_lds);
-      fetch(vh, kb_next);
-    }
-
-    if (valid) {
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const int ch = ((4 * db + v_ch) ^ v_sw) << 4;
-            const char* p0 = v_bytes + v_rd + (32 * g + 16 * s2) * T::kRowBytes + ch;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(p0));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(p0 + 8 * T::kRowBytes));
-            const bf16x8 vf = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
-                                                      __builtin_bit_cast(bf16x4, hi),
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[2 * g + s2], oacc[db], 0, 0, 0);
-          }
-        }
-    }
-
-    __syncthreads();  // every wave is done reading V(it); K(it + 1) is in LDS
-    if (has_next) stash(v_lds);
-  }
-
-  // ---- epilogue: O / l, bf16, store rows < n ----
-  const float l_tot = halves_sum(l_run);
+  const float m_other = xfer[(D / 2) * 64];
+  const float l_other = xfer[(D / 2 + 1) * 64];
+  const float m_tot = fmaxf(w.m_run, m_other);
+  // A group with no tiles has m = -inf and contributes 0; both empty gives NaN, which an
+  // empty mask row deserves.
+  const float w_mine = w.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(w.m_run - m_tot);
+  const float w_other = m_other == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_other - m_tot);
+  const float l_tot = halves_sum(w.l_run * w_mine + l_other * w_other);
   const float inv = 1.0f / l_tot;
-  const int qrow = qb * kBlock + wave * 32 + lq;
+  const float a_mine = w_mine * inv, a_other = w_other * inv;
+  const int qrow = qb * kBlock + w.wi * 32 + lq;
   if (qrow < n) {
     __bf16* orow = o + base + static_cast<int64_t>(qrow) * stride_s;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        const f32x4 x = {oacc[db][4 * ib + 0] * inv, oacc[db][4 * ib + 1] * inv,
-                         oacc[db][4 * ib + 2] * inv, oacc[db][4 * ib + 3] * inv};
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * ib + 4 * hl) = __builtin_convertvector(x, bf16x4);
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = db * 16 + 4 * ib + e;
+          x[e] = w.oacc[db][4 * ib + e] * a_mine + xfer[r * 64] * a_other;
+        }
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * ib + 4 * w.hl) =
+            __builtin_convertvector(x, bf16x4);
       }
-    if (lse != nullptr && hl == 0)
-      lse[static_cast<int64_t>(bh) * n + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (lse != nullptr && w.hl == 0)
+      lse[static_cast<int64_t>(bh) * n + qrow] = (m_tot + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
