@@ -8,17 +8,23 @@
 //     O[rows] = softmax(scale * Q[rows] K[keys]^T) V[keys]
 //   where keys are the real tokens of the key blocks listed in the CSR row qb.
 //
-// Work decomposition. One workgroup of 8 wave64 owns one query block of 128 rows and
-// fills one CU. Its waves form two groups of four: group 0 takes the even positions of
-// the row's key-block list and group 1 the odd ones. Wave i of either group owns query
-// rows 32i .. 32i+31, so each SIMD runs one wave of each group over the same rows. Both
-// keep their own online-softmax state, and the two states are merged at the end.
+// Work decomposition. One workgroup of 8 wave64 owns a pair of neighbouring query blocks
+// (2p and 2p+1, 128 rows each) and fills one CU. Its waves form two groups of four; group
+// g owns query block 2p+g, wave i of a group owns its rows 32i .. 32i+31. Both groups
+// walk the union of the two rows' key-block lists, in ascending order (a merge of the
+// two sorted CSR rows); a group skips the tiles that are not in its own row. Each K/V
+// tile is thus copied to LDS once and used by both query blocks: neighbouring query
+// blocks share most of their key blocks, so this halves the traffic through each CU's
+// L1, which bounds how fast tiles can be streamed in.
 //
-// Ping-pong. A wave's work per key tile is an MFMA part (P*V of the previous tile, then
-// Q*K^T of this tile) and a VALU part (the softmax). The groups run one phase apart,
-// separated by workgroup barriers: while group 0 issues MFMAs, group 1 runs its softmax,
-// then the roles swap. The matrix core of every SIMD thus always has a wave feeding it.
-// The MFMA-phase wave raises its issue priority.
+// Ping-pong. A group's work per tile is an MFMA part (P*V of the previous tile, then
+// Q*K^T of this tile) and a VALU part (the softmax). Group 1 runs one phase behind group
+// 0, with a workgroup barrier after every phase: while one group issues MFMAs the other
+// runs its softmax, then the roles swap, so every SIMD's matrix core always has a wave
+// feeding it. Tile t is used by group 0 in phase 2t and by group 1 in phase 2t+1, so K
+// and V are double-buffered. The group in its softmax phase also issues the next copies
+// (group 1 copies V(t) in phase 2t, group 0 copies K(t+1) in phase 2t+1), spread over
+// its softmax steps: a copy instruction holds its wave back while the L1 drains it.
 //
 // Per tile:
 //  - S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16, with keys on M and queries on N. A
@@ -34,9 +40,8 @@
 //  - V^T operands come from ds_read_b64_tr_b16. One such read gives a lane 4 keys of one
 //    V column, and two of them form an MFMA operand.
 //  - Tiles are copied HBM/L2 -> LDS by buffer_load ... lds, with no staging registers.
-//    A group issues the copies for its next tiles during its softmax phase, when its
-//    buffers are idle. The descriptor's range check returns zeros past the sequence end,
-//    so the ragged last block needs no guarded loads.
+//    The descriptor's range check returns zeros past the sequence end, so the ragged
+//    last block needs no guarded loads.
 //  - Online softmax in base 2: c = scale * log2(e), p = 2^(c*s - m). The running max m
 //    moves only when a tile's max exceeds it by more than 2^8 for some row of the wave.
 //    Until then p <= 256, and O and l are not rescaled. The final O / l is exact for
@@ -46,6 +51,7 @@
 
 #include <cfloat>
 #include <cmath>
+#include <climits>
 #include <cstdint>
 
 #include "../../include/radial_attn.h"
@@ -60,10 +66,11 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBlock = 128;        // query rows per workgroup, keys per tile
+constexpr int kBlock = 128;        // query rows per group, keys per tile
 constexpr int kThreads = 512;      // 8 wave64: two groups of four
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -101,9 +108,39 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
-// One 1 KiB tile-copy instruction: lane l's 16 bytes from byte_offset land at lds + 16 l.
-__device__ __forceinline__ void copy_1k(__amdgpu_buffer_rsrc_t r, char* lds, int byte_offset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, byte_offset, 0, 0, 0);
+// Workgroup barrier that orders LDS but leaves tile copies (vector-memory loads into LDS)
+// in flight: it waits for this wave's own LDS reads (a copy issued after it may then
+// overwrite what was read), and the "memory" clobber keeps the compiler from moving
+// LDS accesses across it. Copies are waited for explicitly with wait_copies<N>.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Wait until at most N of this wave's vector-memory loads are outstanding. They
+// complete in issue order, so this waits for all but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Raw buffer descriptor of a byte range (four scalar dwords): base address, no stride,
+// `bytes` records, 32-bit data format. Reads at or past `bytes` return zero.
+__device__ __forceinline__ i32x4 raw_descriptor(const char* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(a & 0xffffffffu), static_cast<int>((a >> 32) & 0xffffu), bytes,
+               kBufferFlags};
+}
+
+// One 1 KiB tile-copy instruction: lane l's 16 bytes at byte_offset of the descriptor's
+// range land at LDS address lds + 16 l (buffer_load_dwordx4 ... lds, LDS base in M0).
+// It is written as inline asm so that the compiler does not track it as a pending LDS
+// write: its own waits would then stop every later LDS read until the copy lands. The
+// kernel orders these copies itself (wait_copies and lds_barrier). The instruction
+// writes no VGPR, and M0 is used by nothing else in this kernel.
+__device__ __forceinline__ void copy_1k(const i32x4& desc, uint32_t lds, int byte_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(byte_offset), "s"(desc)
+               : "memory");
 }
 
 // Reductions over the two half-waves: for a symmetric op, op(lo, hi) of the pair that
@@ -127,8 +164,7 @@ struct WaveState {
   // inputs
   const char* kh;  // K of this (batch, head), as bytes
   const char* vh;  // V of this (batch, head), as bytes
-  const int32_t* cols;  // this group's list positions: cols[2j] is its tile j
-  int nb, n, row_bytes, wi, lane, hl, mine;
+  int nb, n, row_bytes, wi, lane, hl;
   float c;
   // per-lane offsets
   int copy_off[T::kCopiesPerWave];
@@ -140,93 +176,135 @@ struct WaveState {
   float m_run, l_run;
 };
 
-// Copy one K or V tile (128 rows) into a group buffer: this wave's quarter of it.
+// A pending copy of one K or V tile (128 rows) into a group buffer: this wave's quarter
+// of it, issued one 1 KiB instruction at a time so that the copies can be spread over
+// the compute instead of stalling the wave in one burst.
+// A copy that is not wanted (on = false) gets a descriptor of zero bytes: its loads
+// write zeros into the buffer, which is not read again before its next real copy.
+// That keeps the copy code free of branches, so the scheduler can keep it interleaved.
 template <int D>
-__device__ __forceinline__ void stage_tile(WaveState<D>& w, char* buf, const char* src, int kb) {
+struct Stage {
+  i32x4 desc;
+  uint32_t lds;
+};
+
+template <int D>
+__device__ __forceinline__ Stage<D> stage_tile(const WaveState<D>& w, char* buf, const char* src,
+                                               int kb, bool on) {
   using T = Tile<D>;
-  const bool valid = static_cast<unsigned>(kb) < static_cast<unsigned>(w.nb);
+  const bool valid = on && static_cast<unsigned>(kb) < static_cast<unsigned>(w.nb);
   const int key0 = valid ? kb * kBlock : 0;
   const int rows = valid ? (w.n - key0 < kBlock ? w.n - key0 : kBlock) : 0;
-  const auto r = make_rsrc(src + static_cast<int64_t>(key0) * w.row_bytes,
+  Stage<D> st;
+  st.desc = raw_descriptor(src + static_cast<int64_t>(key0) * w.row_bytes,
                            rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0);
-#pragma unroll
-  for (int t = 0; t < T::kCopiesPerWave; ++t)
-    copy_1k(r, buf + (w.wi * T::kCopiesPerWave + t) * 1024, w.copy_off[t]);
+  st.lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)buf)) +
+           w.wi * T::kCopiesPerWave * 1024;
+  return st;
 }
 
-// MFMA phase j: O += P(j-1) V(j-1), then S(j) = Q K(j)^T. On entry `sacc` holds P(j-1)
-// packed as bf16 (see softmax_phase); on exit it holds S(j).
+// Issue copy instruction t of a pending tile copy.
 template <int D>
-__device__ __forceinline__ void mfma_phase(WaveState<D>& w, const char* kbuf, const char* vbuf,
-                                           int j, f32x16 (&sacc)[4]) {
+__device__ __forceinline__ void stage_issue(const WaveState<D>& w, const Stage<D>& st, int t) {
+  if (t < Tile<D>::kCopiesPerWave) copy_1k(st.desc, st.lds + t * 1024, w.copy_off[t]);
+}
+
+// Issue a whole tile copy at once (prologue only).
+template <int D>
+__device__ __forceinline__ void stage_all(const WaveState<D>& w, char* buf, const char* src, int kb) {
+  const Stage<D> st = stage_tile(w, buf, src, kb, true);
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kCopiesPerWave; ++t) stage_issue(w, st, t);
+}
+
+// PV part of an MFMA phase: O += P(j-1) V(j-1). `sacc` holds P(j-1) packed as bf16
+// (see softmax_tile). V^T fragments go through a two-step ring: the reads for step u + 1
+// are issued before the MFMAs of step u (each step is 2 x D/32 transposed reads, and at
+// most 15 LDS reads can be outstanding). The sched_group_barrier pairs pin that order
+// against the scheduler's wish to save registers.
+template <int D>
+__device__ __forceinline__ void pv_part(WaveState<D>& w, const char* vbuf, const f32x16 (&sacc)[4]) {
   using T = Tile<D>;
-  __builtin_amdgcn_s_setprio(1);
-  if (j >= 1 && j - 1 < w.mine) {
-    const char* vb = vbuf + w.v_rd;
-    auto read_v = [&](int u, bf16x8 (&vf)[D / 32]) {
+  constexpr int R = 2 * (D / 32);  // transposed reads per step
+  const char* vb = vbuf + w.v_rd;
+  auto read_v = [&](int u, bf16x8 (&vf)[D / 32]) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const char* p0 = vb + 16 * u * T::kRowBytes;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(p0 + (((4 * db + w.v_ch) ^ w.v_sw0) << 4)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(p0 + 8 * T::kRowBytes + (((4 * db + w.v_ch) ^ w.v_sw1) << 4)));
-        vf[db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
-                                         __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    };
-    bf16x8 vf[2][D / 32];
-    read_v(0, vf[0]);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {  // u = 2g + s2: 16 keys of the contraction
-      if (u + 1 < 8) read_v(u + 1, vf[(u + 1) & 1]);
-      const f32x4 packed = {sacc[u >> 1][4 * (u & 1) + 0], sacc[u >> 1][4 * (u & 1) + 1],
-                            sacc[u >> 1][4 * (u & 1) + 2], sacc[u >> 1][4 * (u & 1) + 3]};
-      const bf16x8 pu = __builtin_bit_cast(bf16x8, packed);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u & 1][db], pu, w.oacc[db], 0, 0, 0);
+    for (int db = 0; db < D / 32; ++db) {
+      const char* p0 = vb + 16 * u * T::kRowBytes;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(p0 + (((4 * db + w.v_ch) ^ w.v_sw0) << 4)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(p0 + 8 * T::kRowBytes + (((4 * db + w.v_ch) ^ w.v_sw1) << 4)));
+      vf[db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                       __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
+  };
+  bf16x8 vf[2][D / 32];
+  read_v(0, vf[0]);
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {  // u = 2g + s2: 16 keys of the contraction
+    if (u + 1 < 8) {
+      read_v(u + 1, vf[(u + 1) & 1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // reads of step u + 1
+    }
+    const f32x4 packed = {sacc[u >> 1][4 * (u & 1) + 0], sacc[u >> 1][4 * (u & 1) + 1],
+                          sacc[u >> 1][4 * (u & 1) + 2], sacc[u >> 1][4 * (u & 1) + 3]};
+    const bf16x8 pu = __builtin_bit_cast(bf16x8, packed);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u & 1][db], pu, w.oacc[db], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);  // then the MFMAs of step u
   }
-  if (j < w.mine) {
-    const char* kbp = kbuf + w.k_rd;
-    auto read_k = [&](int s, bf16x8 (&kf)[4]) {
-      const int ch = ((2 * s + w.hl) ^ w.k_sw) << 4;
+}
+
+// QK part of an MFMA phase: S(j) = Q K(j)^T into `sacc`. The K fragments go through a
+// two-step ring: the reads for k-step s + 2 are issued right after the MFMAs of step s
+// have taken their operands, so 8 reads are in flight while MFMAs run (pinned the same
+// way).
+template <int D>
+__device__ __forceinline__ void qk_part(WaveState<D>& w, const char* kbuf, f32x16 (&sacc)[4]) {
+  using T = Tile<D>;
+  constexpr int S = D / 16;
+  const char* kbp = kbuf + w.k_rd;
+  auto read_k = [&](int s, bf16x8 (&kf)[4]) {
+    const int ch = ((2 * s + w.hl) ^ w.k_sw) << 4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        kf[g] = *reinterpret_cast<const bf16x8*>(kbp + g * 32 * T::kRowBytes + ch);
-    };
-    bf16x8 kf[2][4];
-    read_k(0, kf[0]);
+    for (int g = 0; g < 4; ++g)
+      kf[g] = *reinterpret_cast<const bf16x8*>(kbp + g * 32 * T::kRowBytes + ch);
+  };
+  bf16x8 kf[2][4];
+  read_k(0, kf[0]);
+  read_k(1, kf[1]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 initial reads
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      if (s + 1 < D / 16) read_k(s + 1, kf[(s + 1) & 1]);
+  for (int s = 0; s < S; ++s) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)  // the first k-step takes an inline zero accumulator
-        sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            kf[s & 1][g], __builtin_bit_cast(bf16x8, w.qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+    for (int g = 0; g < 4; ++g)  // the first k-step takes an inline zero accumulator
+      sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          kf[s & 1][g], __builtin_bit_cast(bf16x8, w.qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs of step s
+    if (s + 2 < S) {
+      read_k(s + 2, kf[s & 1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the reads of step s + 2
     }
   }
 }
 
-// Softmax phase j: copy V(j) and K(j+1) into the idle group buffers, then turn S(j)
-// into P(j) and fold it into the running max / sum (rescaling O when the max moves).
-// P(j) is written back over S(j): the 8 bf16 of P for (g, s2), made from
-// sacc[g][8 s2 .. 8 s2 + 7], are packed into the dwords sacc[g][4 s2 .. 4 s2 + 3]. The
-// compiler then keeps S and P in the same 64 registers.
-template <int D>
-__device__ __forceinline__ void softmax_phase(WaveState<D>& w, char* kbuf, char* vbuf, int j,
-                                              f32x16 (&sacc)[4]) {
-  if (j >= w.mine) return;
-  __builtin_amdgcn_s_setprio(0);
-  const int kb = w.cols[2 * j];
-  stage_tile(w, vbuf, w.vh, kb);
-  if (j + 1 < w.mine) stage_tile(w, kbuf, w.kh, w.cols[2 * j + 2]);
-
+// Softmax of tile j (column kb): mask padding keys, find the row max, rescale O and l
+// when the max moves, and turn S(j) into P(j). P(j) is written back over S(j): the 8 bf16
+// of P for (g, s2), made from sacc[g][8 s2 .. 8 s2 + 7], are packed into the dwords
+// sacc[g][4 s2 .. 4 s2 + 3], so S and P share the same 64 registers. `hook(u)` runs
+// after each eighth of the work (it issues tile copies).
+template <int D, typename Hook>
+__device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&sacc)[4],
+                                             Hook&& hook) {
   if (static_cast<unsigned>(kb) >= static_cast<unsigned>(w.nb)) {
     // Out-of-range column: the tile contributes nothing (P = 0).
 #pragma unroll
     for (int g = 0; g < 4; ++g) sacc[g] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) hook(u);
     return;
   }
   const int key_lim = w.n - kb * kBlock;  // keys at or past this index are padding
@@ -272,30 +350,107 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& w, char* kbuf, char*
     const f32x4 packed = __builtin_bit_cast(f32x4, pu);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sacc[g][4 * s2 + e] = packed[e];
+    hook(u);
   }
 }
 
-// The phase loop of one group. Phase ph of the workgroup is this group's phase
-// ph - G: even = MFMA phase, odd = softmax phase. Both groups pass the same number of
-// barriers (one per workgroup phase).
+// Ascending merge of two sorted CSR rows, the key-block list a workgroup walks. The
+// state is the same in every lane (it lives in scalar registers); INT_MAX marks an
+// exhausted row.
+struct Merge {
+  const int32_t* col;
+  int ia, a_end, ib, b_end;
+  int pa, pb;  // next entry of each row
+};
+
+__device__ __forceinline__ Merge merge_begin(const int32_t* col, int a0, int a1, int b0, int b1) {
+  Merge m{col, a0, a1, b0, b1, INT_MAX, INT_MAX};
+  if (a0 < a1) m.pa = col[a0];
+  if (b0 < b1) m.pb = col[b0];
+  return m;
+}
+
+// The next key block of the union and which rows hold it; false when both are done.
+__device__ __forceinline__ bool merge_next(Merge& m, int& kb, bool& in_a, bool& in_b) {
+  kb = m.pa < m.pb ? m.pa : m.pb;
+  if (kb == INT_MAX) return false;
+  in_a = m.pa == kb;
+  in_b = m.pb == kb;
+  if (in_a) m.pa = ++m.ia < m.a_end ? m.col[m.ia] : INT_MAX;
+  if (in_b) m.pb = ++m.ib < m.b_end ? m.col[m.ib] : INT_MAX;
+  return true;
+}
+
+// One union tile as a group sees it.
+struct TileRef {
+  int kb;     // key block
+  bool here;  // the tile exists (index < union length)
+  bool mine;  // ... and belongs to this group's row
+};
+
+// The phase loop of group G (G = 0: query block 2p, G = 1: query block 2p+1). With U the
+// union length, phase 2t is group 0's MFMA phase for tile t and group 1's softmax phase
+// for tile t-1; phase 2t+1 is the other way round. Each phase ends at a workgroup
+// barrier, and both groups pass 2U + 3 of them.
+//   group 0, MFMA t:    O += P(t-1) V(t-1); S(t) = Q K(t)^T
+//   group 0, softmax t: softmax of tile t; copy K(t+1) meanwhile; wait for it
+//   group 1, MFMA t:    O += P(t-1) V(t-1); S(t) = Q K(t)^T; wait for the V(t) copy
+//   group 1, softmax t: softmax of tile t; copy V(t+1) meanwhile
+// Tile t lives in K buffer t % 2 and V buffer t % 2. A copy into a buffer starts only
+// after the barrier that ends the last phase reading its old tile. P(t-1) and S(t) share
+// registers, so P V runs before Q K^T.
 template <int D, int G>
-__device__ __forceinline__ void run_group(WaveState<D>& w, char* kbuf, char* vbuf, int phases) {
-  f32x16 sacc[4];  // S(j) after an MFMA phase, P(j) after a softmax phase
-  int ph = 0;
-  if (G == 1) {
-    if (w.mine > 0) stage_tile(w, kbuf, w.kh, w.cols[0]);
-    __syncthreads();
-    ph = 1;
+__device__ __forceinline__ void run_group(WaveState<D>& w, Merge m, char* __restrict__ k0,
+                                          char* __restrict__ k1, char* __restrict__ v0,
+                                          char* __restrict__ v1) {
+  f32x16 sacc[4];  // S(t) after an MFMA phase, P(t) after a softmax phase
+  auto pick = [](int t, char* b0, char* b1) { return (t & 1) ? b1 : b0; };
+  auto fetch = [&](TileRef& r) {
+    bool in_a = false, in_b = false;
+    r.here = merge_next(m, r.kb, in_a, in_b);
+    r.mine = r.here && (G == 0 ? in_a : in_b);
+  };
+  TileRef prev{0, false, false}, cur, next;
+  fetch(cur);
+  fetch(next);
+  if (G == 1) {  // phase 0: copy V(0)
+    if (cur.here) stage_all(w, v0, w.vh, cur.kb);
+    lds_barrier();
   }
-  for (int j = 0; ph < phases; ++j) {
-    mfma_phase(w, kbuf, vbuf, j, sacc);
-    __syncthreads();
-    if (++ph >= phases) break;
-    softmax_phase(w, kbuf, vbuf, j, sacc);
-    __syncthreads();
-    ++ph;
+  for (int t = 0;; ++t) {
+    // ---- MFMA phase t ----
+    __builtin_amdgcn_s_setprio(1);
+    if (prev.mine) pv_part(w, pick(t - 1, v0, v1), sacc);
+    if (cur.mine) qk_part(w, pick(t, k0, k1), sacc);
+    if (G == 1) wait_copies<0>();  // V(t)
+    lds_barrier();
+    // ---- softmax phase t ----
+    __builtin_amdgcn_s_setprio(0);
+    const Stage<D> st = G == 0 ? stage_tile(w, pick(t + 1, k0, k1), w.kh, next.kb, next.here)
+                               : stage_tile(w, pick(t + 1, v0, v1), w.vh, next.kb, next.here);
+    auto hook = [&](int u) {
+      // Keep the scheduler from bunching the copies: each softmax step's math stays
+      // between its copy instructions.
+      __builtin_amdgcn_sched_barrier(0);
+      stage_issue(w, st, u);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (cur.mine) {
+      softmax_tile(w, cur.kb, sacc, hook);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) stage_issue(w, st, u);
+    }
+    if (G == 0) wait_copies<0>();  // K(t+1)
+    lds_barrier();
+    if (!cur.here) break;  // phase 2U+1 (group 0) / 2U+2 (group 1) done
+    prev = cur;
+    cur = next;
+    fetch(next);
   }
+  if (G == 0) lds_barrier();  // group 1's last phase
   __builtin_amdgcn_s_setprio(0);
+  wait_copies<0>();
 }
 
 template <int D>
@@ -305,28 +460,29 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
     const int32_t* __restrict__ col_idx, int nb, int heads, int n, float c,
     int64_t stride_b, int64_t stride_h, int stride_s) {
   using T = Tile<D>;
-  // K and V buffers of each group at fixed offsets; the merge at the end reuses them.
+  // Two K and two V buffers at fixed offsets.
   __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes];
   char* const k0 = smem;
-  char* const v0 = smem + T::kBytes;
-  char* const k1 = smem + 2 * T::kBytes;
+  char* const k1 = smem + T::kBytes;
+  char* const v0 = smem + 2 * T::kBytes;
   char* const v1 = smem + 3 * T::kBytes;
 
   // Work mapping. Workgroup ids go to the 8 XCDs round-robin (XCD = id % 8) and are
-  // dispatched in id order. Ids [bh * nb, (bh + 1) * nb) all belong to head bh, so the
-  // whole chip works on one or two heads at a time and their K/V stays in the shared
-  // Infinity Cache. Inside a head, the ids that land on XCD x take one contiguous run of
-  // query blocks, in order, so neighbouring query blocks (which read mostly the same
-  // K/V tiles) share that XCD's L2.
+  // dispatched in id order. Ids [bh * np, (bh + 1) * np) all belong to head bh (np query
+  // block pairs per head), so the whole chip works on one or two heads at a time and
+  // their K/V stays in the shared Infinity Cache. Inside a head, the ids that land on
+  // XCD x take one contiguous run of pairs, in order, so neighbouring query blocks
+  // (which read mostly the same K/V tiles) share that XCD's L2.
+  const int np = (nb + 1) >> 1;
   const int pid = blockIdx.x;
-  const int bh = pid / nb;
-  const int first_id = bh * nb;
+  const int bh = pid / np;
+  const int first_id = bh * np;
   const int xcd = pid & 7;
-  int seg = 0;  // query blocks of this head taken by XCDs 0 .. xcd-1
+  int seg = 0;  // pairs of this head taken by XCDs 0 .. xcd-1
   for (int y = 0; y < xcd; ++y)
-    seg += ((first_id + nb - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
+    seg += ((first_id + np - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
   const int first_here = first_id + ((xcd - first_id) & 7);  // first id of this head on xcd
-  const int qb = seg + ((pid - first_here) >> 3);
+  const int pair = seg + ((pid - first_here) >> 3);
   const int b = bh / heads, h = bh - b * heads;
   const int64_t base = b * stride_b + h * stride_h;
 
@@ -334,7 +490,8 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   // The wave index is the same in every lane; saying so lets it live in a scalar
   // register (it feeds M0, the LDS base of the tile copies).
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // 0: even list positions, 1: odd
+  const int grp = wave >> 2;       // query block 2 pair + grp
+  const int qb = 2 * pair + grp;   // may be nb (no rows) for the last pair of an odd nb
 
   WaveState<D> w;
   w.kh = reinterpret_cast<const char*>(k + base);
@@ -351,13 +508,17 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   // ---- Q^T as the MFMA B operand: d = 16s + 8hl .. +7 of this lane's query ----
   {
     const int q0 = qb * kBlock;
-    const int rows = min(kBlock, n - q0);
-    const auto rq = make_rsrc(q + base + static_cast<int64_t>(q0) * stride_s,
-                              (rows - 1) * w.row_bytes + T::kRowBytes);
+    const int rows = n - q0 < kBlock ? n - q0 : kBlock;
+    const auto rq = make_rsrc(q + base + static_cast<int64_t>(q0 < n ? q0 : 0) * stride_s,
+                              rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0);
     const int off = (w.wi * 32 + lq) * w.row_bytes + w.hl * 16;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       w.qf[s] = buffer_load16(rq, off + s * 32);
+    // Wait for Q here, where the compiler sees it. Otherwise its wait-count bookkeeping
+    // carries the Q loads into the phase loop as pending and waits on the vector-memory
+    // counter there, i.e. on the tile copies, every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // ---- tile copies: this wave's quarter of a tile, 1 KiB per instruction ----
@@ -390,43 +551,30 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   w.m_run = -INFINITY;  // max of c * s used for p, base-2 units
   w.l_run = 0.f;        // sum of bf16(p) over this lane's keys
 
-  const int start = row_ptr[qb];
-  const int count = row_ptr[qb + 1] - start;
-  w.mine = (count - grp + 1) >> 1;  // tiles of this group
-  w.cols = col_idx + start + grp;
+  // The two rows' column ranges (the second row is empty past the last query block).
+  const int qa = 2 * pair, qbb = 2 * pair + 1;
+  const int a0 = row_ptr[qa], a1 = row_ptr[qa + 1];
+  const int b0 = qbb < nb ? row_ptr[qbb] : 0, b1 = qbb < nb ? row_ptr[qbb + 1] : 0;
+  const Merge m = merge_begin(col_idx, a0, a1, b0, b1);
 
-  if (grp == 0 && w.mine > 0) stage_tile(w, k0, w.kh, w.cols[0]);
-  __syncthreads();
-  const int phases = count + 2;
-  if (grp == 0)
-    run_group<D, 0>(w, k0, v0, phases);
-  else
-    run_group<D, 1>(w, k1, v1, phases);
-
-  // ---- merge the two groups' states; group 1 hands its state to group 0 via LDS ----
-  // Layout: [wave][r][lane] floats, r = 0..D/2-1 for O^T, then m, then l.
-  constexpr int kState = D / 2 + 2;
-  float* const xfer = reinterpret_cast<float*>(smem) + w.wi * kState * 64 + w.lane;
-  static_assert(4 * kState * 64 * 4 <= 4 * T::kBytes, "merge area must fit the buffers");
-  if (grp == 1) {
-#pragma unroll
-    for (int r = 0; r < D / 2; ++r) xfer[r * 64] = w.oacc[r >> 4][r & 15];
-    xfer[(D / 2) * 64] = w.m_run;
-    xfer[(D / 2 + 1) * 64] = w.l_run;
+  // Prologue: group 0's first K tile. The compiler does not see the tile copies, so a
+  // barrier never waits for them by itself: every wait for a copy is explicit.
+  if (grp == 0) {
+    Merge m0 = m;
+    int kb;
+    bool in_a, in_b;
+    if (merge_next(m0, kb, in_a, in_b)) stage_all(w, k0, w.kh, kb);
   }
+  wait_copies<0>();
   __syncthreads();
-  if (grp == 1) return;
+  if (grp == 0)
+    run_group<D, 0>(w, m, k0, k1, v0, v1);
+  else
+    run_group<D, 1>(w, m, k0, k1, v0, v1);
 
-  const float m_other = xfer[(D / 2) * 64];
-  const float l_other = xfer[(D / 2 + 1) * 64];
-  const float m_tot = fmaxf(w.m_run, m_other);
-  // A group with no tiles has m = -inf and contributes 0; both empty gives NaN, which an
-  // empty mask row deserves.
-  const float w_mine = w.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(w.m_run - m_tot);
-  const float w_other = m_other == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_other - m_tot);
-  const float l_tot = halves_sum(w.l_run * w_mine + l_other * w_other);
+  // ---- epilogue: O / l, bf16, store rows < n ----
+  const float l_tot = halves_sum(w.l_run);
   const float inv = 1.0f / l_tot;
-  const float a_mine = w_mine * inv, a_other = w_other * inv;
   const int qrow = qb * kBlock + w.wi * 32 + lq;
   if (qrow < n) {
     __bf16* orow = o + base + static_cast<int64_t>(qrow) * stride_s;
@@ -434,17 +582,13 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = db * 16 + 4 * ib + e;
-          x[e] = w.oacc[db][4 * ib + e] * a_mine + xfer[r * 64] * a_other;
-        }
+        const f32x4 x = {w.oacc[db][4 * ib + 0] * inv, w.oacc[db][4 * ib + 1] * inv,
+                         w.oacc[db][4 * ib + 2] * inv, w.oacc[db][4 * ib + 3] * inv};
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * ib + 4 * w.hl) =
             __builtin_convertvector(x, bf16x4);
       }
     if (lse != nullptr && w.hl == 0)
-      lse[static_cast<int64_t>(bh) * n + qrow] = (m_tot + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      lse[static_cast<int64_t>(bh) * n + qrow] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
@@ -466,7 +610,7 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return RADIAL_ERR_MISALIGNED;
   if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
-  const int64_t items = static_cast<int64_t>(batch) * heads * nb;
+  const int64_t items = static_cast<int64_t>(batch) * heads * ((nb + 1) / 2);
   // A tile of 128 rows is addressed with 32-bit byte offsets from its first row.
   if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
 
