@@ -11,28 +11,27 @@
 // Work decomposition. One workgroup of 8 wave64 owns a pair of neighbouring query blocks
 // (2p and 2p+1, 128 rows each) and fills one CU. Its waves form two groups of four; group
 // g owns query block 2p+g, wave i of a group owns its rows 32i .. 32i+31. Both groups
-// walk the union of the two rows' key-block lists, in ascending order (a merge of the
-// two sorted CSR rows); a group skips the tiles that are not in its own row. Each K/V
-// tile is thus copied to LDS once and used by both query blocks: neighbouring query
-// blocks share most of their key blocks, so this halves the traffic through each CU's
-// L1, which bounds how fast tiles can be streamed in.
+// walk the union of the two rows' key-block lists in ascending order; a group skips the
+// tiles that are not in its own row. Each K/V tile is thus copied to LDS once and used by
+// both query blocks (neighbouring query blocks share most key blocks). The union list is
+// built once, in the prologue, into LDS: a parallel merge of the two CSR rows.
 //
 // Ping-pong. A group's work per tile is an MFMA part (P*V of the previous tile, then
 // Q*K^T of this tile) and a VALU part (the softmax). Group 1 runs one phase behind group
 // 0, with a workgroup barrier after every phase: while one group issues MFMAs the other
-// runs its softmax, then the roles swap, so every SIMD's matrix core always has a wave
-// feeding it. Tile t is used by group 0 in phase 2t and by group 1 in phase 2t+1, so K
-// and V are double-buffered. The group in its softmax phase also issues the next copies
-// (group 1 copies V(t) in phase 2t, group 0 copies K(t+1) in phase 2t+1), spread over
-// its softmax steps: a copy instruction holds its wave back while the L1 drains it.
+// runs its softmax, so every SIMD's matrix core always has a wave feeding it. Union tile
+// t is read by group 0 in phase 2t and by group 1 in phase 2t+1. Group 1 issues every
+// tile copy, from its softmax phases: V(t) and K(t+1) in phase 2t, into the buffers that
+// phase 2t-1 finished reading. It waits for them at the end of phase 2t+1, so a copy has
+// two phases to land before group 0 reads it in phase 2t+2.
 //
 // Per tile:
 //  - S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16, with keys on M and queries on N. A
-//    lane holds one query (lane % 32) and 64 of the tile's 128 keys, so the row max and
-//    row sum are in-lane, plus one v_permlane32_swap between the half-waves.
+//    lane holds one query (lane % 32) and 64 of the tile's 128 keys, so row reductions
+//    are in-lane, plus one v_permlane32_swap between the half-waves.
 //  - O^T = V^T P^T runs on the same MFMA, with head_dim on M and queries on N. The S^T
 //    accumulator is, key for key, the B operand this product needs once the contraction
-//    runs over keys in accumulator order. So P goes from registers into the MFMA after
+//    runs over keys in accumulator order, so P goes from registers into the MFMA after
 //    one bf16 pack.
 //  - K and V tiles are stored key-major in LDS ([key][d], no padding). Chunk c (16
 //    bytes) of row r sits at position c ^ swz(r), which spreads every read pattern below
@@ -42,11 +41,13 @@
 //  - Tiles are copied HBM/L2 -> LDS by buffer_load ... lds, with no staging registers.
 //    The descriptor's range check returns zeros past the sequence end, so the ragged
 //    last block needs no guarded loads.
-//  - Online softmax in base 2: c = scale * log2(e), p = 2^(c*s - m). The running max m
-//    moves only when a tile's max exceeds it by more than 2^8 for some row of the wave.
-//    Until then p <= 256, and O and l are not rescaled. The final O / l is exact for
-//    any m used consistently. The row sum adds the bf16-rounded p, the same values the
-//    PV product multiplies.
+//  - Online softmax in base 2: c = scale * log2(e), p = 2^(c*s - m). The reference m is
+//    set from the row maximum of a wave's first tile and moves only when a tile's sum of
+//    p for some lane exceeds 2^20, i.e. when the scores have grown by about 20 (base 2)
+//    past m. That case is found after the fact from the sum, and the tile is redone
+//    with the new m (O and l rescaled). So the common path has no row maximum. The final
+//    O / l is exact for any m used consistently. The row sum adds the bf16-rounded p,
+//    the same values the PV product multiplies.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -74,9 +75,16 @@ constexpr int kBlock = 128;        // query rows per group, keys per tile
 constexpr int kThreads = 512;      // 8 wave64: two groups of four
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: p stays <= 256 between rescales
+// A lane's sum of p over one tile (64 keys) above this means m is stale: rescale.
+// It bounds every p by 2^20 between rescales.
+constexpr float kTileSumLimit = 1048576.0f;
 // Fourth dword of a raw gfx9 buffer descriptor: 32-bit data format, no stride/swizzle.
 constexpr int kBufferFlags = 0x00020000;
+// Union list: one 16-bit entry per key block (kb | in-row-A << 14 | in-row-B << 15).
+// A union of two rows has at most nb entries, so nb <= kMaxBlocks bounds it. With four
+// 32 KiB tile buffers, the list and a few counters fill the 160 KiB of LDS.
+constexpr int kMaxBlocks = 16352;
+constexpr int kListBytes = kMaxBlocks * 2;
 
 template <int D>
 struct Tile {
@@ -84,7 +92,12 @@ struct Tile {
   static constexpr int kChunks = D / 8;               // 16-byte chunks per row
   static constexpr int kBytes = kBlock * kRowBytes;   // one K or V tile
   static constexpr int kCopiesPerWave = kBytes / 1024 / 4;  // 1 KiB per copy instruction
-  static_assert(kCopiesPerWave * 4 * 1024 == kBytes, "a group's copies must cover the tile");
+  static_assert(kCopiesPerWave * 4 * 1024 == kBytes, "four waves' copies must cover a tile");
+  // One copy instruction covers 1024 / kRowBytes rows, and the bank swizzle repeats
+  // every 16 rows, so the lane offsets of a wave's copies repeat every kOffsetPeriod
+  // instructions; the repeats differ only by 16 rows, which goes into the descriptor.
+  static constexpr int kOffsetPeriod = kRowBytes / 64;
+  static_assert(4 * kBytes >= 2 * kMaxBlocks, "the two key-block maps must fit in the tile buffers");
 };
 
 // Bank swizzle. The LDS has 64 four-byte banks, so a 256-byte span is one bank cycle:
@@ -167,24 +180,25 @@ struct WaveState {
   int nb, n, row_bytes, wi, lane, hl;
   float c;
   // per-lane offsets
-  int copy_off[T::kCopiesPerWave];
-  int k_rd, k_sw, v_rd, v_sw0, v_sw1, v_ch;
+  int copy_off[T::kOffsetPeriod];
+  // LDS read offsets of the MFMA operands: a lane part (base) plus a swizzle term that
+  // is XORed with the step index (x); see the prologue.
+  int k_base, k_x, v_base0, v_x0, v_base1, v_x1;
   // Q^T fragments (bf16 pairs; kept as dwords so the struct is a valid host type too)
   u32x4 qf[D / 16];
   // softmax state
   f32x16 oacc[D / 32];
   float m_run, l_run;
+  bool first;  // no tile of this wave's rows has been through the softmax yet
 };
 
-// A pending copy of one K or V tile (128 rows) into a group buffer: this wave's quarter
-// of it, issued one 1 KiB instruction at a time so that the copies can be spread over
-// the compute instead of stalling the wave in one burst.
-// A copy that is not wanted (on = false) gets a descriptor of zero bytes: its loads
-// write zeros into the buffer, which is not read again before its next real copy.
-// That keeps the copy code free of branches, so the scheduler can keep it interleaved.
+// A pending copy of one K or V tile (128 rows) into a buffer: this wave's quarter of it,
+// issued one 1 KiB instruction at a time.
 template <int D>
 struct Stage {
-  i32x4 desc;
+  // One descriptor per run of kOffsetPeriod instructions: run j starts 16 j rows into the
+  // tile, so its lane offsets are those of run 0.
+  i32x4 desc[Tile<D>::kCopiesPerWave / Tile<D>::kOffsetPeriod];
   uint32_t lds;
 };
 
@@ -192,12 +206,16 @@ template <int D>
 __device__ __forceinline__ Stage<D> stage_tile(const WaveState<D>& w, char* buf, const char* src,
                                                int kb, bool on) {
   using T = Tile<D>;
-  const bool valid = on && static_cast<unsigned>(kb) < static_cast<unsigned>(w.nb);
-  const int key0 = valid ? kb * kBlock : 0;
-  const int rows = valid ? (w.n - key0 < kBlock ? w.n - key0 : kBlock) : 0;
+  const int key0 = on ? kb * kBlock : 0;
+  const int rows = on ? (w.n - key0 < kBlock ? w.n - key0 : kBlock) : 0;
+  const int bytes = rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0;
   Stage<D> st;
-  st.desc = raw_descriptor(src + static_cast<int64_t>(key0) * w.row_bytes,
-                           rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0);
+#pragma unroll
+  for (int j = 0; j < T::kCopiesPerWave / T::kOffsetPeriod; ++j) {
+    const int skip = 16 * j * w.row_bytes;
+    st.desc[j] = raw_descriptor(src + static_cast<int64_t>(key0) * w.row_bytes + skip,
+                                bytes > skip ? bytes - skip : 0);
+  }
   st.lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)buf)) +
            w.wi * T::kCopiesPerWave * 1024;
   return st;
@@ -206,134 +224,125 @@ __device__ __forceinline__ Stage<D> stage_tile(const WaveState<D>& w, char* buf,
 // Issue copy instruction t of a pending tile copy.
 template <int D>
 __device__ __forceinline__ void stage_issue(const WaveState<D>& w, const Stage<D>& st, int t) {
-  if (t < Tile<D>::kCopiesPerWave) copy_1k(st.desc, st.lds + t * 1024, w.copy_off[t]);
-}
-
-// Issue a whole tile copy at once (prologue only).
-template <int D>
-__device__ __forceinline__ void stage_all(const WaveState<D>& w, char* buf, const char* src, int kb) {
-  const Stage<D> st = stage_tile(w, buf, src, kb, true);
-#pragma unroll
-  for (int t = 0; t < Tile<D>::kCopiesPerWave; ++t) stage_issue(w, st, t);
-}
-
-// PV part of an MFMA phase: O += P(j-1) V(j-1). `sacc` holds P(j-1) packed as bf16
-// (see softmax_tile). V^T fragments go through a two-step ring: the reads for step u + 1
-// are issued before the MFMAs of step u (each step is 2 x D/32 transposed reads, and at
-// most 15 LDS reads can be outstanding). The sched_group_barrier pairs pin that order
-// against the scheduler's wish to save registers.
-template <int D>
-__device__ __forceinline__ void pv_part(WaveState<D>& w, const char* vbuf, const f32x16 (&sacc)[4]) {
   using T = Tile<D>;
-  constexpr int R = 2 * (D / 32);  // transposed reads per step
-  const char* vb = vbuf + w.v_rd;
-  auto read_v = [&](int u, bf16x8 (&vf)[D / 32]) {
+  if (t < T::kCopiesPerWave)
+    copy_1k(st.desc[t / T::kOffsetPeriod], st.lds + t * 1024, w.copy_off[t % T::kOffsetPeriod]);
+}
+
+// The MFMA phase of one group for union tile t: O += P(t-1) V(t-1) (when PV), then
+// S(t) = Q K(t)^T (when QK). LDS reads run ahead of the MFMAs that consume them: the V^T
+// fragments of step u + 1 are read before the MFMAs of step u, the first K fragments are
+// read during the last P V steps, and K fragments of step s + 2 are read after the MFMAs
+// of step s. The sched_group_barrier pairs pin that order against the scheduler's wish to
+// save registers. Each PV step is 2 x D/32 transposed reads; at most 15 LDS reads can be
+// outstanding per wave.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void mfma_phase(WaveState<D>& w, const char* vbuf, const char* kbuf,
+                                           const bf16x8 (&pk)[8], f32x16 (&sacc)[4]) {
+  using T = Tile<D>;
+  constexpr int NDB = D / 32;  // d tiles of O^T
+  constexpr int NS = D / 16;   // k-steps of S^T
+  constexpr int R = 2 * NDB;   // transposed reads per PV step
+  // The swizzle terms go through an empty asm so that the compiler recomputes the read
+  // addresses in every phase (a few XORs) instead of keeping 2 x 8 of them in registers
+  // across the loop.
+  int vx0 = w.v_x0, vx1 = w.v_x1, kx = w.k_x;
+  asm volatile("" : "+v"(vx0), "+v"(vx1), "+v"(kx));
+  const char* vb0 = vbuf + w.v_base0;
+  const char* vb1 = vbuf + w.v_base1;
+  const char* kb = kbuf + w.k_base;
+  auto read_v = [&](int u, bf16x8 (&vf)[NDB]) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const char* p0 = vb + 16 * u * T::kRowBytes;
+    for (int db = 0; db < NDB; ++db) {
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(p0 + (((4 * db + w.v_ch) ^ w.v_sw0) << 4)));
+          (lds_i16x4*)(vb0 + 16 * u * T::kRowBytes + ((db << 6) ^ vx0)));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(p0 + 8 * T::kRowBytes + (((4 * db + w.v_ch) ^ w.v_sw1) << 4)));
+          (lds_i16x4*)(vb1 + 16 * u * T::kRowBytes + ((db << 6) ^ vx1)));
       vf[db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
                                        __builtin_bit_cast(bf16x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  bf16x8 vf[2][D / 32];
-  read_v(0, vf[0]);
-  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {  // u = 2g + s2: 16 keys of the contraction
-    if (u + 1 < 8) {
-      read_v(u + 1, vf[(u + 1) & 1]);
-      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // reads of step u + 1
-    }
-    const f32x4 packed = {sacc[u >> 1][4 * (u & 1) + 0], sacc[u >> 1][4 * (u & 1) + 1],
-                          sacc[u >> 1][4 * (u & 1) + 2], sacc[u >> 1][4 * (u & 1) + 3]};
-    const bf16x8 pu = __builtin_bit_cast(bf16x8, packed);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u & 1][db], pu, w.oacc[db], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);  // then the MFMAs of step u
-  }
-}
-
-// QK part of an MFMA phase: S(j) = Q K(j)^T into `sacc`. The K fragments go through a
-// two-step ring: the reads for k-step s + 2 are issued right after the MFMAs of step s
-// have taken their operands, so 8 reads are in flight while MFMAs run (pinned the same
-// way).
-template <int D>
-__device__ __forceinline__ void qk_part(WaveState<D>& w, const char* kbuf, f32x16 (&sacc)[4]) {
-  using T = Tile<D>;
-  constexpr int S = D / 16;
-  const char* kbp = kbuf + w.k_rd;
   auto read_k = [&](int s, bf16x8 (&kf)[4]) {
-    const int ch = ((2 * s + w.hl) ^ w.k_sw) << 4;
+    const int ch = (s << 5) ^ kx;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      kf[g] = *reinterpret_cast<const bf16x8*>(kbp + g * 32 * T::kRowBytes + ch);
+      kf[g] = *reinterpret_cast<const bf16x8*>(kb + g * 32 * T::kRowBytes + ch);
   };
   bf16x8 kf[2][4];
-  read_k(0, kf[0]);
-  read_k(1, kf[1]);
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 initial reads
+  if constexpr (PV) {
+    bf16x8 vf[2][NDB];
+    read_v(0, vf[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
+    for (int u = 0; u < 8; ++u) {  // 16 keys of the contraction per step
+      if (u + 1 < 8) {
+        read_v(u + 1, vf[(u + 1) & 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // reads of step u + 1
+      }
+      if constexpr (QK) {
+        if (u == 6) {
+          read_k(0, kf[0]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        } else if (u == 7) {
+          read_k(1, kf[1]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+      }
 #pragma unroll
-    for (int g = 0; g < 4; ++g)  // the first k-step takes an inline zero accumulator
-      sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          kf[s & 1][g], __builtin_bit_cast(bf16x8, w.qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs of step s
-    if (s + 2 < S) {
-      read_k(s + 2, kf[s & 1]);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the reads of step s + 2
+      for (int db = 0; db < NDB; ++db)
+        w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u & 1][db], pk[u], w.oacc[db], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NDB, 0);  // then the MFMAs of step u
+    }
+  }
+  if constexpr (QK) {
+    if constexpr (!PV) {
+      read_k(0, kf[0]);
+      read_k(1, kf[1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 initial reads
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)  // the first k-step takes an inline zero accumulator
+        sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kf[s & 1][g], __builtin_bit_cast(bf16x8, w.qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs of step s
+      if (s + 2 < NS) {
+        read_k(s + 2, kf[s & 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the reads of step s + 2
+      }
     }
   }
 }
 
-// Softmax of tile j (column kb): mask padding keys, find the row max, rescale O and l
-// when the max moves, and turn S(j) into P(j). P(j) is written back over S(j): the 8 bf16
-// of P for (g, s2), made from sacc[g][8 s2 .. 8 s2 + 7], are packed into the dwords
-// sacc[g][4 s2 .. 4 s2 + 3], so S and P share the same 64 registers. `hook(u)` runs
-// after each eighth of the work (it issues tile copies).
-template <int D, typename Hook>
-__device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&sacc)[4],
-                                             Hook&& hook) {
-  if (static_cast<unsigned>(kb) >= static_cast<unsigned>(w.nb)) {
-    // Out-of-range column: the tile contributes nothing (P = 0).
-#pragma unroll
-    for (int g = 0; g < 4; ++g) sacc[g] = f32x16{};
-#pragma unroll
-    for (int u = 0; u < 8; ++u) hook(u);
-    return;
-  }
-  const int key_lim = w.n - kb * kBlock;  // keys at or past this index are padding
-  if (key_lim < kBlock) {
-    // Key of accumulator entry (g, i) is 32g + 8(i/4) + (i%4) + 4hl: compare the
-    // constant part against one per-lane limit.
-    const int lim = key_lim - 4 * w.hl;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * g + 8 * (i >> 2) + (i & 3) >= lim) sacc[g][i] = -INFINITY;
-  }
+template <int D>
+__device__ __forceinline__ void run_mfma(WaveState<D>& w, bool pv, bool qk, const char* vbuf,
+                                         const char* kbuf, const bf16x8 (&pk)[8],
+                                         f32x16 (&sacc)[4]) {
+  if (pv) mfma_phase<D, true, false>(w, vbuf, kbuf, pk, sacc);
+  if (qk) mfma_phase<D, false, true>(w, vbuf, kbuf, pk, sacc);
+}
+
+// Row maximum of c * S over this wave's tile (both half-waves), base-2 units.
+template <int D>
+__device__ __forceinline__ float tile_max(const WaveState<D>& w, const f32x16 (&sacc)[4]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[g][i]);
-  const float m_tile = halves_max(mx) * w.c;
-  if (__builtin_amdgcn_ballot_w64(m_tile > w.m_run + kRescaleThreshold) != 0) {
-    const float m_new = fmaxf(w.m_run, m_tile);
-    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);
-    w.m_run = m_new;
-    w.l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) w.oacc[i] *= alpha;
-  }
+  return halves_max(mx) * w.c;
+}
+
+// p = 2^(c s - m) for this lane's 64 scores, packed as bf16 into pk (the B operands of
+// the PV steps: pk[u] holds the 8 p of accumulator entries 8 (u & 1) .. + 7 of S^T block
+// u >> 1). Returns the lane's sum of the bf16-rounded p. hook(u) runs after each step.
+template <int D, typename Hook>
+__device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sacc)[4],
+                                        bf16x8 (&pk)[8], Hook&& hook) {
   const float neg_m = -w.m_run;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  float lt = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int g = u >> 1, s2 = u & 1;
@@ -341,116 +350,140 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
       p8[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + jj], w.c, neg_m));
-    const bf16x8 pu = __builtin_convertvector(p8, bf16x8);
+    pk[u] = __builtin_convertvector(p8, bf16x8);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const bf16x2 pair = {pu[2 * jj], pu[2 * jj + 1]};
-      w.l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, w.l_run, false);
+      const bf16x2 pair = {pk[u][2 * jj], pk[u][2 * jj + 1]};
+      lt = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lt, false);
     }
-    const f32x4 packed = __builtin_bit_cast(f32x4, pu);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sacc[g][4 * s2 + e] = packed[e];
     hook(u);
   }
+  return lt;
 }
 
-// Ascending merge of two sorted CSR rows, the key-block list a workgroup walks. The
-// state is the same in every lane (it lives in scalar registers); INT_MAX marks an
-// exhausted row.
-struct Merge {
-  const int32_t* col;
-  int ia, a_end, ib, b_end;
-  int pa, pb;  // next entry of each row
-};
-
-__device__ __forceinline__ Merge merge_begin(const int32_t* col, int a0, int a1, int b0, int b1) {
-  Merge m{col, a0, a1, b0, b1, INT_MAX, INT_MAX};
-  if (a0 < a1) m.pa = col[a0];
-  if (b0 < b1) m.pb = col[b0];
-  return m;
-}
-
-// The next key block of the union and which rows hold it; false when both are done.
-__device__ __forceinline__ bool merge_next(Merge& m, int& kb, bool& in_a, bool& in_b) {
-  kb = m.pa < m.pb ? m.pa : m.pb;
-  if (kb == INT_MAX) return false;
-  in_a = m.pa == kb;
-  in_b = m.pb == kb;
-  if (in_a) m.pa = ++m.ia < m.a_end ? m.col[m.ia] : INT_MAX;
-  if (in_b) m.pb = ++m.ib < m.b_end ? m.col[m.ib] : INT_MAX;
-  return true;
-}
-
-// One union tile as a group sees it.
-struct TileRef {
-  int kb;     // key block
-  bool here;  // the tile exists (index < union length)
-  bool mine;  // ... and belongs to this group's row
-};
-
-// The phase loop of group G (G = 0: query block 2p, G = 1: query block 2p+1). With U the
-// union length, phase 2t is group 0's MFMA phase for tile t and group 1's softmax phase
-// for tile t-1; phase 2t+1 is the other way round. Each phase ends at a workgroup
-// barrier, and both groups pass 2U + 3 of them.
-//   group 0, MFMA t:    O += P(t-1) V(t-1); S(t) = Q K(t)^T
-//   group 0, softmax t: softmax of tile t; copy K(t+1) meanwhile; wait for it
-//   group 1, MFMA t:    O += P(t-1) V(t-1); S(t) = Q K(t)^T; wait for the V(t) copy
-//   group 1, softmax t: softmax of tile t; copy V(t+1) meanwhile
-// Tile t lives in K buffer t % 2 and V buffer t % 2. A copy into a buffer starts only
-// after the barrier that ends the last phase reading its old tile. P(t-1) and S(t) share
-// registers, so P V runs before Q K^T.
-template <int D, int G>
-__device__ __forceinline__ void run_group(WaveState<D>& w, Merge m, char* __restrict__ k0,
-                                          char* __restrict__ k1, char* __restrict__ v0,
-                                          char* __restrict__ v1) {
-  f32x16 sacc[4];  // S(t) after an MFMA phase, P(t) after a softmax phase
-  auto pick = [](int t, char* b0, char* b1) { return (t & 1) ? b1 : b0; };
-  auto fetch = [&](TileRef& r) {
-    bool in_a = false, in_b = false;
-    r.here = merge_next(m, r.kb, in_a, in_b);
-    r.mine = r.here && (G == 0 ? in_a : in_b);
-  };
-  TileRef prev{0, false, false}, cur, next;
-  fetch(cur);
-  fetch(next);
-  if (G == 1) {  // phase 0: copy V(0)
-    if (cur.here) stage_all(w, v0, w.vh, cur.kb);
-    lds_barrier();
+// Softmax of union tile kb: mask padding keys, turn S into P (pk), and fold the tile into
+// the running row sum. The first tile of a wave sets m from its row maximum. Later tiles
+// use the m they find; if a lane's tile sum then exceeds kTileSumLimit (or is not
+// finite), m is moved to the new row maximum, O and l are rescaled and P is redone.
+template <int D, typename Hook>
+__device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&sacc)[4],
+                                             bf16x8 (&pk)[8], Hook&& hook) {
+  const int key_lim = w.n - kb * kBlock;  // keys at or past this index are padding
+  if (key_lim < kBlock) {
+    // Key of accumulator entry (g, i) is 32g + 8(i/4) + (i%4) + 4hl: compare the
+    // constant part against one per-lane limit.
+    // The limit is applied arithmetically, min(s, +inf or -inf), so that the 64 tests
+    // need no lane masks (which would exhaust the scalar registers).
+    const int lim = key_lim - 4 * w.hl;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int pad = (lim - 1 - (32 * g + 8 * (i >> 2) + (i & 3))) >> 31;  // -1: padding
+        sacc[g][i] = fminf(sacc[g][i], __int_as_float(0x7f800000 | (pad & 0x80000000)));
+      }
   }
-  for (int t = 0;; ++t) {
-    // ---- MFMA phase t ----
-    __builtin_amdgcn_s_setprio(1);
-    if (prev.mine) pv_part(w, pick(t - 1, v0, v1), sacc);
-    if (cur.mine) qk_part(w, pick(t, k0, k1), sacc);
-    if (G == 1) wait_copies<0>();  // V(t)
-    lds_barrier();
-    // ---- softmax phase t ----
-    __builtin_amdgcn_s_setprio(0);
-    const Stage<D> st = G == 0 ? stage_tile(w, pick(t + 1, k0, k1), w.kh, next.kb, next.here)
-                               : stage_tile(w, pick(t + 1, v0, v1), w.vh, next.kb, next.here);
-    auto hook = [&](int u) {
-      // Keep the scheduler from bunching the copies: each softmax step's math stays
-      // between its copy instructions.
+  if (w.first) {
+    w.m_run = tile_max(w, sacc);
+    w.first = false;
+  }
+  float lt = tile_p(w, sacc, pk, hook);
+  if (__builtin_amdgcn_ballot_w64(!(lt <= kTileSumLimit)) != 0) {
+    const float m_new = fmaxf(w.m_run, tile_max(w, sacc));
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);
+    w.m_run = m_new;
+    w.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) w.oacc[i] *= alpha;
+    lt = tile_p(w, sacc, pk, [](int) {});
+  }
+  w.l_run += lt;
+}
+
+// Union-list entry bits.
+constexpr uint32_t kInA = 1u << 14, kInB = 1u << 15, kKbMask = kInA - 1;
+
+// The phase loop of group G (G = 0: query block 2p, G = 1: query block 2p+1) over the U
+// union tiles. Phase 2t is group 0's MFMA phase for tile t and group 1's softmax phase
+// for tile t-1; phase 2t+1 is the other way round. Each phase ends at a workgroup
+// barrier, and both groups pass 2U + 2 of them.
+//   group 0, MFMA t (phase 2t):        O += P(t-1) V(t-1); S(t) = Q K(t)^T
+//   group 0, softmax t (phase 2t+1):   softmax of tile t
+//   group 1, MFMA t (phase 2t+1):      O += P(t-1) V(t-1); S(t) = Q K(t)^T; wait for this
+//                                      wave's copies
+//   group 1, softmax t (phase 2t+2):   copy V(t+1) and K(t+2); softmax of tile t
+// Phase 0 is group 1's copy of V(0) and K(1). Tile t lives in K buffer t % 2 and V buffer
+// t % 2; the copies of phase 2t overwrite tiles t-1 (K) and t-2 (V), whose last reads were
+// in phase 2t-1. One loop iteration runs tile t's MFMA phase and then its softmax, so S
+// is live only inside an iteration; P is carried to the next iteration's P V.
+template <int D, int G>
+__device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list, int U,
+                                          char* __restrict__ k0, char* __restrict__ k1,
+                                          char* __restrict__ v0, char* __restrict__ v1) {
+  constexpr uint32_t kMine = G == 0 ? kInA : kInB;
+  bf16x8 pk[8];  // P(t) after a softmax phase
+  auto pick = [](int t, char* b0, char* b1) { return (t & 1) ? b1 : b0; };
+  // List entries are the same in every lane: readfirstlane keeps them (and every branch
+  // on them) scalar.
+  auto entry = [&](int t) -> uint32_t {
+    return t < U ? static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(list[t])) : 0u;
+  };
+  // Group 1's copies of V(t) and K(t + 1), two instructions per softmax step: V in the
+  // first half, K in the second. A copy past the last tile gets a descriptor of zero
+  // bytes: its loads fetch nothing and write zeros into a buffer that is free (it held
+  // tile t-2 or t-1), which keeps the copy code free of branches.
+  auto copies = [&](int t, uint32_t e_t, uint32_t e_t1) {
+    const Stage<D> sv = stage_tile(w, pick(t, v0, v1), w.vh, static_cast<int>(e_t & kKbMask), t < U);
+    const Stage<D> sk =
+        stage_tile(w, pick(t + 1, k0, k1), w.kh, static_cast<int>(e_t1 & kKbMask), t + 1 < U);
+    return [=, &w](int u) {
       __builtin_amdgcn_sched_barrier(0);
-      stage_issue(w, st, u);
+      constexpr int C = Tile<D>::kCopiesPerWave;
+      const int i0 = 2 * u, i1 = 2 * u + 1;
+      stage_issue(w, i0 < C ? sv : sk, i0 < C ? i0 : i0 - C);
+      stage_issue(w, i1 < C ? sv : sk, i1 < C ? i1 : i1 - C);
       __builtin_amdgcn_sched_barrier(0);
     };
-    if (cur.mine) {
-      softmax_tile(w, cur.kb, sacc, hook);
-    } else {
+  };
+  uint32_t e_prev = 0, e_cur = entry(0), e_next = entry(1);
+  if constexpr (G == 1) {
+    // ---- phase 0: copy V(0), K(1) ----
+    const auto hook = copies(0, e_cur, e_next);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) stage_issue(w, st, u);
-    }
-    if (G == 0) wait_copies<0>();  // K(t+1)
+    for (int u = 0; u < 8; ++u) hook(u);
     lds_barrier();
-    if (!cur.here) break;  // phase 2U+1 (group 0) / 2U+2 (group 1) done
-    prev = cur;
-    cur = next;
-    fetch(next);
   }
-  if (G == 0) lds_barrier();  // group 1's last phase
+  for (int t = 0; t <= U; ++t) {
+    const bool prev_mine = (e_prev & kMine) != 0;  // e_prev = 0 for t = 0
+    const bool cur_mine = t < U && (e_cur & kMine) != 0;
+    f32x16 sacc[4];  // S(t)
+    // ---- MFMA phase of tile t ----
+    __builtin_amdgcn_s_setprio(1);
+    run_mfma(w, prev_mine, cur_mine, pick(t - 1, v0, v1), pick(t, k0, k1), pk, sacc);
+    if constexpr (G == 1) wait_copies<0>();  // V(t) and K(t+1) are in LDS
+    lds_barrier();
+    if (t == U) break;
+    // ---- softmax phase of tile t ----
+    __builtin_amdgcn_s_setprio(0);
+    const uint32_t e_next2 = entry(t + 2);
+    if constexpr (G == 0) {
+      if (cur_mine) softmax_tile(w, static_cast<int>(e_cur & kKbMask), sacc, pk, [](int) {});
+    } else {
+      const auto hook = copies(t + 1, e_next, e_next2);
+      if (cur_mine) {
+        softmax_tile(w, static_cast<int>(e_cur & kKbMask), sacc, pk, hook);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) hook(u);
+      }
+    }
+    lds_barrier();
+    e_prev = e_cur;
+    e_cur = e_next;
+    e_next = e_next2;
+  }
+  if constexpr (G == 0) lds_barrier();  // group 1's last phase
   __builtin_amdgcn_s_setprio(0);
-  wait_copies<0>();
 }
 
 template <int D>
@@ -460,12 +493,14 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
     const int32_t* __restrict__ col_idx, int nb, int heads, int n, float c,
     int64_t stride_b, int64_t stride_h, int stride_s) {
   using T = Tile<D>;
-  // Two K and two V buffers at fixed offsets.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes];
+  // Two K and two V buffers at fixed offsets, then the union list.
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + kListBytes];
+  __shared__ int counts[9];  // per-wave sums of the list compaction, then the union length
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
   char* const v0 = smem + 2 * T::kBytes;
   char* const v1 = smem + 3 * T::kBytes;
+  uint16_t* const list = reinterpret_cast<uint16_t*>(smem + 4 * T::kBytes);
 
   // Work mapping. Workgroup ids go to the 8 XCDs round-robin (XCD = id % 8) and are
   // dispatched in id order. Ids [bh * np, (bh + 1) * np) all belong to head bh (np query
@@ -493,6 +528,54 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   const int grp = wave >> 2;       // query block 2 pair + grp
   const int qb = 2 * pair + grp;   // may be nb (no rows) for the last pair of an odd nb
 
+  // ---- union list of the two CSR rows ----
+  // The rows' key blocks are marked in two byte maps over [0, nb) (in the tile buffers,
+  // which are free until the first copy), then every thread compacts a contiguous run
+  // of nb / 512 key blocks into the list at its offset from a workgroup prefix sum. The
+  // list comes out ascending, each block once; column indices outside [0, nb) are
+  // skipped.
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    const int qa = 2 * pair, qbb = 2 * pair + 1;
+    const int a0 = row_ptr[qa], a1 = row_ptr[qa + 1];
+    const int b0 = qbb < nb ? row_ptr[qbb] : 0, b1 = qbb < nb ? row_ptr[qbb + 1] : 0;
+    uint8_t* const fa = reinterpret_cast<uint8_t*>(smem);
+    uint8_t* const fb = fa + kMaxBlocks;
+    for (int i = tid; i < 2 * kMaxBlocks / 16; i += kThreads)
+      reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int i = a0 + tid; i < a1; i += kThreads) {
+      const int x = col_idx[i];
+      if (static_cast<unsigned>(x) < static_cast<unsigned>(nb)) fa[x] = 1;
+    }
+    for (int i = b0 + tid; i < b1; i += kThreads) {
+      const int x = col_idx[i];
+      if (static_cast<unsigned>(x) < static_cast<unsigned>(nb)) fb[x] = 1;
+    }
+    __syncthreads();
+    const int per = (nb + kThreads - 1) / kThreads;
+    const int k_lo = min(tid * per, nb), k_hi = min(k_lo + per, nb);
+    int cnt = 0;
+    for (int kk = k_lo; kk < k_hi; ++kk) cnt += (fa[kk] | fb[kk]) != 0;
+    int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) counts[wv] = incl;
+    __syncthreads();
+    int pos = incl - cnt;
+    for (int w2 = 0; w2 < wv; ++w2) pos += counts[w2];
+    for (int kk = k_lo; kk < k_hi; ++kk) {
+      const uint32_t f = fa[kk] | (fb[kk] << 1);
+      if (f) list[pos++] = static_cast<uint16_t>(kk | (f & 1 ? kInA : 0u) | (f & 2 ? kInB : 0u));
+    }
+    if (tid == kThreads - 1) counts[8] = pos;
+    __syncthreads();  // the list is complete and the byte maps are free again
+  }
+  const int U = counts[8];
+
   WaveState<D> w;
   w.kh = reinterpret_cast<const char*>(k + base);
   w.vh = reinterpret_cast<const char*>(v + base);
@@ -505,6 +588,27 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   const int lq = w.lane & 31;  // query column owned by this lane
   w.hl = w.lane >> 5;          // half-wave
 
+  // ---- tile copies: this wave's quarter of a tile, 1 KiB per instruction ----
+  // Copy t of wave wi fills bytes [(wi * kCopiesPerWave + t) KiB, +1 KiB) of a buffer;
+  // lane l writes 16 bytes at l * 16, i.e. chunk position p of row r, and so loads
+  // global chunk p ^ swz(r) of that row.
+#pragma unroll
+  for (int t = 0; t < T::kOffsetPeriod; ++t) {
+    const int ci = (w.wi * T::kCopiesPerWave + t) * 64 + w.lane;
+    const int row = ci / T::kChunks, p = ci % T::kChunks;
+    w.copy_off[t] = row * w.row_bytes + ((p ^ swz<D>(row)) << 4);
+  }
+
+  // Prologue copy: K of union tile 0, by group 0. The compiler does not see the tile
+  // copies, so a barrier never waits for them by itself: every wait for a copy is
+  // explicit.
+  if (grp == 0 && U > 0) {
+    const int kb0 = __builtin_amdgcn_readfirstlane(list[0]) & kKbMask;
+    const Stage<D> st = stage_tile(w, k0, w.kh, kb0, true);
+#pragma unroll
+    for (int t = 0; t < T::kCopiesPerWave; ++t) stage_issue(w, st, t);
+  }
+
   // ---- Q^T as the MFMA B operand: d = 16s + 8hl .. +7 of this lane's query ----
   {
     const int q0 = qb * kBlock;
@@ -515,62 +619,48 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
 #pragma unroll
     for (int s = 0; s < D / 16; ++s)
       w.qf[s] = buffer_load16(rq, off + s * 32);
-    // Wait for Q here, where the compiler sees it. Otherwise its wait-count bookkeeping
-    // carries the Q loads into the phase loop as pending and waits on the vector-memory
-    // counter there, i.e. on the tile copies, every iteration.
+    // Wait for Q (and the K(0) copy) here, where the compiler sees it. Otherwise its
+    // wait-count bookkeeping carries the Q loads into the phase loop as pending and
+    // waits on the vector-memory counter there, i.e. on the tile copies.
     __builtin_amdgcn_s_waitcnt(0);
   }
 
-  // ---- tile copies: this wave's quarter of a tile, 1 KiB per instruction ----
-  // Copy t of wave wi fills bytes [(wi * kCopiesPerWave + t) KiB, +1 KiB) of a buffer;
-  // lane l writes 16 bytes at l * 16, i.e. chunk position p of row r, and so loads
-  // global chunk p ^ swz(r) of that row.
-#pragma unroll
-  for (int t = 0; t < T::kCopiesPerWave; ++t) {
-    const int ci = (w.wi * T::kCopiesPerWave + t) * 64 + w.lane;
-    const int row = ci / T::kChunks, p = ci % T::kChunks;
-    w.copy_off[t] = row * w.row_bytes + ((p ^ swz<D>(row)) << 4);
-  }
-
   // ---- per-lane LDS read offsets for the MFMA operands (bytes) ----
-  // K (A operand of S^T): row 32g + lq, chunk 2s + hl.
-  w.k_rd = lq * T::kRowBytes;
-  w.k_sw = swz<D>(lq);
+  // K (A operand of S^T): row 32g + lq, chunk 2s + hl at position (2s + hl) ^ swz(lq).
+  // Since 2s + hl = (s << 1) | hl, that position is ((s ^ (swz >> 1)) << 1) |
+  // ((hl ^ swz) & 1): a lane part plus s XORed with a lane constant.
+  {
+    const int sw = swz<D>(lq);
+    w.k_base = lq * T::kRowBytes + (((w.hl ^ sw) & 1) << 4);
+    w.k_x = (sw >> 1) << 5;
+  }
   // V^T (A operand of O^T) via ds_read_b64_tr_b16: in 16-lane group gi, source lane sl
   // points at key 4hl + sl/4 (+ 8 for the second read of a pair, + tile offsets) and
-  // d = 32db + 16(gi&1) + 4(sl&3).
-  const int gi = (w.lane >> 4) & 3, sl = w.lane & 15;
-  const int v_key = 4 * w.hl + (sl >> 2);
-  w.v_rd = v_key * T::kRowBytes + 8 * (sl & 1);
-  w.v_sw0 = swz<D>(v_key);
-  w.v_sw1 = swz<D>(v_key + 8);
-  w.v_ch = 2 * (gi & 1) + ((sl & 3) >> 1);
+  // d = 32db + 16(gi&1) + 4(sl&3), i.e. chunk 4db + ch with ch = 2(gi&1) + (sl&3)/2 < 4,
+  // at position (4db + ch) ^ swz(key) = ((db ^ (swz >> 2)) << 2) | ((ch ^ swz) & 3).
+  {
+    const int gi = (w.lane >> 4) & 3, sl = w.lane & 15;
+    const int key = 4 * w.hl + (sl >> 2);
+    const int ch = 2 * (gi & 1) + ((sl & 3) >> 1);
+    const int sw0 = swz<D>(key), sw1 = swz<D>(key + 8);
+    const int rd = key * T::kRowBytes + 8 * (sl & 1);
+    w.v_base0 = rd + (((ch ^ sw0) & 3) << 4);
+    w.v_x0 = (sw0 & ~3) << 4;
+    w.v_base1 = rd + 8 * T::kRowBytes + (((ch ^ sw1) & 3) << 4);
+    w.v_x1 = (sw1 & ~3) << 4;
+  }
 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) w.oacc[i] = f32x16{};
-  w.m_run = -INFINITY;  // max of c * s used for p, base-2 units
-  w.l_run = 0.f;        // sum of bf16(p) over this lane's keys
+  w.m_run = 0.f;   // reference max of c * s, base-2 units (set by the first tile)
+  w.l_run = 0.f;   // sum of bf16(p) over this lane's keys
+  w.first = true;
 
-  // The two rows' column ranges (the second row is empty past the last query block).
-  const int qa = 2 * pair, qbb = 2 * pair + 1;
-  const int a0 = row_ptr[qa], a1 = row_ptr[qa + 1];
-  const int b0 = qbb < nb ? row_ptr[qbb] : 0, b1 = qbb < nb ? row_ptr[qbb + 1] : 0;
-  const Merge m = merge_begin(col_idx, a0, a1, b0, b1);
-
-  // Prologue: group 0's first K tile. The compiler does not see the tile copies, so a
-  // barrier never waits for them by itself: every wait for a copy is explicit.
-  if (grp == 0) {
-    Merge m0 = m;
-    int kb;
-    bool in_a, in_b;
-    if (merge_next(m0, kb, in_a, in_b)) stage_all(w, k0, w.kh, kb);
-  }
-  wait_copies<0>();
-  __syncthreads();
+  __syncthreads();  // K(0) is in LDS
   if (grp == 0)
-    run_group<D, 0>(w, m, k0, k1, v0, v1);
+    run_group<D, 0>(w, list, U, k0, k1, v0, v1);
   else
-    run_group<D, 1>(w, m, k0, k1, v0, v1);
+    run_group<D, 1>(w, list, U, k0, k1, v0, v1);
 
   // ---- epilogue: O / l, bf16, store rows < n ----
   const float l_tot = halves_sum(w.l_run);
@@ -611,13 +701,15 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
     return RADIAL_ERR_MISALIGNED;
   if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
   const int64_t items = static_cast<int64_t>(batch) * heads * ((nb + 1) / 2);
-  // A tile of 128 rows is addressed with 32-bit byte offsets from its first row.
-  if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
+  // A tile of 128 rows is addressed with 32-bit byte offsets from its first row, and
+  // the union list holds one 16-bit entry per key block.
+  if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock || nb > kMaxBlocks)
+    return RADIAL_ERR_TOO_LARGE;
 
   // Base-2 score scale. It is kept >= FLT_MIN so a padding score of -inf stays -inf
   // after scaling (never -inf * 0 = NaN). For scale = 0 every finite score times FLT_MIN
-  // rounds away against the running max, giving p = 2^-m for each real key: the mean of
-  // V over the key set, which is the scale-0 softmax.
+  // rounds away against m, giving p = 2^-m for each real key: the mean of V over the key
+  // set, which is the scale-0 softmax.
   const float c = fmaxf(scale * kLog2e, FLT_MIN);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<uint32_t>(items)), block(kThreads);
