@@ -326,12 +326,15 @@ __device__ __forceinline__ void run_mfma(WaveState<D>& w, bool pv, bool qk, cons
 // Row maximum of c * S over this wave's tile (both half-waves), base-2 units.
 template <int D>
 __device__ __forceinline__ float tile_max(const WaveState<D>& w, const f32x16 (&sacc)[4]) {
-  float mx = -INFINITY;
+  // Four independent chains (one per S^T block), then a small tree.
+  float mx[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < 4; ++g) {
+    mx[g] = sacc[g][0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[g][i]);
-  return halves_max(mx) * w.c;
+    for (int i = 1; i < 16; ++i) mx[g] = fmaxf(mx[g], sacc[g][i]);
+  }
+  return halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * w.c;
 }
 
 // p = 2^(c s - m) for this lane's 64 scores, packed as bf16 into pk (the B operands of
@@ -342,7 +345,9 @@ __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sa
                                         bf16x8 (&pk)[8], Hook&& hook) {
   const float neg_m = -w.m_run;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  float lt = 0.f;
+  // Four independent partial sums, so that the dot products do not form one long
+  // dependency chain.
+  float lt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int g = u >> 1, s2 = u & 1;
@@ -354,11 +359,11 @@ __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sa
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const bf16x2 pair = {pk[u][2 * jj], pk[u][2 * jj + 1]};
-      lt = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lt, false);
+      lt[jj] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lt[jj], false);
     }
     hook(u);
   }
-  return lt;
+  return (lt[0] + lt[1]) + (lt[2] + lt[3]);
 }
 
 // Softmax of union tile kb: mask padding keys, turn S into P (pk), and fold the tile into
@@ -460,12 +465,12 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
     // ---- MFMA phase of tile t ----
     __builtin_amdgcn_s_setprio(1);
     run_mfma(w, prev_mine, cur_mine, pick(t - 1, v0, v1), pick(t, k0, k1), pk, sacc);
+    const uint32_t e_next2 = entry(t + 2);  // its LDS latency hides behind the MFMAs
     if constexpr (G == 1) wait_copies<0>();  // V(t) and K(t+1) are in LDS
     lds_barrier();
     if (t == U) break;
     // ---- softmax phase of tile t ----
     __builtin_amdgcn_s_setprio(0);
-    const uint32_t e_next2 = entry(t + 2);
     if constexpr (G == 0) {
       if (cur_mine) softmax_tile(w, static_cast<int>(e_cur & kKbMask), sacc, pk, [](int) {});
     } else {
