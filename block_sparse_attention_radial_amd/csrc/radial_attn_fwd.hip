@@ -231,11 +231,12 @@ __device__ __forceinline__ void stage_issue(const WaveState<D>& w, const Stage<D
 
 // The MFMA phase of one group for union tile t: O += P(t-1) V(t-1) (when PV), then
 // S(t) = Q K(t)^T (when QK). LDS reads run ahead of the MFMAs that consume them: the V^T
-// fragments of step u + 1 are read before the MFMAs of step u, the first K fragments are
-// read during the last P V steps, and K fragments of step s + 2 are read after the MFMAs
-// of step s. The sched_group_barrier pairs pin that order against the scheduler's wish to
-// save registers. Each PV step is 2 x D/32 transposed reads; at most 15 LDS reads can be
-// outstanding per wave.
+// fragments of step u + 1 are read while the MFMAs of step u issue (two transposed
+// reads between consecutive MFMAs), and K fragments of step s + 2 are read while the
+// MFMAs of step s issue (one read between consecutive MFMAs). The sched_group_barrier
+// sequences pin that interleaving against the scheduler's wish to save registers or to
+// bunch the reads; spreading the reads keeps the LDS pipe busy without stalling MFMA
+// issue. At most 15 LDS reads can be outstanding per wave.
 template <int D, bool PV, bool QK>
 __device__ __forceinline__ void mfma_phase(WaveState<D>& w, const char* vbuf, const char* kbuf,
                                            const bf16x8 (&pk)[8], f32x16 (&sacc)[4]) {
@@ -275,23 +276,15 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& w, const char* vbuf, co
     __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {  // 16 keys of the contraction per step
-      if (u + 1 < 8) {
-        read_v(u + 1, vf[(u + 1) & 1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // reads of step u + 1
-      }
-      if constexpr (QK) {
-        if (u == 6) {
-          read_k(0, kf[0]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        } else if (u == 7) {
-          read_k(1, kf[1]);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        }
-      }
+      if (u + 1 < 8) read_v(u + 1, vf[(u + 1) & 1]);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         w.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[u & 1][db], pk[u], w.oacc[db], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NDB, 0);  // then the MFMAs of step u
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if (u + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
   }
   if constexpr (QK) {
@@ -306,10 +299,11 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& w, const char* vbuf, co
       for (int g = 0; g < 4; ++g)  // the first k-step takes an inline zero accumulator
         sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             kf[s & 1][g], __builtin_bit_cast(bf16x8, w.qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs of step s
-      if (s + 2 < NS) {
-        read_k(s + 2, kf[s & 1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // then the reads of step s + 2
+      if (s + 2 < NS) read_k(s + 2, kf[s & 1]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (s + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
   }
