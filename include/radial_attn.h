@@ -103,8 +103,9 @@ int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, 
  *
  * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim),
  * UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH, MISALIGNED (q/k/v/o not 16-byte aligned, or a
- * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*nb workgroups above
- * 2^31 - 1), HIP (launch failure).
+ * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*ceil(nb/2) workgroups
+ * above 2^31 - 1, nb above 16352, or a 128-row tile past 2^31 bytes), HIP (launch
+ * failure).
  */
 int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,

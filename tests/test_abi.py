@@ -105,6 +105,10 @@ def fwd(**kw):
     (dict(stride_s=132), MISALIGNED), (dict(stride_h=1000 * 128 + 4), MISALIGNED),
     (dict(batch=1 << 12, heads=1 << 12, seqlen=1 << 20, nb=1 << 13,
           stride_h=(1 << 20) * 128, stride_b=(1 << 32) * 128), TOO_LARGE),
+    # The kernel's union list holds one 16-bit entry per key block: nb <= 16352.
+    (dict(heads=1, seqlen=16353 * 128, nb=16353, stride_h=16353 * 128 * 128,
+          stride_b=16353 * 128 * 128), TOO_LARGE),
+    (dict(stride_s=(1 << 30) // 128 * 2), TOO_LARGE),  # a 128-row tile past 2^31 bytes
 ])
 def test_attn_fwd_validation(kw, code):
     assert fwd(**kw) == code
