@@ -1,0 +1,122 @@
+"""GPU parity on masks and inputs the radial workloads do not produce.
+
+The kernel takes any block CSR (rows ascending), so it is checked on seeded random block
+masks against the fp64 oracle, element by element. Score ranges that force the softmax's
+rescale path (a later tile whose scores exceed the reference maximum by far more than the
+2^20 bound on p) and the opposite case (a first tile far above everything after it) are
+checked the same way. The bar is the one of test_gpu_parity: max-abs 2e-2, mean-abs 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_radial_amd as radial
+from oracle import radial_oracle as ro
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+# When a few keys dominate a row, the row sum l is a sum of a few bf16-rounded p, so
+# ln l is off by up to 2^-9 (relative rounding of p); the fp32 m + log2 l adds about
+# 1e-7 relative on scores of a few hundred. 2^-8 bounds both with room.
+PEAKED_LSE_TOL = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    radial.lib()
+
+
+def f64(x):
+    return x.detach().to("cpu", torch.float64).numpy()
+
+
+def random_csr(nb: int, density: float, rng) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded random block mask: each row keeps its diagonal block plus a random subset."""
+    rows = []
+    for r in range(nb):
+        keep = rng.random(nb) < density
+        keep[r] = True
+        rows.append(np.flatnonzero(keep).astype(np.int32))
+    row_ptr = np.zeros(nb + 1, dtype=np.int32)
+    row_ptr[1:] = np.cumsum([len(x) for x in rows])
+    return row_ptr, np.concatenate(rows)
+
+
+def run_and_check(q, k, v, row_ptr, col_idx, scale, magnitude=1.0, lse_tol=1e-3):
+    mask = radial.Mask(torch.from_numpy(row_ptr), torch.from_numpy(col_idx), 1, q.shape[-2], 1)
+    B, H, n, _ = q.shape
+    lse = torch.empty(B, H, n, dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = ro.attention(f64(q), f64(k), f64(v), row_ptr, col_idx, scale)
+    got = f64(o)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    assert err.max() <= MAX_ABS * magnitude and err.mean() <= MEAN_ABS * magnitude, (
+        err.max(), err.mean())
+    assert np.abs(f64(lse) - ref_lse).max() <= lse_tol
+
+
+@pytest.mark.parametrize("seed,n,D,density", [
+    (0, 128 * 9 + 37, 128, 0.3),   # odd nb: the last pair has one query block
+    (1, 128 * 12, 64, 0.15),
+    (2, 128 * 7 + 1, 128, 0.6),    # one real row in the last block
+    (3, 128 * 16 + 100, 128, 0.05),
+    (4, 128 * 5, 64, 1.0),         # dense
+])
+def test_random_block_masks(seed, n, D, density):
+    rng = np.random.default_rng(seed)
+    nb = (n + 127) // 128
+    row_ptr, col_idx = random_csr(nb, density, rng)
+    g = torch.Generator().manual_seed(seed)
+    q, k, v = (torch.randn(2, 2, n, D, generator=g).to(torch.bfloat16) for _ in range(3))
+    run_and_check(q, k, v, row_ptr, col_idx, D ** -0.5)
+
+
+def test_rescale_path_growing_scores():
+    """Key block j is scaled by 1.6^j, so every few tiles the scores pass the running
+    reference by more than the bound, and the tile is redone after a rescale."""
+    n, D = 128 * 12 + 50, 128
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(1, 2, n, D, generator=g)
+    k = torch.randn(1, 2, n, D, generator=g)
+    v = torch.randn(1, 2, n, D, generator=g)
+    growth = torch.tensor([1.6 ** (t // 128) for t in range(n)]).view(1, 1, n, 1)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k * growth, v))
+    row_ptr, col_idx = ro.full_csr(n)
+    run_and_check(q, k, v, row_ptr, col_idx, D ** -0.5, lse_tol=PEAKED_LSE_TOL)
+
+
+def test_first_tile_dominates():
+    """Key block 0 carries scores far above all others: no rescale, later p underflow."""
+    n, D = 128 * 10, 64
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn(1, 1, n, D, generator=g)
+    k = torch.randn(1, 1, n, D, generator=g)
+    v = torch.randn(1, 1, n, D, generator=g)
+    k[..., :128, :] *= 40.0
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    row_ptr, col_idx = ro.full_csr(n)
+    run_and_check(q, k, v, row_ptr, col_idx, D ** -0.5, lse_tol=PEAKED_LSE_TOL)
+
+
+def test_batched_strided_layout_wan_frames():
+    """B = 2, H = 3 on six Wan frames, with q/k/v stored [B, n, H, D]."""
+    F, S, w0, D = 6, 1560, 1560, 128
+    n = F * S
+    mask = radial.build_mask(F, S, w0)
+    g = torch.Generator().manual_seed(13)
+    base = [torch.randn(2, n, 3, D, generator=g).to(torch.bfloat16) for _ in range(3)]
+    q, k, v = (x.cuda().transpose(1, 2) for x in base)  # [B, H, n, D] views
+    assert q.stride(-1) == 1 and not q.is_contiguous()
+    o = radial.attn_fwd(q, k, v, mask.to("cuda"))
+    torch.cuda.synchronize()
+    rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
+    blocks = [0, 1, 37, mask.nb // 2, mask.nb - 2, mask.nb - 1]
+    ref, _ = ro.attention(f64(q), f64(k), f64(v), rp, ci, D ** -0.5, query_blocks=blocks)
+    rows = np.concatenate([np.arange(b * 128, min(n, b * 128 + 128)) for b in blocks])
+    err = np.abs(f64(o)[..., rows, :] - ref[..., rows, :])
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
