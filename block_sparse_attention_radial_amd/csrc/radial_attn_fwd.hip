@@ -46,14 +46,17 @@
 //    p for some lane exceeds 2^20, i.e. when the scores have grown by about 20 (base 2)
 //    past m. That case is found after the fact from the sum, and the tile is redone
 //    with the new m (O and l rescaled). So the common path has no row maximum. The final
-//    O / l is exact for any m used consistently. The row sum adds the bf16-rounded p,
-//    the same values the PV product multiplies.
+//    O / l is exact for any m used consistently. The row sum adds p in fp32, with plain
+//    adds: v_dot2 (which could add the bf16-rounded p) runs far slower while the other
+//    wave of the SIMD keeps the matrix core busy.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <atomic>
 
 #include "../../include/radial_attn.h"
 
@@ -333,14 +336,13 @@ __device__ __forceinline__ float tile_max(const WaveState<D>& w, const f32x16 (&
 
 // p = 2^(c s - m) for this lane's 64 scores, packed as bf16 into pk (the B operands of
 // the PV steps: pk[u] holds the 8 p of accumulator entries 8 (u & 1) .. + 7 of S^T block
-// u >> 1). Returns the lane's sum of the bf16-rounded p. hook(u) runs after each step.
+// u >> 1). Returns the lane's sum of p (fp32). hook(u) runs after each step.
 template <int D, typename Hook>
 __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sacc)[4],
                                         bf16x8 (&pk)[8], Hook&& hook) {
   const float neg_m = -w.m_run;
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  // Four independent partial sums, so that the dot products do not form one long
-  // dependency chain.
+  // Four independent partial sums (one per step mod 4), each fed by a small tree, so
+  // that the adds do not form one long dependency chain.
   float lt[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -350,11 +352,8 @@ __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sa
     for (int jj = 0; jj < 8; ++jj)
       p8[jj] = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + jj], w.c, neg_m));
     pk[u] = __builtin_convertvector(p8, bf16x8);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const bf16x2 pair = {pk[u][2 * jj], pk[u][2 * jj + 1]};
-      lt[jj] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, lt[jj], false);
-    }
+    const float a0 = p8[0] + p8[1], a1 = p8[2] + p8[3], a2 = p8[4] + p8[5], a3 = p8[6] + p8[7];
+    lt[u & 3] += (a0 + a1) + (a2 + a3);
     hook(u);
   }
   return (lt[0] + lt[1]) + (lt[2] + lt[3]);
@@ -373,14 +372,20 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
     // constant part against one per-lane limit.
     // The limit is applied arithmetically, min(s, +inf or -inf), so that the 64 tests
     // need no lane masks (which would exhaust the scalar registers).
+    // The per-block base goes through an empty asm so that the compiler does not fold
+    // the 64 offsets into 64 distinct constants (scalar registers); the remaining
+    // offsets, 0 .. 27, are inline operands.
     const int lim = key_lim - 4 * w.hl;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g) {
+      int base = lim - 1 - 32 * g;
+      asm volatile("" : "+v"(base));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int pad = (lim - 1 - (32 * g + 8 * (i >> 2) + (i & 3))) >> 31;  // -1: padding
+        const int pad = (base - (8 * (i >> 2) + (i & 3))) >> 31;  // -1: padding
         sacc[g][i] = fminf(sacc[g][i], __int_as_float(0x7f800000 | (pad & 0x80000000)));
       }
+    }
   }
   if (w.first) {
     w.m_run = tile_max(w, sacc);
@@ -485,30 +490,30 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
   __builtin_amdgcn_s_setprio(0);
 }
 
+// One work item: query blocks 2p and 2p+1 of one (batch, head). smem holds two K and
+// two V buffers at fixed offsets, then the union list; counts holds the per-wave sums of
+// the list compaction, then the union length.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, int nb, int heads, int n, float c,
-    int64_t stride_b, int64_t stride_h, int stride_s) {
+__device__ __forceinline__ void run_item(
+    int pid, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
+    const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
+    float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col_idx, int nb, int heads, int n, float c, int64_t stride_b,
+    int64_t stride_h, int stride_s) {
   using T = Tile<D>;
-  // Two K and two V buffers at fixed offsets, then the union list.
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + kListBytes];
-  __shared__ int counts[9];  // per-wave sums of the list compaction, then the union length
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
   char* const v0 = smem + 2 * T::kBytes;
   char* const v1 = smem + 3 * T::kBytes;
   uint16_t* const list = reinterpret_cast<uint16_t*>(smem + 4 * T::kBytes);
 
-  // Work mapping. Workgroup ids go to the 8 XCDs round-robin (XCD = id % 8) and are
-  // dispatched in id order. Ids [bh * np, (bh + 1) * np) all belong to head bh (np query
-  // block pairs per head), so the whole chip works on one or two heads at a time and
-  // their K/V stays in the shared Infinity Cache. Inside a head, the ids that land on
-  // XCD x take one contiguous run of pairs, in order, so neighbouring query blocks
-  // (which read mostly the same K/V tiles) share that XCD's L2.
+  // Work mapping. Item ids are taken by the XCDs round-robin (XCD = id % 8), in id order
+  // on each XCD (see radial_fwd_kernel). Ids [bh * np, (bh + 1) * np) all belong to head
+  // bh (np query block pairs per head), so the whole chip works on one or two heads at a
+  // time and their K/V stays in the shared Infinity Cache. Inside a head, the ids that
+  // land on XCD x take one contiguous run of pairs, in order, so neighbouring query
+  // blocks (which read mostly the same K/V tiles) share that XCD's L2.
   const int np = (nb + 1) >> 1;
-  const int pid = blockIdx.x;
   const int bh = pid / np;
   const int first_id = bh * np;
   const int xcd = pid & 7;
@@ -520,7 +525,6 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   const int b = bh / heads, h = bh - b * heads;
   const int64_t base = b * stride_b + h * stride_h;
 
-  const int tid = threadIdx.x;
   // The wave index is the same in every lane; saying so lets it live in a scalar
   // register (it feeds M0, the LDS base of the tile copies).
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -681,7 +685,143 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(
   }
 }
 
+// This lane's index in the wave, as a new value on every call: volatile asm is neither
+// hoisted out of loops nor merged, so nothing derived from it stays live across a loop.
+__device__ __forceinline__ int lane_id_fresh() {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return lane;
+}
+
+// Work counters: slot s serves one launch. Entries 0..7 hand out the items of each XCD,
+// entry 8 counts the workgroups that have finished. The loader zero-fills the array,
+// and every launch leaves its slot at zero again.
+constexpr int kCounterSlots = 256;
+__device__ int g_work[kCounterSlots][16];
+
+// Persistent grid: one workgroup per CU (a multiple of 8 workgroups). The hardware
+// deals workgroup ids to the 8 XCDs round-robin, so workgroup i runs on XCD i % 8 and
+// takes the items x, x + 8, x + 16, ... of its XCD x from counter x, in order, until
+// they run out; then it helps the other XCDs, taking from counters x + 1, x + 2, ...
+// (mod 8) in turn. A CU that finishes early takes the next item at once: with one
+// workgroup per item, the dispatcher left CUs idle between workgroups and the last CUs
+// finished whole items after the rest, and under the chip's power limit the XCDs run
+// at different clocks, so a fixed share per XCD left the faster ones idle at the end.
+// The last workgroup to finish resets the counters.
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int64_t stride_b, stride_h;
+  int nb, heads, n, stride_s;
+  float c;
+  int items, slot;
+};
+typedef __attribute__((address_space(4))) const FwdArgs* ArgsPtr;
+
+// Field-by-field copy out of the kernel-argument segment (scalar loads).
+__device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
+  FwdArgs a;
+  a.q = ap->q;
+  a.k = ap->k;
+  a.v = ap->v;
+  a.o = ap->o;
+  a.lse = ap->lse;
+  a.row_ptr = ap->row_ptr;
+  a.col_idx = ap->col_idx;
+  a.stride_b = ap->stride_b;
+  a.stride_h = ap->stride_h;
+  a.nb = ap->nb;
+  a.heads = ap->heads;
+  a.n = ap->n;
+  a.stride_s = ap->stride_s;
+  a.c = ap->c;
+  a.items = ap->items;
+  a.slot = ap->slot;
+  return a;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs args) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + kListBytes];
+  __shared__ int counts[9];
+  __shared__ int next_item;
+  (void)args;
+  // The arguments are read again (scalar loads from the kernel-argument segment) for
+  // every item: kept in scalar registers across the item loop, they would not fit beside
+  // the item's own.
+  ArgsPtr ap = (ArgsPtr)(__builtin_amdgcn_kernarg_segment_ptr());
+  // The thread id is rebuilt for every item from the wave index (a scalar) and the lane
+  // (v_mbcnt), so that no vector register is held across the items.
+  const int wave64 = __builtin_amdgcn_readfirstlane(threadIdx.x) & ~63;
+  __shared__ int lists_done;  // lists x, x + 1, ... found empty (thread 0's state)
+  if (threadIdx.x == 0) lists_done = 0;
+  for (;;) {
+    // New values for the compiler, so that nothing derived from them is hoisted out of
+    // the loop and kept live across the items.
+    asm volatile("" : "+s"(ap));
+    const int tid = wave64 + lane_id_fresh();
+    const FwdArgs a = load_args(ap);
+    const int x = blockIdx.x & 7;
+    if (tid == 0) {
+      int item = -1;
+      for (int e = lists_done; e < 8; ++e) {
+        const int y = (x + e) & 7;
+        const int64_t it = y + 8 * static_cast<int64_t>(atomicAdd(&g_work[a.slot][y], 1));
+        if (it < a.items) {
+          item = static_cast<int>(it);
+          break;
+        }
+        lists_done = e + 1;
+      }
+      next_item = item;
+    }
+    __syncthreads();  // every wave read the previous item's id before run_item's barriers
+    const int item = __builtin_amdgcn_readfirstlane(next_item);
+    if (item < 0) break;
+    run_item<D>(item, tid, smem, counts, a.q, a.k, a.v, a.o, a.lse, a.row_ptr, a.col_idx, a.nb,
+                a.heads, a.n, a.c, a.stride_b, a.stride_h, a.stride_s);
+  }
+  if (wave64 + lane_id_fresh() == 0) {
+    int* const ctr = g_work[ap->slot];
+    __threadfence();  // this workgroup's last takes come before its count
+    if (atomicAdd(&ctr[8], 1) == static_cast<int>(gridDim.x) - 1) {
+#pragma unroll
+      for (int y = 0; y <= 8; ++y) atomicExch(&ctr[y], 0);
+    }
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (cached per device), or -1 on a HIP error.
+int cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = cache[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Counter slots: eager calls rotate through the first half; a call made under stream
+// capture takes one from the second half, so that the slot baked into a graph is not
+// the one of any eager call made in the next 128 calls.
+std::atomic<uint32_t> g_next_slot{0};
+std::atomic<uint32_t> g_next_capture_slot{0};
 
 }  // namespace
 
@@ -704,25 +844,36 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   // the union list holds one 16-bit entry per key block.
   if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock || nb > kMaxBlocks)
     return RADIAL_ERR_TOO_LARGE;
+  const int cus = cu_count();
+  if (cus < 0) return RADIAL_ERR_HIP;
+  // A multiple of 8 workgroups (one per XCD and round), at most one per CU and per item.
+  const int64_t per_xcd = std::min<int64_t>(std::max(cus / 8, 1), (items + 7) / 8);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (st != nullptr && hipStreamIsCapturing(st, &capture) != hipSuccess) return RADIAL_ERR_HIP;
+  constexpr uint32_t kHalf = kCounterSlots / 2;
+  const bool captured = capture == hipStreamCaptureStatusActive;
+  const uint32_t turn = (captured ? g_next_capture_slot : g_next_slot)
+                            .fetch_add(1, std::memory_order_relaxed);
+  const int slot = static_cast<int>((captured ? kHalf : 0u) + turn % kHalf);
 
   // Base-2 score scale. It is kept >= FLT_MIN so a padding score of -inf stays -inf
   // after scaling (never -inf * 0 = NaN). For scale = 0 every finite score times FLT_MIN
   // rounds away against m, giving p = 2^-m for each real key: the mean of V over the key
   // set, which is the scale-0 softmax.
   const float c = fmaxf(scale * kLog2e, FLT_MIN);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<uint32_t>(items)), block(kThreads);
+  const dim3 grid(static_cast<uint32_t>(8 * per_xcd)), block(kThreads);
+  const int it = static_cast<int>(items);
   const auto* qq = static_cast<const __bf16*>(q);
   const auto* kk = static_cast<const __bf16*>(k);
   const auto* vv = static_cast<const __bf16*>(v);
   auto* oo = static_cast<__bf16*>(o);
-  const int ss = static_cast<int>(stride_s);
+  const FwdArgs args{qq, kk, vv, oo, lse, row_ptr, col_idx, stride_b, stride_h, nb, heads,
+                     seqlen, static_cast<int>(stride_s), c, it, slot};
   if (head_dim == 128) {
-    hipLaunchKernelGGL(radial_fwd_kernel<128>, grid, block, 0, st, qq, kk, vv, oo, lse, row_ptr,
-                       col_idx, nb, heads, seqlen, c, stride_b, stride_h, ss);
+    hipLaunchKernelGGL(radial_fwd_kernel<128>, grid, block, 0, st, args);
   } else {
-    hipLaunchKernelGGL(radial_fwd_kernel<64>, grid, block, 0, st, qq, kk, vv, oo, lse, row_ptr,
-                       col_idx, nb, heads, seqlen, c, stride_b, stride_h, ss);
+    hipLaunchKernelGGL(radial_fwd_kernel<64>, grid, block, 0, st, args);
   }
   return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
 }

@@ -20,8 +20,9 @@
  *
  * Conventions for every call:
  *  - The return value is 0 (RADIAL_OK) on success or a negative RADIAL_ERR_* code.
- *    No call aborts, prints, or leaves global state behind.
- *  - All buffers are owned by the caller. The library allocates no memory.
+ *    No call aborts or prints.
+ *  - All buffers are owned by the caller. The library allocates no memory. Its only
+ *    state is described under radial_attn_fwd (work counters in static device memory).
  *  - Every check that can fail is done on the host before any HIP call.
  */
 #ifndef RADIAL_ATTN_H
@@ -98,14 +99,26 @@ int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, 
  *
  * Keys at or past seqlen in the last block are excluded. Rows at or past seqlen are
  * never read or written. Accumulation is fp32, and probabilities are rounded to bf16
- * before the P*V product. Buffers must stay alive and unmodified until the stream work
- * has finished.
+ * before the P*V product (the row sum adds them unrounded). Buffers must stay alive and
+ * unmodified until the stream work has finished.
+ *
+ * Scheduling state. The kernel runs one workgroup per compute unit; the workgroups take
+ * (batch, head, query-block pair) items from atomic counters. The counters live in a
+ * ring of 256 slots in the library's static device memory (one copy per device, zero
+ * when the library loads). Each call uses one slot and its kernel leaves that slot at
+ * zero when it ends. Eager calls rotate through slots 0..127. A call made while
+ * `stream` is being captured into a graph takes its slot from 128..255, so a graph
+ * keeps a slot of its own (the 128 most recent captures never share one). Two kernels
+ * that use the same slot at the same time produce wrong results: at most 128 eager
+ * calls may be in flight on one device at once, and one graph's replays must not
+ * overlap (HIP orders the launches of one graph). Results do not depend on which
+ * workgroup computes which item.
  *
  * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim),
  * UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH, MISALIGNED (q/k/v/o not 16-byte aligned, or a
- * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*ceil(nb/2) workgroups
- * above 2^31 - 1, nb above 16352, or a 128-row tile past 2^31 bytes), HIP (launch
- * failure).
+ * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*ceil(nb/2) work items
+ * above 2^31 - 1, nb above 16352, or a 128-row tile past 2^31 bytes), HIP (the device
+ * query, the capture query or the launch failed).
  */
 int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,

@@ -16,9 +16,10 @@ from oracle import radial_oracle as ro
 pytestmark = pytest.mark.gpu
 
 MAX_ABS, MEAN_ABS = 2e-2, 2e-3
-# When a few keys dominate a row, the row sum l is a sum of a few bf16-rounded p, so
-# ln l is off by up to 2^-9 (relative rounding of p); the fp32 m + log2 l adds about
-# 1e-7 relative on scores of a few hundred. 2^-8 bounds both with room.
+# When a few keys dominate a row, lse rests on a few p: if they were summed after bf16
+# rounding, ln l would be off by up to 2^-9. The fp32 m + log2 l adds about 1e-7
+# relative on scores of a few hundred. 2^-8 bounds both with room, whichever rounding
+# the row sum uses.
 PEAKED_LSE_TOL = 2.0 ** -8
 
 
