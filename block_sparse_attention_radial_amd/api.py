@@ -28,9 +28,12 @@ _SIGNATURES = {
         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "radial_build_mask": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
+    "radial_build_pairs": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_int32)]),
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
-        ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 4 + [ctypes.c_int64] * 3
-        + [ctypes.c_void_p]),
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 4
+        + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_error_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
@@ -77,13 +80,18 @@ def _check(fn: str, code: int):
 
 @dataclass
 class Mask:
-    """Block mask in compressed-row form: int32 row_ptr[nb + 1], col_idx[nnz]."""
+    """Block mask in compressed-row form: int32 row_ptr[nb + 1], col_idx[nnz].
+
+    `pairs` (optional, int32 [npairs, 2]) says which rows the kernel computes together
+    (build_pairs); None means rows 2p and 2p + 1. It changes the time, not the result.
+    """
 
     row_ptr: torch.Tensor
     col_idx: torch.Tensor
     frames: int
     tokens_per_frame: int
     w0: int
+    pairs: torch.Tensor | None = None
 
     @property
     def n(self) -> int:
@@ -103,7 +111,8 @@ class Mask:
 
     def to(self, device) -> "Mask":
         return Mask(self.row_ptr.to(device), self.col_idx.to(device), self.frames,
-                    self.tokens_per_frame, self.w0)
+                    self.tokens_per_frame, self.w0,
+                    None if self.pairs is None else self.pairs.to(device))
 
 
 def mask_dims(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK):
@@ -113,14 +122,33 @@ def mask_dims(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK):
     return nb.value, nnz.value
 
 
-def build_mask(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK) -> Mask:
-    """The static radial block mask for a frames x tokens_per_frame video (host tensors)."""
+def build_pairs(row_ptr: torch.Tensor, col_idx: torch.Tensor,
+                tokens_per_frame: int = 0) -> torch.Tensor:
+    """Pair table (int32 [npairs, 2], host) for a host CSR: rows with many key blocks in
+    common share a workgroup; (a, -1) is a row that runs alone."""
+    row_ptr = row_ptr.to("cpu", torch.int32).contiguous()
+    col_idx = col_idx.to("cpu", torch.int32).contiguous()
+    nb = row_ptr.numel() - 1
+    pairs = torch.empty(max(nb, 1), 2, dtype=torch.int32)
+    npairs = ctypes.c_int32()
+    _check("radial_build_pairs", lib().radial_build_pairs(
+        nb, row_ptr.data_ptr(), col_idx.data_ptr(), tokens_per_frame, pairs.data_ptr(),
+        ctypes.byref(npairs)))
+    return pairs[:npairs.value].clone()
+
+
+def build_mask(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK,
+               pairs: bool = True) -> Mask:
+    """The static radial block mask for a frames x tokens_per_frame video (host tensors),
+    with its pair table unless `pairs` is False."""
     nb, nnz = mask_dims(frames, tokens_per_frame, w0, block)
     row_ptr = torch.empty(nb + 1, dtype=torch.int32)
     col_idx = torch.empty(max(nnz, 1), dtype=torch.int32)
     _check("radial_build_mask", lib().radial_build_mask(
         frames, tokens_per_frame, w0, block, row_ptr.data_ptr(), col_idx.data_ptr(), nnz))
-    return Mask(row_ptr, col_idx[:nnz], frames, tokens_per_frame, w0)
+    col_idx = col_idx[:nnz]
+    table = build_pairs(row_ptr, col_idx, tokens_per_frame) if pairs else None
+    return Mask(row_ptr, col_idx, frames, tokens_per_frame, w0, table)
 
 
 def dense_mask(seqlen: int, device="cpu") -> Mask:
@@ -147,8 +175,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         raise TypeError("q, k, v must be bfloat16")
     if not (q.is_cuda and k.device == q.device and v.device == q.device):
         raise ValueError("q, k, v must be on the same GPU")
-    if mask.row_ptr.device != q.device or mask.col_idx.device != q.device:
+    if mask.row_ptr.device != q.device or mask.col_idx.device != q.device or (
+            mask.pairs is not None and mask.pairs.device != q.device):
         raise ValueError("the mask must be on the same device as q (Mask.to(device))")
+    if mask.pairs is not None and (mask.pairs.dtype != torch.int32 or mask.pairs.dim() != 2
+                                   or mask.pairs.shape[1] != 2
+                                   or not mask.pairs.is_contiguous()):
+        raise ValueError("mask.pairs must be a contiguous int32 [npairs, 2] tensor")
     if q.stride() != k.stride() or q.stride() != v.stride() or q.stride(-1) != 1:
         raise ValueError("q, k, v must share strides with a contiguous last axis")
     B, H, n, D = q.shape
@@ -165,6 +198,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
     _check("radial_attn_fwd", lib().radial_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         None if lse is None else lse.data_ptr(),
-        mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb, float(scale),
+        mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb,
+        None if mask.pairs is None else mask.pairs.data_ptr(),
+        0 if mask.pairs is None else mask.pairs.shape[0], float(scale),
         B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
     return out

@@ -8,13 +8,14 @@
 //     O[rows] = softmax(scale * Q[rows] K[keys]^T) V[keys]
 //   where keys are the real tokens of the key blocks listed in the CSR row qb.
 //
-// Work decomposition. One workgroup of 8 wave64 owns a pair of neighbouring query blocks
-// (2p and 2p+1, 128 rows each) and fills one CU. Its waves form two groups of four; group
-// g owns query block 2p+g, wave i of a group owns its rows 32i .. 32i+31. Both groups
-// walk the union of the two rows' key-block lists in ascending order; a group skips the
-// tiles that are not in its own row. Each K/V tile is thus copied to LDS once and used by
-// both query blocks (neighbouring query blocks share most key blocks). The union list is
-// built once, in the prologue, into LDS: a parallel merge of the two CSR rows.
+// Work decomposition. One workgroup of 8 wave64 fills one CU and computes a pair of
+// query blocks (128 rows each): the pair (a, b) from a host-built pair table that puts
+// together rows with many key blocks in common, or blocks 2p and 2p+1 without one. Its
+// waves form two groups of four; group 0 owns row a, group 1 row b, and wave i of a
+// group owns its rows 32i .. 32i+31. Both groups walk the union of the two rows'
+// key-block lists in ascending order; a group skips the tiles that are not in its own
+// row. Each K/V tile is thus copied to LDS once and used by both query blocks. The union
+// list is built once per pair, in the prologue, into LDS.
 //
 // Ping-pong. A group's work per tile is an MFMA part (P*V of the previous tile, then
 // Q*K^T of this tile) and a VALU part (the softmax). Group 1 runs one phase behind group
@@ -490,16 +491,17 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
   __builtin_amdgcn_s_setprio(0);
 }
 
-// One work item: query blocks 2p and 2p+1 of one (batch, head). smem holds two K and
-// two V buffers at fixed offsets, then the union list; counts holds the per-wave sums of
-// the list compaction, then the union length.
+// One work item: the two query-block rows of pair p (from the pair table, or 2p and
+// 2p+1) of one (batch, head). smem holds two K and two V buffers at fixed offsets, then
+// the union list; counts holds the per-wave sums of the list compaction, then the union
+// length.
 template <int D>
 __device__ __forceinline__ void run_item(
     int pid, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, int nb, int heads, int n, float c, int64_t stride_b,
-    int64_t stride_h, int stride_s) {
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int np, int nb,
+    int heads, int n, float c, int64_t stride_b, int64_t stride_h, int stride_s) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -513,7 +515,6 @@ __device__ __forceinline__ void run_item(
   // time and their K/V stays in the shared Infinity Cache. Inside a head, the ids that
   // land on XCD x take one contiguous run of pairs, in order, so neighbouring query
   // blocks (which read mostly the same K/V tiles) share that XCD's L2.
-  const int np = (nb + 1) >> 1;
   const int bh = pid / np;
   const int first_id = bh * np;
   const int xcd = pid & 7;
@@ -524,12 +525,23 @@ __device__ __forceinline__ void run_item(
   const int pair = seg + ((pid - first_here) >> 3);
   const int b = bh / heads, h = bh - b * heads;
   const int64_t base = b * stride_b + h * stride_h;
+  // The pair's rows. A row outside [0, nb) (the second row of an odd nb's last pair, or
+  // an absent entry of the table) adds no key blocks and has no queries: -1.
+  int ra = 2 * pair, rb = 2 * pair + 1;
+  if (pairs != nullptr) {
+    ra = pairs[2 * pair];
+    rb = pairs[2 * pair + 1];
+  }
+  ra = static_cast<unsigned>(ra) < static_cast<unsigned>(nb) ? ra : -1;
+  rb = static_cast<unsigned>(rb) < static_cast<unsigned>(nb) ? rb : -1;
 
   // The wave index is the same in every lane; saying so lets it live in a scalar
   // register (it feeds M0, the LDS base of the tile copies).
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;       // query block 2 pair + grp
-  const int qb = 2 * pair + grp;   // may be nb (no rows) for the last pair of an odd nb
+  const int grp = wave >> 2;                 // group 0: row ra, group 1: row rb
+  const int q0 = (grp == 0 ? ra : rb) >= 0  // first query of the group's row; n: none
+                     ? (grp == 0 ? ra : rb) * kBlock
+                     : n;
 
   // ---- union list of the two CSR rows ----
   // The rows' key blocks are marked in two byte maps over [0, nb) (in the tile buffers,
@@ -539,9 +551,8 @@ __device__ __forceinline__ void run_item(
   // skipped.
   {
     const int lane = tid & 63, wv = tid >> 6;
-    const int qa = 2 * pair, qbb = 2 * pair + 1;
-    const int a0 = row_ptr[qa], a1 = row_ptr[qa + 1];
-    const int b0 = qbb < nb ? row_ptr[qbb] : 0, b1 = qbb < nb ? row_ptr[qbb + 1] : 0;
+    const int a0 = ra >= 0 ? row_ptr[ra] : 0, a1 = ra >= 0 ? row_ptr[ra + 1] : 0;
+    const int b0 = rb >= 0 ? row_ptr[rb] : 0, b1 = rb >= 0 ? row_ptr[rb + 1] : 0;
     uint8_t* const fa = reinterpret_cast<uint8_t*>(smem);
     uint8_t* const fb = fa + kMaxBlocks;
     for (int i = tid; i < 2 * kMaxBlocks / 16; i += kThreads)
@@ -614,7 +625,6 @@ __device__ __forceinline__ void run_item(
 
   // ---- Q^T as the MFMA B operand: d = 16s + 8hl .. +7 of this lane's query ----
   {
-    const int q0 = qb * kBlock;
     const int rows = n - q0 < kBlock ? n - q0 : kBlock;
     const auto rq = make_rsrc(q + base + static_cast<int64_t>(q0 < n ? q0 : 0) * stride_s,
                               rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0);
@@ -668,7 +678,7 @@ __device__ __forceinline__ void run_item(
   // ---- epilogue: O / l, bf16, store rows < n ----
   const float l_tot = halves_sum(w.l_run);
   const float inv = 1.0f / l_tot;
-  const int qrow = qb * kBlock + w.wi * 32 + lq;
+  const int qrow = q0 + w.wi * 32 + lq;
   if (qrow < n) {
     __bf16* orow = o + base + static_cast<int64_t>(qrow) * stride_s;
 #pragma unroll
@@ -716,8 +726,9 @@ struct FwdArgs {
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
+  const int32_t* pairs;
   int64_t stride_b, stride_h;
-  int nb, heads, n, stride_s;
+  int npairs, nb, heads, n, stride_s;
   float c;
   int items, slot;
 };
@@ -733,6 +744,8 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.lse = ap->lse;
   a.row_ptr = ap->row_ptr;
   a.col_idx = ap->col_idx;
+  a.pairs = ap->pairs;
+  a.npairs = ap->npairs;
   a.stride_b = ap->stride_b;
   a.stride_h = ap->stride_h;
   a.nb = ap->nb;
@@ -784,8 +797,9 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     __syncthreads();  // every wave read the previous item's id before run_item's barriers
     const int item = __builtin_amdgcn_readfirstlane(next_item);
     if (item < 0) break;
-    run_item<D>(item, tid, smem, counts, a.q, a.k, a.v, a.o, a.lse, a.row_ptr, a.col_idx, a.nb,
-                a.heads, a.n, a.c, a.stride_b, a.stride_h, a.stride_s);
+    run_item<D>(item, tid, smem, counts, a.q, a.k, a.v, a.o, a.lse, a.row_ptr, a.col_idx,
+                a.pairs, a.npairs, a.nb, a.heads, a.n, a.c, a.stride_b, a.stride_h,
+                a.stride_s);
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -827,7 +841,7 @@ std::atomic<uint32_t> g_next_capture_slot{0};
 
 extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                    float* lse, const int32_t* row_ptr, const int32_t* col_idx,
-                                   int32_t nb, float scale, int32_t batch, int32_t heads,
+                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale, int32_t batch, int32_t heads,
                                    int32_t seqlen, int32_t head_dim, int64_t stride_b,
                                    int64_t stride_h, int64_t stride_s, void* stream) {
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
@@ -839,7 +853,9 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return RADIAL_ERR_MISALIGNED;
   if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
-  const int64_t items = static_cast<int64_t>(batch) * heads * ((nb + 1) / 2);
+  if (pairs == nullptr) npairs = (nb + 1) / 2;
+  else if (npairs < (nb + 1) / 2 || npairs > nb) return RADIAL_ERR_INVALID_ARG;
+  const int64_t items = static_cast<int64_t>(batch) * heads * npairs;
   // A tile of 128 rows is addressed with 32-bit byte offsets from its first row, and
   // the union list holds one 16-bit entry per key block.
   if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock || nb > kMaxBlocks)
@@ -868,8 +884,9 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   const auto* kk = static_cast<const __bf16*>(k);
   const auto* vv = static_cast<const __bf16*>(v);
   auto* oo = static_cast<__bf16*>(o);
-  const FwdArgs args{qq, kk, vv, oo, lse, row_ptr, col_idx, stride_b, stride_h, nb, heads,
-                     seqlen, static_cast<int>(stride_s), c, it, slot};
+  const FwdArgs args{qq,       kk,       vv,    oo,     lse,    row_ptr,
+                     col_idx,  pairs,    stride_b, stride_h, npairs, nb,
+                     heads,    seqlen,   static_cast<int>(stride_s), c, it, slot};
   if (head_dim == 128) {
     hipLaunchKernelGGL(radial_fwd_kernel<128>, grid, block, 0, st, args);
   } else {

@@ -79,6 +79,39 @@ int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, 
                           int32_t* row_ptr, int32_t* col_idx, int64_t nnz_capacity);
 
 /*
+ * radial_build_pairs — choose the pairs of query-block rows that the forward kernel
+ * computes together. Host code, deterministic.
+ *
+ * The kernel gives each workgroup two rows and walks the union of their key-block
+ * lists: a tile in both rows is copied once for both, a tile in only one leaves the
+ * other row's waves idle for that step. The pairing changes no result (each row's
+ * output depends only on its own key blocks), only the time. This builder scores
+ * candidate partners at row offsets 1, 2, 3 and, when tokens_per_frame > 0, about one
+ * and two frames (round(k * tokens_per_frame / 128) + {-1, 0, 1}, k = 1, 2) by the
+ * number of key blocks they share, and matches greedily, best score first. It follows
+ * "Radial Attention: A Breakthrough in Efficient Long Video Generation", How Radial
+ * Attention Works: the window narrows with frame distance, so rows at the same
+ * spatial position in neighbouring frames share most of their distant-frame blocks.
+ *
+ * nb, row_ptr, col_idx: a block mask in host memory (radial_build_mask's output, or any
+ *            mask with ascending rows; unsorted rows still give a valid pairing).
+ * tokens_per_frame: the frame length of the video, or 0 for no frame structure.
+ * pairs:     caller-owned host array of at least 2 * nb int32. On return, entries 2i and
+ *            2i + 1 (i < *npairs_out) hold the rows (a, b) of pair i with a < b, or
+ *            (a, -1) for a row that runs alone. Every row of [0, nb) appears exactly
+ *            once, and pairs are sorted by a.
+ * npairs_out: receives the pair count, between ceil(nb / 2) and nb (ceil(nb / 2) unless
+ *            rows are left alone).
+ * Cost: about 18 * nnz merge steps. Above 2^28 steps (dense masks of many thousand
+ * blocks) it returns the adjacent pairing (2p, 2p + 1) instead.
+ *
+ * Errors: INVALID_ARG (null pointer, nb <= 0, tokens_per_frame < 0, row_ptr not starting
+ * at 0 or decreasing).
+ */
+int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* col_idx,
+                           int32_t tokens_per_frame, int32_t* pairs, int32_t* npairs_out);
+
+/*
  * radial_attn_fwd — block-sparse softmax attention forward pass on the GPU. The call is
  * asynchronous on `stream`.
  *
@@ -94,6 +127,11 @@ int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, 
  *             nb = ceil(seqlen / 128). Column indices outside [0, nb) are skipped.
  *             Every row must have at least one active block, which is always true of a
  *             radial mask (the diagonal is allowed).
+ * pairs, npairs: optional device copy of radial_build_pairs' output (npairs pairs of
+ *             two int32). Null computes the adjacent pairs (2p, 2p + 1) and ignores
+ *             npairs. A table must list every row once; entries outside [0, nb) are
+ *             treated as absent rows (never read or written), and a row listed twice is
+ *             computed twice.
  * scale:      softmax scale, finite and >= 0 (head_dim^-0.5 is the usual value).
  * stream:     a hipStream_t, or null for the default stream.
  *
@@ -114,17 +152,18 @@ int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, 
  * overlap (HIP orders the launches of one graph). Results do not depend on which
  * workgroup computes which item.
  *
- * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim),
+ * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim, a pair
+ * table with npairs outside [ceil(nb / 2), nb]),
  * UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH, MISALIGNED (q/k/v/o not 16-byte aligned, or a
- * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*ceil(nb/2) work items
+ * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*pairs work items
  * above 2^31 - 1, nb above 16352, or a 128-row tile past 2^31 bytes), HIP (the device
  * query, the capture query or the launch failed).
  */
 int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,
-                        float scale, int32_t batch, int32_t heads, int32_t seqlen,
-                        int32_t head_dim, int64_t stride_b, int64_t stride_h,
-                        int64_t stride_s, void* stream);
+                        const int32_t* pairs, int32_t npairs, float scale, int32_t batch,
+                        int32_t heads, int32_t seqlen, int32_t head_dim, int64_t stride_b,
+                        int64_t stride_h, int64_t stride_s, void* stream);
 
 /* radial_error_string — a static, human-readable text for a return code. */
 const char* radial_error_string(int32_t code);

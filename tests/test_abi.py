@@ -26,7 +26,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(
-        ["radial_mask_dims", "radial_build_mask", "radial_attn_fwd", "radial_error_string"])
+        ["radial_mask_dims", "radial_build_mask", "radial_build_pairs", "radial_attn_fwd",
+         "radial_error_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -84,13 +85,14 @@ def test_build_mask_errors():
 def fwd(**kw):
     """Call radial_attn_fwd with valid-looking defaults, overridden by kw."""
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, row_ptr=0x50000,
-             col_idx=0x60000, nb=8, scale=0.125, batch=1, heads=2, seqlen=1000, head_dim=128,
-             stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_s=128, stream=None)
+             col_idx=0x60000, nb=8, pairs=None, npairs=0, scale=0.125, batch=1, heads=2,
+             seqlen=1000, head_dim=128, stride_b=2 * 1000 * 128, stride_h=1000 * 128,
+             stride_s=128, stream=None)
     a.update(kw)
     return radial.lib().radial_attn_fwd(
         a["q"], a["k"], a["v"], a["o"], a["lse"], a["row_ptr"], a["col_idx"], a["nb"],
-        a["scale"], a["batch"], a["heads"], a["seqlen"], a["head_dim"], a["stride_b"],
-        a["stride_h"], a["stride_s"], a["stream"])
+        a["pairs"], a["npairs"], a["scale"], a["batch"], a["heads"], a["seqlen"],
+        a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -109,6 +111,9 @@ def fwd(**kw):
     (dict(heads=1, seqlen=16353 * 128, nb=16353, stride_h=16353 * 128 * 128,
           stride_b=16353 * 128 * 128), TOO_LARGE),
     (dict(stride_s=(1 << 30) // 128 * 2), TOO_LARGE),  # a 128-row tile past 2^31 bytes
+    # A pair table must hold between ceil(nb / 2) and nb pairs.
+    (dict(pairs=0x70000, npairs=3), INVALID), (dict(pairs=0x70000, npairs=9), INVALID),
+    (dict(pairs=0x70000, npairs=-1), INVALID),
 ])
 def test_attn_fwd_validation(kw, code):
     assert fwd(**kw) == code

@@ -92,3 +92,59 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), r
         assert torch.equal(out2, ref2), r
+
+
+def random_table(nb, rng, singles):
+    """A valid pair table: a random partition of the rows into pairs, `singles` rows alone."""
+    perm = rng.permutation(nb)
+    alone, rest = perm[:singles], perm[singles:]
+    pairs = [sorted(rest[i:i + 2]) for i in range(0, len(rest) - 1, 2)]
+    if len(rest) % 2:
+        alone = list(alone) + [rest[-1]]
+    rows = [(int(a), int(b)) for a, b in pairs] + [(int(a), -1) for a in alone]
+    rows.sort()
+    return torch.tensor(rows, dtype=torch.int32)
+
+
+def test_pairing_does_not_change_results():
+    """Each row's output depends only on its own key blocks, in ascending order: the
+    greedy table, no table (adjacent pairs) and random tables give the same bits."""
+    import numpy as np
+    frames, tokens, w0 = 6, 1560, 1560
+    g = torch.Generator(device="cuda").manual_seed(6)
+    n = frames * tokens
+    q, k, v = (torch.randn(1, 3, n, 128, generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    host = radial.build_mask(frames, tokens, w0)
+    nb = host.nb
+    rng = np.random.default_rng(0)
+    tables = [host.pairs, None, random_table(nb, rng, 0), random_table(nb, rng, 7)]
+    outs = []
+    for t in tables:
+        m = radial.Mask(host.row_ptr, host.col_idx, frames, tokens, w0, t).to("cuda")
+        lse = torch.empty(1, 3, n, dtype=torch.float32, device="cuda")
+        outs.append((radial.attn_fwd(q, k, v, m, lse=lse), lse))
+    torch.cuda.synchronize()
+    for i, (o, lse) in enumerate(outs[1:], 1):
+        assert torch.equal(o, outs[0][0]), i
+        assert torch.equal(lse, outs[0][1]), i
+
+
+def test_row_absent_from_table_is_not_written():
+    """A table entry outside [0, nb) is an absent row: never read or written."""
+    frames, tokens, w0 = 4, 1024, 512
+    q, k, v, _ = problem(8, heads=2, frames=frames, tokens=tokens, w0=w0)
+    host = radial.build_mask(frames, tokens, w0, pairs=False)
+    nb = host.nb  # 32
+    table = torch.tensor([[2 * p, 2 * p + 1] for p in range(nb // 2)], dtype=torch.int32)
+    table[3, 1] = nb + 5   # row 7 is left out
+    ref = radial.attn_fwd(q, k, v, host.to("cuda"))
+    m = radial.Mask(host.row_ptr, host.col_idx, frames, tokens, w0, table).to("cuda")
+    out = torch.full_like(q, 7.0)
+    radial.attn_fwd(q, k, v, m, out=out)
+    torch.cuda.synchronize()
+    rows7 = slice(7 * 128, 8 * 128)
+    assert torch.all(out[:, :, rows7] == 7.0)
+    keep = torch.ones(out.shape[2], dtype=torch.bool)
+    keep[rows7] = False
+    assert torch.equal(out[:, :, keep], ref[:, :, keep])
