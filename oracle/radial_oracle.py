@@ -26,6 +26,9 @@ The pages leave some steps open. This module takes the plainest reading of each:
 3. Block semantics. A block pair is active iff at least one element in it is allowed.
    Every real key of an active block takes part in the softmax. Keys at or past the
    sequence end never take part.
+4. Element semantics (an option of `attention`): the rule of reading 1 also removes the
+   single disallowed entries inside the active blocks, as -inf scores before the
+   softmax. The diagonal is always allowed (W0 >= 1), so no row is left empty.
 
 Parity pins for every function here are in tests/test_oracle.py. Each pin checks the
 function against something other than itself: brute force with exact rationals, closed
@@ -174,7 +177,7 @@ def row_keys(row_ptr, col_idx, qb: int, n: int, block: int = BLOCK) -> np.ndarra
 # --------------------------------------------------------------------------------------
 
 def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
-              query_blocks=None):
+              query_blocks=None, element=None):
     """fp64 softmax attention, each query block over the keys of its active blocks.
 
     q, k, v have shape [..., n, D]; leading dims (batch, heads) share one mask. For query
@@ -183,6 +186,11 @@ def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
     is the same softmax. Returns (o, lse) with lse_i = max x + ln(sum_j p_j), i.e. the
     natural-log log-sum-exp of the scaled scores. Rows of query blocks not listed in
     `query_blocks` are left as NaN.
+
+    element = (tokens_per_frame, w0) switches to element semantics: inside K_i, only the
+    keys j that the element rule allows for (i, j) take part (the SKILL.md page, Step 1:
+    masked positions are -inf before the softmax). The block mask stays the set of
+    blocks visited; the rule removes single entries inside them.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -195,6 +203,11 @@ def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
         rows = slice(qb * block, min(n, (qb + 1) * block))
         keys = row_keys(row_ptr, col_idx, qb, n, block)
         x = scale * (q[..., rows, :] @ np.swapaxes(k[..., keys, :], -1, -2))
+        if element is not None:
+            S, w0 = element
+            qi = np.arange(rows.start, rows.stop, dtype=np.int64)[:, None]
+            kj = keys[None, :]
+            x = np.where(allowed(qi // S, qi % S, kj // S, kj % S, w0), x, -np.inf)
         m = x.max(axis=-1, keepdims=True)
         p = np.exp(x - m)
         denom = p.sum(axis=-1, keepdims=True)

@@ -377,3 +377,80 @@ def test_ragged_padding_keys_excluded():
     rp, ci = ro.full_csr(n, 128)
     keys = ro.row_keys(rp, ci, 0, n)
     assert keys.max() == n - 1 and len(keys) == n
+
+
+# --------------------------------------------------------------------------------------
+# Element semantics (the rule applied inside the active blocks)
+# --------------------------------------------------------------------------------------
+
+def test_element_semantics_bruteforce_rows_fsum():
+    """Exact-rational rule and math.fsum per row, against the oracle's element option."""
+    F, S, w0, block, D = 3, 10, 4, 8, 5
+    n = F * S
+    q, k, v = (rand((n, D), s) for s in (31, 32, 33))
+    rp, ci = ro.csr(ro.block_mask(F, S, w0, block))
+    o, lse = ro.attention(q, k, v, rp, ci, scale=0.7, block=block, element=(S, w0))
+    for i in range(n):
+        keys = [j for j in range(n) if bf_allowed(i, j, S, w0)]
+        x = [0.7 * math.fsum(q[i, c] * k[j, c] for c in range(D)) for j in keys]
+        mx = max(x)
+        p = [math.exp(t - mx) for t in x]
+        l = math.fsum(p)
+        for c in range(D):
+            ref = math.fsum(pj * v[j, c] for pj, j in zip(p, keys)) / l
+            assert abs(o[i, c] - ref) < 1e-12
+        assert abs(lse[i] - (mx + math.log(l))) < 1e-12
+
+
+def test_element_semantics_single_frame_is_torch_sliding_window():
+    """F = 1: the rule is |i - j| < W0, a banded mask built here directly, fed to torch's
+    scaled_dot_product_attention (fp64, CPU)."""
+    n, w0, D = 700, 45, 16
+    q, k, v = (rand((2, n, D), s) for s in (34, 35, 36))
+    rp, ci = ro.csr(ro.block_mask(1, n, w0))
+    o, _ = ro.attention(q, k, v, rp, ci, scale=0.3, element=(n, w0))
+    i = np.arange(n)
+    band_mask = torch.from_numpy(np.abs(i[:, None] - i[None, :]) < w0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v)), attn_mask=band_mask, scale=0.3).numpy()
+    assert np.abs(o - ref).max() < 1e-12
+
+
+def test_element_semantics_element_dense_window_is_dense():
+    """(S - 1) * 2**floor(log2 F) < W0 allows every pair: element semantics is dense."""
+    F, S, D = 5, 60, 8
+    w0 = (S - 1) * 4 + 1
+    n = F * S
+    q, k, v = (rand((n, D), s) for s in (37, 38, 39))
+    rp, ci = ro.csr(ro.block_mask(F, S, w0))
+    o, _ = ro.attention(q, k, v, rp, ci, scale=0.4, element=(S, w0))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x)[None] for x in (q, k, v)), scale=0.4)[0].numpy()
+    assert np.abs(o - ref).max() < 1e-12
+
+
+def test_element_semantics_scale_zero_is_mean_over_allowed_keys():
+    F, S, w0, D = 4, 150, 40, 6
+    n = F * S
+    q, k, v = (rand((n, D), s) for s in (40, 41, 42))
+    rp, ci = ro.csr(ro.block_mask(F, S, w0))
+    o, _ = ro.attention(q, k, v, rp, ci, scale=0.0, element=(S, w0))
+    for i in range(0, n, 23):
+        keys = [j for j in range(n) if bf_allowed(i, j, S, w0)]
+        assert np.abs(o[i] - v[keys].mean(axis=0)).max() < 1e-12
+
+
+def test_element_semantics_removes_entries_block_semantics_keeps():
+    """With a narrow window the two semantics differ, and element semantics never
+    reaches a key that block semantics does not."""
+    F, S, w0, D = 4, 256, 40, 8
+    n = F * S
+    q, k = rand((n, D), 43), rand((n, D), 44)
+    rp, ci = ro.csr(ro.block_mask(F, S, w0))
+    o_blk, _ = ro.attention(q, k, np.eye(n)[:, :n], rp, ci, scale=1.0)
+    o_el, _ = ro.attention(q, k, np.eye(n)[:, :n], rp, ci, scale=1.0, element=(S, w0))
+    assert np.abs(o_blk - o_el).max() > 1e-3
+    assert ((o_el > 0) <= (o_blk > 0)).all()
+    for i in range(0, n, 41):
+        assert set(np.nonzero(o_el[i])[0].tolist()) == {
+            j for j in range(n) if bf_allowed(i, j, S, w0)}
