@@ -2,6 +2,7 @@
 """Radial attention forward pass on one MI355X: effective TFLOP/s on active blocks.
 
     python bench.py [--steps K] [--warmup W] [--workload wan|hunyuan|long4x|small|tiny]
+                    [--element]
 
 A step is one call of the block-sparse forward kernel over the whole workload
 (every batch, head and query block), with Q/K/V already resident in HBM. The static mask
@@ -9,7 +10,8 @@ is built once before timing, and its host build time is reported on its own. Aft
 untimed warm-up steps, exactly K steps are timed with HIP events on the stream the
 kernel runs on, between device synchronisations. The same kernel with the all-active
 mask gives the dense baseline. The CPU oracle is timed beside it on a bounded sample.
-Rank 0 prints one JSON line.
+Rank 0 prints one JSON line. --element times element masking instead (the radial rule on
+single entries inside the active blocks; the oracle runs the same option).
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -72,7 +74,7 @@ def time_launches(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps, wall
 
 
-def cpu_baseline(wl, q, k, v, mask, seconds: float):
+def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False):
     """Time the fp64 CPU oracle over heads 0, 1, ... (each head's query blocks in a seeded
     order) until about `seconds` of work has run. Report the same active-tile flop rate
     as the GPU."""
@@ -94,7 +96,8 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float):
         heads += 1
         t0 = time.perf_counter()
         for qb in order:
-            ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)])
+            ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)],
+                         element=(wl.tokens_per_frame, wl.w0) if element else None)
             blocks += 1
             tiles += int(rp[qb + 1] - rp[qb])
             if elapsed + time.perf_counter() - t0 >= seconds:
@@ -125,6 +128,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--element", action="store_true",
+                    help="element masking inside the active blocks (block semantics otherwise)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale "
                          "HBM traffic counters against a kernel of known size")
@@ -167,10 +172,10 @@ def main():
     log(f"workload {wl.name}: n={wl.n} nb={mask.nb} nnz={mask.nnz} "
         f"({mask.nnz / mask.nb ** 2:.3f} of blocks), mask build {mask_ms:.2f} ms")
 
-    ms, wall = time_launches(lambda: radial.attn_fwd(q, k, v, mdev, out=o),
+    ms, wall = time_launches(lambda: radial.attn_fwd(q, k, v, mdev, out=o, element=args.element),
                              args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"sparse: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
+    log(f"sparse{' (element masking)' if args.element else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
 
     dense = None
     if not args.no_dense:
@@ -186,10 +191,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds)
+        cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds, args.element)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
-    traffic = traffic_bytes(wl.name)
+    traffic = traffic_bytes(wl.name + ("-element" if args.element else ""))
     line = {
         "metric": "active-block attention TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 1 GPU",
         "value": round(tflops, 3),
@@ -208,6 +213,7 @@ def main():
             "head_dim": wl.head_dim, "frames": wl.frames,
             "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
             "block": 128, "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2,
+            "semantics": "element" if args.element else "block",
         },
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "speedup_vs_dense": None if dense is None else round(dense["speedup"], 3),

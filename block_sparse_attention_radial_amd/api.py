@@ -32,7 +32,7 @@ _SIGNATURES = {
                                             ctypes.c_int32, ctypes.c_void_p,
                                             ctypes.POINTER(ctypes.c_int32)]),
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
-        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 4
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 6
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_error_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
@@ -161,13 +161,15 @@ def dense_mask(seqlen: int, device="cpu") -> Mask:
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
              scale: float | None = None, out: torch.Tensor | None = None,
-             lse: torch.Tensor | None = None) -> torch.Tensor:
+             lse: torch.Tensor | None = None, element: bool = False) -> torch.Tensor:
     """Radial attention forward on q, k, v of shape [B, H, n, D] (bf16, on the GPU).
 
     Any layout with a contiguous last axis and strides shared by q, k, v and out works,
     e.g. a [B, n, H, D] buffer viewed as [B, H, n, D]. `lse` (optional, fp32 [B, H, n],
-    contiguous) receives the natural-log log-sum-exp of every row. The call is
-    asynchronous on torch's current stream.
+    contiguous) receives the natural-log log-sum-exp of every row. `element` applies the
+    radial rule to single entries inside the active blocks, with the mask's frame length
+    and W0 (block semantics otherwise). The call is asynchronous on torch's current
+    stream.
     """
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share the shape [B, H, n, D]")
@@ -194,12 +196,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         raise ValueError("lse must be a contiguous float32 [B, H, n] tensor on q's device")
     if scale is None:
         scale = D ** -0.5
+    if element and mask.tokens_per_frame < BLOCK:
+        raise ValueError("element masking needs a frame length of at least 128 tokens")
+    elem_s, elem_w0 = (mask.tokens_per_frame, mask.w0) if element else (0, 0)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check("radial_attn_fwd", lib().radial_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         None if lse is None else lse.data_ptr(),
         mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb,
         None if mask.pairs is None else mask.pairs.data_ptr(),
-        0 if mask.pairs is None else mask.pairs.shape[0], float(scale),
+        0 if mask.pairs is None else mask.pairs.shape[0], float(scale), elem_s, elem_w0,
         B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
     return out

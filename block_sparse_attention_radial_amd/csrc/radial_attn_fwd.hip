@@ -193,7 +193,10 @@ struct WaveState {
   // softmax state
   f32x16 oacc[D / 32];
   float m_run, l_run;
-  bool first;  // no tile of this wave's rows has been through the softmax yet
+  bool first;  // some lane of this wave has no reference m yet
+  // element rule (element masking only): frame length, W0 - 1, and the first query of
+  // the group's row
+  int es, ew0m1, q0;
 };
 
 // A pending copy of one K or V tile (128 rows) into a buffer: this wave's quarter of it,
@@ -338,10 +341,12 @@ __device__ __forceinline__ float tile_max(const WaveState<D>& w, const f32x16 (&
 // p = 2^(c s - m) for this lane's 64 scores, packed as bf16 into pk (the B operands of
 // the PV steps: pk[u] holds the 8 p of accumulator entries 8 (u & 1) .. + 7 of S^T block
 // u >> 1). Returns the lane's sum of p (fp32). hook(u) runs after each step.
-template <int D, typename Hook>
+template <int D, bool E, typename Hook>
 __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sacc)[4],
                                         bf16x8 (&pk)[8], Hook&& hook) {
-  const float neg_m = -w.m_run;
+  // With element masking a lane can still lack m (every key so far masked, m = -inf);
+  // its scores are all -inf too, and m = 0 keeps their p at 0 rather than NaN.
+  const float neg_m = E && w.m_run == -INFINITY ? 0.f : -w.m_run;
   // Four independent partial sums (one per step mod 4), each fed by a small tree, so
   // that the adds do not form one long dependency chain.
   float lt[4] = {0.f, 0.f, 0.f, 0.f};
@@ -360,11 +365,84 @@ __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sa
   return (lt[0] + lt[1]) + (lt[2] + lt[3]);
 }
 
-// Softmax of union tile kb: mask padding keys, turn S into P (pk), and fold the tile into
-// the running row sum. The first tile of a wave sets m from its row maximum. Later tiles
-// use the m they find; if a lane's tile sum then exceeds kTileSumLimit (or is not
-// finite), m is moved to the new row maximum, O and l are rescaled and P is redone.
-template <int D, typename Hook>
+// (a / S, a % S) for 0 <= a < 2^24 and 128 <= S, given inv_s within a few ulp of 1 / S:
+// the float estimate of the quotient is off by at most one, then one correction each way.
+__device__ __forceinline__ void div_frame(int a, int S, float inv_s, int& f, int& s) {
+  f = static_cast<int>(static_cast<float>(a) * inv_s);
+  s = a - f * S;
+  if (s >= S) { ++f; s -= S; }
+  if (s < 0) { --f; s += S; }
+}
+
+// Bits lo .. hi (clamped to 0 .. 31) of a 32-bit word.
+__device__ __forceinline__ uint32_t run_bits(int lo, int hi) {
+  const int a = min(max(lo, 0), 32), b = min(max(hi + 1, 0), 32);  // [a, b)
+  const uint32_t below_b = b >= 32 ? ~0u : (1u << b) - 1u;
+  const uint32_t below_a = a >= 32 ? ~0u : (1u << a) - 1u;
+  return below_b & ~below_a;
+}
+
+// Element masking of union tile kb (the rule of "Radial Attention: A Breakthrough in
+// Efficient Long Video Generation", How Radial Attention Works, applied to single
+// entries, with frame-major coordinates and -inf for masked scores as on the
+// radial-attention-video SKILL.md page, Step 1): key j is allowed for query i iff
+//   |s_i - s_j| <= (W0 - 1) >> floor(log2(|f_i - f_j| + 1)),
+// the integer form of |s_i - s_j| * 2^floor(log2(d + 1)) < W0. A lane holds one query
+// and keys key0 + c, c = 32g + 8(e/4) + e%4 for accumulator entry (g, e), key0 =
+// 128 kb + 4 hl. With S >= 128 those keys lie in at most two frames, kf and kf + 1 (c
+// from cut on), and in each the allowed keys form one run of c: [lo_a, hi_a] and
+// [lo_b, hi_b]. Per group of 32 keys the runs become a 32-bit mask; each entry then
+// takes its bit as 0 or all ones (v_bfe_i32) and selects its score or -inf with it
+// (v_bfi_b32): two VALU instructions and no lane masks. A tile that every lane of the
+// wave keeps whole is left alone.
+template <int D>
+__device__ __forceinline__ void element_mask(const WaveState<D>& w, int kb, f32x16 (&sacc)[4]) {
+  // S and the first query go through an empty asm so that what is derived from them is
+  // recomputed here, per tile, rather than held in registers across the tile loop.
+  int S = w.es, q0 = w.q0;
+  asm volatile("" : "+s"(S), "+s"(q0));
+  // An approximate reciprocal is enough: div_frame corrects the quotient by one.
+  const float inv_s = __builtin_amdgcn_rcpf(static_cast<float>(S));
+  // Frame and spatial index of the wave's first query and of the tile's first key (both
+  // the same in every lane), then this lane's own: one frame wrap at most, as S >= 128.
+  int fq, sq, kf, ks;
+  div_frame(q0 + 32 * w.wi, S, inv_s, fq, sq);
+  div_frame(kb * kBlock, S, inv_s, kf, ks);
+  sq += w.lane & 31;
+  if (sq >= S) { sq -= S; ++fq; }
+  ks += 4 * w.hl;
+  if (ks >= S) { ks -= S; ++kf; }
+  const int cut = S - ks;  // entries with c >= cut are keys of frame kf + 1
+  const int da = fq > kf ? fq - kf : kf - fq;
+  const int db = fq > kf + 1 ? fq - kf - 1 : kf + 1 - fq;
+  const int ra = w.ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(da) + 1u));
+  const int rb = w.ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(db) + 1u));
+  const int base = sq - ks;  // c of the key at the query's own spatial index, frame kf
+  const int lo_a = max(base - ra, 0), hi_a = min(base + ra, cut - 1);
+  const int lo_b = max(base + S - rb, cut), hi_b = base + S + rb;
+  const bool full = lo_a <= 0 && hi_a >= min(cut, 124) - 1 &&
+                    (cut >= 124 || (lo_b <= cut && hi_b >= 123));
+  if (__builtin_amdgcn_ballot_w64(!full) == 0) return;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t bits = run_bits(lo_a - 32 * g, hi_a - 32 * g) |
+                          run_bits(lo_b - 32 * g, hi_b - 32 * g);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t keep =
+          static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(bits), 8 * (e >> 2) + (e & 3), 1));
+      sacc[g][e] = __uint_as_float((keep & __float_as_uint(sacc[g][e])) | (~keep & 0xff800000u));
+    }
+  }
+}
+
+// Softmax of union tile kb: mask padding keys (and, with E, disallowed entries), turn S
+// into P (pk), and fold the tile into the running row sum. The first tile of a wave sets
+// m from its row maximum. Later tiles use the m they find; if a lane's tile sum then
+// exceeds kTileSumLimit (or is not finite), m is moved to the new row maximum, O and l
+// are rescaled and P is redone. With E a lane whose keys have all been masked so far
+// has m = -inf and takes m from the first tile that gives it a finite maximum.
+template <int D, bool E, typename Hook>
 __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&sacc)[4],
                                              bf16x8 (&pk)[8], Hook&& hook) {
   const int key_lim = w.n - kb * kBlock;  // keys at or past this index are padding
@@ -388,19 +466,27 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
       }
     }
   }
+  if constexpr (E) element_mask(w, kb, sacc);
   if (w.first) {
-    w.m_run = tile_max(w, sacc);
-    w.first = false;
+    if constexpr (E) {
+      const float tm = tile_max(w, sacc);
+      if (w.m_run == -INFINITY) w.m_run = tm;
+      w.first = __builtin_amdgcn_ballot_w64(w.m_run == -INFINITY) != 0;
+    } else {
+      w.m_run = tile_max(w, sacc);
+      w.first = false;
+    }
   }
-  float lt = tile_p(w, sacc, pk, hook);
+  float lt = tile_p<D, E>(w, sacc, pk, hook);
   if (__builtin_amdgcn_ballot_w64(!(lt <= kTileSumLimit)) != 0) {
     const float m_new = fmaxf(w.m_run, tile_max(w, sacc));
-    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_new);
+    // A lane still without m (both -inf) keeps its zero O and l.
+    const float alpha = E && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
     w.m_run = m_new;
     w.l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) w.oacc[i] *= alpha;
-    lt = tile_p(w, sacc, pk, [](int) {});
+    lt = tile_p<D, E>(w, sacc, pk, [](int) {});
   }
   w.l_run += lt;
 }
@@ -421,7 +507,7 @@ constexpr uint32_t kInA = 1u << 14, kInB = 1u << 15, kKbMask = kInA - 1;
 // t % 2; the copies of phase 2t overwrite tiles t-1 (K) and t-2 (V), whose last reads were
 // in phase 2t-1. One loop iteration runs tile t's MFMA phase and then its softmax, so S
 // is live only inside an iteration; P is carried to the next iteration's P V.
-template <int D, int G>
+template <int D, int G, bool E>
 __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list, int U,
                                           char* __restrict__ k0, char* __restrict__ k1,
                                           char* __restrict__ v0, char* __restrict__ v1) {
@@ -472,11 +558,11 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
     // ---- softmax phase of tile t ----
     __builtin_amdgcn_s_setprio(0);
     if constexpr (G == 0) {
-      if (cur_mine) softmax_tile(w, static_cast<int>(e_cur & kKbMask), sacc, pk, [](int) {});
+      if (cur_mine) softmax_tile<D, E>(w, static_cast<int>(e_cur & kKbMask), sacc, pk, [](int) {});
     } else {
       const auto hook = copies(t + 1, e_next, e_next2);
       if (cur_mine) {
-        softmax_tile(w, static_cast<int>(e_cur & kKbMask), sacc, pk, hook);
+        softmax_tile<D, E>(w, static_cast<int>(e_cur & kKbMask), sacc, pk, hook);
       } else {
 #pragma unroll
         for (int u = 0; u < 8; ++u) hook(u);
@@ -495,13 +581,14 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
 // 2p+1) of one (batch, head). smem holds two K and two V buffers at fixed offsets, then
 // the union list; counts holds the per-wave sums of the list compaction, then the union
 // length.
-template <int D>
+template <int D, bool E>
 __device__ __forceinline__ void run_item(
     int pid, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int np, int nb,
-    int heads, int n, float c, int64_t stride_b, int64_t stride_h, int stride_s) {
+    int heads, int n, float c, int64_t stride_b, int64_t stride_h, int stride_s, int es,
+    int ew0) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -665,15 +752,20 @@ __device__ __forceinline__ void run_item(
 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) w.oacc[i] = f32x16{};
-  w.m_run = 0.f;   // reference max of c * s, base-2 units (set by the first tile)
-  w.l_run = 0.f;   // sum of bf16(p) over this lane's keys
+  // reference max of c * s, base-2 units (set by the first tile; -inf = not yet, which
+  // element masking can prolong)
+  w.m_run = E ? -INFINITY : 0.f;
+  w.l_run = 0.f;   // sum of p over this lane's keys
   w.first = true;
+  w.es = es;
+  w.ew0m1 = ew0 - 1;
+  w.q0 = q0;
 
   __syncthreads();  // K(0) is in LDS
   if (grp == 0)
-    run_group<D, 0>(w, list, U, k0, k1, v0, v1);
+    run_group<D, 0, E>(w, list, U, k0, k1, v0, v1);
   else
-    run_group<D, 1>(w, list, U, k0, k1, v0, v1);
+    run_group<D, 1, E>(w, list, U, k0, k1, v0, v1);
 
   // ---- epilogue: O / l, bf16, store rows < n ----
   const float l_tot = halves_sum(w.l_run);
@@ -729,6 +821,7 @@ struct FwdArgs {
   const int32_t* pairs;
   int64_t stride_b, stride_h;
   int npairs, nb, heads, n, stride_s;
+  int elem_s, elem_w0;
   float c;
   int items, slot;
 };
@@ -752,13 +845,15 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.heads = ap->heads;
   a.n = ap->n;
   a.stride_s = ap->stride_s;
+  a.elem_s = ap->elem_s;
+  a.elem_w0 = ap->elem_w0;
   a.c = ap->c;
   a.items = ap->items;
   a.slot = ap->slot;
   return a;
 }
 
-template <int D>
+template <int D, bool E>
 __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs args) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + kListBytes];
@@ -797,9 +892,9 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     __syncthreads();  // every wave read the previous item's id before run_item's barriers
     const int item = __builtin_amdgcn_readfirstlane(next_item);
     if (item < 0) break;
-    run_item<D>(item, tid, smem, counts, a.q, a.k, a.v, a.o, a.lse, a.row_ptr, a.col_idx,
-                a.pairs, a.npairs, a.nb, a.heads, a.n, a.c, a.stride_b, a.stride_h,
-                a.stride_s);
+    run_item<D, E>(item, tid, smem, counts, a.q, a.k, a.v, a.o, a.lse, a.row_ptr, a.col_idx,
+                   a.pairs, a.npairs, a.nb, a.heads, a.n, a.c, a.stride_b, a.stride_h,
+                   a.stride_s, a.elem_s, a.elem_w0);
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -841,12 +936,18 @@ std::atomic<uint32_t> g_next_capture_slot{0};
 
 extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                    float* lse, const int32_t* row_ptr, const int32_t* col_idx,
-                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale, int32_t batch, int32_t heads,
+                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
+                                   int32_t element_tokens_per_frame, int32_t element_w0, int32_t batch, int32_t heads,
                                    int32_t seqlen, int32_t head_dim, int64_t stride_b,
                                    int64_t stride_h, int64_t stride_s, void* stream) {
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
   if (batch <= 0 || heads <= 0 || seqlen <= 0 || nb <= 0) return RADIAL_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
+  // Element masking: a frame spans at least one 128-key tile, and W0 >= 1 keeps the
+  // diagonal allowed.
+  if (element_tokens_per_frame != 0 &&
+      (element_tokens_per_frame < kBlock || element_w0 < 1))
+    return RADIAL_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return RADIAL_ERR_UNSUPPORTED_HEAD_DIM;
   if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
   if (stride_s < head_dim || stride_h < 0 || stride_b < 0) return RADIAL_ERR_INVALID_ARG;
@@ -886,11 +987,19 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   auto* oo = static_cast<__bf16*>(o);
   const FwdArgs args{qq,       kk,       vv,    oo,     lse,    row_ptr,
                      col_idx,  pairs,    stride_b, stride_h, npairs, nb,
-                     heads,    seqlen,   static_cast<int>(stride_s), c, it, slot};
+                     heads,    seqlen,   static_cast<int>(stride_s),
+                     element_tokens_per_frame, element_w0, c, it, slot};
+  const bool elem = element_tokens_per_frame != 0;
   if (head_dim == 128) {
-    hipLaunchKernelGGL(radial_fwd_kernel<128>, grid, block, 0, st, args);
+    if (elem)
+      hipLaunchKernelGGL((radial_fwd_kernel<128, true>), grid, block, 0, st, args);
+    else
+      hipLaunchKernelGGL((radial_fwd_kernel<128, false>), grid, block, 0, st, args);
   } else {
-    hipLaunchKernelGGL(radial_fwd_kernel<64>, grid, block, 0, st, args);
+    if (elem)
+      hipLaunchKernelGGL((radial_fwd_kernel<64, true>), grid, block, 0, st, args);
+    else
+      hipLaunchKernelGGL((radial_fwd_kernel<64, false>), grid, block, 0, st, args);
   }
   return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
 }

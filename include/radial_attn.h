@@ -133,6 +133,19 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  *             treated as absent rows (never read or written), and a row listed twice is
  *             computed twice.
  * scale:      softmax scale, finite and >= 0 (head_dim^-0.5 is the usual value).
+ * element_tokens_per_frame, element_w0: 0 for block semantics (every real key of an
+ *             active block takes part). A frame length >= 128 and W0 >= 1 switch on
+ *             element masking: inside the active blocks, key j takes part for query i
+ *             only if |s_i - s_j| * 2^floor(log2(|f_i - f_j| + 1)) < W0, with
+ *             f = t / frame length and s = t % frame length (frame-major tokens), the
+ *             rule of "Radial Attention: A Breakthrough in Efficient Long Video
+ *             Generation", How Radial Attention Works, applied entry by entry, masked
+ *             scores being -inf before the softmax (the radial-attention-video SKILL.md
+ *             page, Step 1). Pass the mask's own frame length and W0; a key the rule
+ *             allows outside the CSR's blocks is not visited. Every row must keep at
+ *             least one allowed key (the diagonal always is when the CSR comes from
+ *             radial_build_mask with the same frame length and W0); a row with none
+ *             gets NaN.
  * stream:     a hipStream_t, or null for the default stream.
  *
  * Keys at or past seqlen in the last block are excluded. Rows at or past seqlen are
@@ -153,7 +166,8 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  * workgroup computes which item.
  *
  * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim, a pair
- * table with npairs outside [ceil(nb / 2), nb]),
+ * table with npairs outside [ceil(nb / 2), nb], element masking with a frame length
+ * other than 0 below 128 or with W0 < 1),
  * UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH, MISALIGNED (q/k/v/o not 16-byte aligned, or a
  * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*pairs work items
  * above 2^31 - 1, nb above 16352, or a 128-row tile past 2^31 bytes), HIP (the device
@@ -161,7 +175,8 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  */
 int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,
-                        const int32_t* pairs, int32_t npairs, float scale, int32_t batch,
+                        const int32_t* pairs, int32_t npairs, float scale,
+                        int32_t element_tokens_per_frame, int32_t element_w0, int32_t batch,
                         int32_t heads, int32_t seqlen, int32_t head_dim, int64_t stride_b,
                         int64_t stride_h, int64_t stride_s, void* stream);
 

@@ -85,13 +85,15 @@ def test_build_mask_errors():
 def fwd(**kw):
     """Call radial_attn_fwd with valid-looking defaults, overridden by kw."""
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, row_ptr=0x50000,
-             col_idx=0x60000, nb=8, pairs=None, npairs=0, scale=0.125, batch=1, heads=2,
+             col_idx=0x60000, nb=8, pairs=None, npairs=0, scale=0.125, elem_s=0, elem_w0=0,
+             batch=1, heads=2,
              seqlen=1000, head_dim=128, stride_b=2 * 1000 * 128, stride_h=1000 * 128,
              stride_s=128, stream=None)
     a.update(kw)
     return radial.lib().radial_attn_fwd(
         a["q"], a["k"], a["v"], a["o"], a["lse"], a["row_ptr"], a["col_idx"], a["nb"],
-        a["pairs"], a["npairs"], a["scale"], a["batch"], a["heads"], a["seqlen"],
+        a["pairs"], a["npairs"], a["scale"], a["elem_s"], a["elem_w0"], a["batch"], a["heads"],
+        a["seqlen"],
         a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
 
 
@@ -114,6 +116,9 @@ def fwd(**kw):
     # A pair table must hold between ceil(nb / 2) and nb pairs.
     (dict(pairs=0x70000, npairs=3), INVALID), (dict(pairs=0x70000, npairs=9), INVALID),
     (dict(pairs=0x70000, npairs=-1), INVALID),
+    # Element masking needs a frame of at least one tile and W0 >= 1.
+    (dict(elem_s=100, elem_w0=50), INVALID), (dict(elem_s=-5, elem_w0=50), INVALID),
+    (dict(elem_s=256, elem_w0=0), INVALID),
 ])
 def test_attn_fwd_validation(kw, code):
     assert fwd(**kw) == code
