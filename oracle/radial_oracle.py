@@ -29,6 +29,9 @@ The pages leave some steps open. This module takes the plainest reading of each:
 4. Element semantics (an option of `attention`): the rule of reading 1 also removes the
    single disallowed entries inside the active blocks, as -inf scores before the
    softmax. The diagonal is always allowed (W0 >= 1), so no row is left empty.
+5. The backward pass (`attention_backward`) is the vector-Jacobian product of the
+   same softmax attention over the same key sets; the pages use it for LoRA
+   fine-tuning (the SKILL.md page, Step 4: loss.backward() through the attention).
 
 Parity pins for every function here are in tests/test_oracle.py. Each pin checks the
 function against something other than itself: brute force with exact rationals, closed
@@ -214,6 +217,60 @@ def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
         o[..., rows, :] = (p @ v[..., keys, :]) / denom
         lse[..., rows] = (m + np.log(denom))[..., 0]
     return o, lse
+
+
+def attention_backward(q, k, v, do, row_ptr, col_idx, scale: float, block: int = BLOCK,
+                       element=None):
+    """fp64 gradients (dq, dk, dv) of `attention` for the output cotangent do.
+
+    This is the vector-Jacobian product of softmax attention over the same key sets
+    (the radial-attention-video SKILL.md page, Step 4, fine-tunes through the attention
+    with loss.backward()). Per query row i with key set K_i, P = softmax(scale q K^T)
+    over K_i and o_i = P V:
+        dv_j += P_ij do_i,    dP_ij = <do_i, v_j>,    dS_ij = P_ij (dP_ij - <do_i, o_i>),
+        dq_i = scale sum_j dS_ij k_j,    dk_j += scale dS_ij q_i.
+    The identity sum_j P_ij dP_ij = <do_i, o_i> is what makes dS the softmax Jacobian
+    applied to dP. `element` is as in `attention`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n = q.shape[-2]
+    nb = num_blocks(n, block)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for qb in range(nb):
+        rows = slice(qb * block, min(n, (qb + 1) * block))
+        keys = row_keys(row_ptr, col_idx, qb, n, block)
+        x = scale * (q[..., rows, :] @ np.swapaxes(k[..., keys, :], -1, -2))
+        if element is not None:
+            S, w0 = element
+            qi = np.arange(rows.start, rows.stop, dtype=np.int64)[:, None]
+            kj = keys[None, :]
+            x = np.where(allowed(qi // S, qi % S, kj // S, kj % S, w0), x, -np.inf)
+        p = np.exp(x - x.max(axis=-1, keepdims=True))
+        p /= p.sum(axis=-1, keepdims=True)
+        o = p @ v[..., keys, :]
+        g = do[..., rows, :]
+        dp = g @ np.swapaxes(v[..., keys, :], -1, -2)
+        ds = p * (dp - (g * o).sum(axis=-1, keepdims=True))
+        dq[..., rows, :] = scale * (ds @ k[..., keys, :])
+        dk[..., keys, :] += scale * (np.swapaxes(ds, -1, -2) @ q[..., rows, :])
+        dv[..., keys, :] += np.swapaxes(p, -1, -2) @ g
+    return dq, dk, dv
+
+
+def transpose_csr(row_ptr, col_idx, nb: int):
+    """Column-major view of a block mask: for key block c, the query blocks whose rows
+    list it, ascending (the CSR of the transposed mask)."""
+    rows = np.repeat(np.arange(nb, dtype=np.int64), np.diff(np.asarray(row_ptr)))
+    cols = np.asarray(col_idx, dtype=np.int64)
+    order = np.lexsort((rows, cols))
+    col_ptr = np.zeros(nb + 1, dtype=np.int32)
+    np.add.at(col_ptr, cols + 1, 1)
+    return np.cumsum(col_ptr).astype(np.int32), rows[order].astype(np.int32)
 
 
 def full_csr(n: int, block: int = BLOCK):

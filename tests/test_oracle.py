@@ -454,3 +454,92 @@ def test_element_semantics_removes_entries_block_semantics_keeps():
     for i in range(0, n, 41):
         assert set(np.nonzero(o_el[i])[0].tolist()) == {
             j for j in range(n) if bf_allowed(i, j, S, w0)}
+
+
+# --------------------------------------------------------------------------------------
+# Backward (dq, dk, dv)
+# --------------------------------------------------------------------------------------
+
+def test_backward_matches_finite_differences():
+    """Central differences of L = sum(o * do) in every input entry, on a tiny shape
+    with a sparse block mask."""
+    F, S, w0, block, D = 3, 6, 2, 4, 3
+    n = F * S
+    q, k, v, do = (rand((n, D), s) for s in (51, 52, 53, 54))
+    rp, ci = ro.csr(ro.block_mask(F, S, w0, block))
+    dq, dk, dv = ro.attention_backward(q, k, v, do, rp, ci, scale=0.8, block=block)
+
+    def loss(q_, k_, v_):
+        o, _ = ro.attention(q_, k_, v_, rp, ci, scale=0.8, block=block)
+        return math.fsum((o * do).ravel())
+
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v, name: xp}
+            args_m = {"q": q, "k": k, "v": v, name: xm}
+            num = (loss(args_p["q"], args_p["k"], args_p["v"])
+                   - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+            assert abs(num - grad[idx]) < 1e-6, (name, idx, num, grad[idx])
+
+
+def torch_sdpa_grads(q, k, v, do, scale, attn_mask=None):
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=attn_mask,
+                                                         scale=scale)
+    o.backward(torch.from_numpy(do))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def test_backward_dense_matches_torch_autograd():
+    n, D = 300, 16
+    q, k, v, do = (rand((2, n, D), s) for s in (55, 56, 57, 58))
+    rp, ci = ro.full_csr(n, 128)
+    got = ro.attention_backward(q, k, v, do, rp, ci, scale=0.3)
+    ref = torch_sdpa_grads(q, k, v, do, 0.3)
+    for a, b in zip(got, ref):
+        assert np.abs(a - b).max() < 1e-11
+
+
+def test_backward_element_single_frame_matches_torch_band():
+    n, w0, D = 400, 30, 8
+    q, k, v, do = (rand((n, D), s) for s in (59, 60, 61, 62))
+    rp, ci = ro.csr(ro.block_mask(1, n, w0))
+    got = ro.attention_backward(q, k, v, do, rp, ci, scale=0.5, element=(n, w0))
+    i = np.arange(n)
+    band = torch.from_numpy(np.abs(i[:, None] - i[None, :]) < w0)
+    ref = torch_sdpa_grads(q[None], k[None], v[None], do[None], 0.5, attn_mask=band)
+    for a, b in zip(got, ref):
+        assert np.abs(a - b[0]).max() < 1e-11
+
+
+def test_backward_closed_forms():
+    """Rows of P sum to one, so sum_j dv_j = sum_i do_i; scale 0 gives dq = dk = 0."""
+    F, S, w0 = 4, 200, 20
+    n = F * S
+    q, k, v, do = (rand((n, 8), s) for s in (63, 64, 65, 66))
+    rp, ci = ro.csr(ro.block_mask(F, S, w0))
+    dq, dk, dv = ro.attention_backward(q, k, v, do, rp, ci, scale=0.25)
+    assert np.abs(dv.sum(axis=0) - do.sum(axis=0)).max() < 1e-10
+    dq0, dk0, dv0 = ro.attention_backward(q, k, v, do, rp, ci, scale=0.0)
+    assert np.abs(dq0).max() == 0 and np.abs(dk0).max() == 0
+    assert np.abs(dv0.sum(axis=0) - do.sum(axis=0)).max() < 1e-10
+
+
+def test_transpose_csr_vs_dense():
+    F, S, w0 = 5, 300, 40
+    bm = ro.block_mask(F, S, w0)
+    rp, ci = ro.csr(bm)
+    cp, ri = ro.transpose_csr(rp, ci, bm.shape[0])
+    rp_t, ci_t = ro.csr(bm.T.copy())
+    assert np.array_equal(cp, rp_t) and np.array_equal(ri, ci_t)
+    # A non-symmetric mask too.
+    rng = np.random.default_rng(5)
+    m = rng.random((23, 23)) < 0.3
+    rp, ci = ro.csr(m)
+    cp, ri = ro.transpose_csr(rp, ci, 23)
+    rp_t, ci_t = ro.csr(m.T.copy())
+    assert np.array_equal(cp, rp_t) and np.array_equal(ri, ci_t)
