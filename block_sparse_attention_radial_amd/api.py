@@ -34,6 +34,10 @@ _SIGNATURES = {
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 6
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_transpose_mask": (ctypes.c_int32, [ctypes.c_int32] + [ctypes.c_void_p] * 4),
+    "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_int32] * 4
+        + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_error_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
@@ -84,6 +88,8 @@ class Mask:
 
     `pairs` (optional, int32 [npairs, 2]) says which rows the kernel computes together
     (build_pairs); None means rows 2p and 2p + 1. It changes the time, not the result.
+    `col_ptr` / `row_idx` (optional) are the transposed mask the backward pass walks;
+    `transposed()` builds them when absent.
     """
 
     row_ptr: torch.Tensor
@@ -92,6 +98,8 @@ class Mask:
     tokens_per_frame: int
     w0: int
     pairs: torch.Tensor | None = None
+    col_ptr: torch.Tensor | None = None
+    row_idx: torch.Tensor | None = None
 
     @property
     def n(self) -> int:
@@ -110,9 +118,24 @@ class Mask:
         return self.row_ptr.device
 
     def to(self, device) -> "Mask":
+        mv = lambda t: None if t is None else t.to(device)  # noqa: E731
         return Mask(self.row_ptr.to(device), self.col_idx.to(device), self.frames,
-                    self.tokens_per_frame, self.w0,
-                    None if self.pairs is None else self.pairs.to(device))
+                    self.tokens_per_frame, self.w0, mv(self.pairs), mv(self.col_ptr),
+                    mv(self.row_idx))
+
+    def transposed(self) -> "Mask":
+        """This mask with col_ptr / row_idx filled in (radial_transpose_mask, on the host,
+        then moved to the mask's device)."""
+        if self.col_ptr is None or self.row_idx is None:
+            rp = self.row_ptr.to("cpu", torch.int32).contiguous()
+            ci = self.col_idx.to("cpu", torch.int32).contiguous()
+            cp = torch.empty(self.nb + 1, dtype=torch.int32)
+            ri = torch.empty(max(ci.numel(), 1), dtype=torch.int32)
+            _check("radial_transpose_mask", lib().radial_transpose_mask(
+                self.nb, rp.data_ptr(), ci.data_ptr(), cp.data_ptr(), ri.data_ptr()))
+            self.col_ptr = cp.to(self.device)
+            self.row_idx = ri[:int(cp[-1])].to(self.device)
+        return self
 
 
 def mask_dims(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK):
@@ -148,7 +171,8 @@ def build_mask(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK,
         frames, tokens_per_frame, w0, block, row_ptr.data_ptr(), col_idx.data_ptr(), nnz))
     col_idx = col_idx[:nnz]
     table = build_pairs(row_ptr, col_idx, tokens_per_frame) if pairs else None
-    return Mask(row_ptr, col_idx, frames, tokens_per_frame, w0, table)
+    # The radial mask is symmetric at block level: its transpose is itself.
+    return Mask(row_ptr, col_idx, frames, tokens_per_frame, w0, table, row_ptr, col_idx)
 
 
 def dense_mask(seqlen: int, device="cpu") -> Mask:
@@ -208,3 +232,69 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         0 if mask.pairs is None else mask.pairs.shape[0], float(scale), elem_s, elem_w0,
         B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
     return out
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             do: torch.Tensor, lse: torch.Tensor, mask: Mask, scale: float | None = None,
+             element: bool = False):
+    """Gradients (dq, dk, dv) of attn_fwd for the output gradient `do`, from the forward's
+    output `o` and log-sum-exp `lse` (all on the GPU; layouts as for attn_fwd). The call
+    is asynchronous on torch's current stream."""
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, do)):
+        raise ValueError("q, k, v, o, do must share the shape [B, H, n, D]")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, do)):
+        raise TypeError("q, k, v, o, do must be bfloat16")
+    if not q.is_cuda or any(t.device != q.device for t in (k, v, o, do, lse)):
+        raise ValueError("every tensor must be on the same GPU")
+    if any(t.stride() != q.stride() for t in (k, v, o, do)) or q.stride(-1) != 1:
+        raise ValueError("q, k, v, o, do must share strides with a contiguous last axis")
+    B, H, n, D = q.shape
+    if lse.shape != (B, H, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [B, H, n] output")
+    mask = mask.transposed()
+    if any(t.device != q.device for t in (mask.row_ptr, mask.col_idx, mask.col_ptr,
+                                          mask.row_idx)):
+        raise ValueError("the mask must be on the same device as q (Mask.to(device))")
+    if scale is None:
+        scale = D ** -0.5
+    if element and mask.tokens_per_frame < BLOCK:
+        raise ValueError("element masking needs a frame length of at least 128 tokens")
+    elem_s, elem_w0 = (mask.tokens_per_frame, mask.w0) if element else (0, 0)
+    dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+                  for _ in range(3))
+    delta = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check("radial_attn_bwd", lib().radial_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+        mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.col_ptr.data_ptr(),
+        mask.row_idx.data_ptr(), mask.nb, float(scale), elem_s, elem_w0,
+        B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
+    return dq, dk, dv
+
+
+class RadialAttentionFunction(torch.autograd.Function):
+    """attn_fwd with its backward (attn_bwd) for autograd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask, scale, element):
+        B, H, n, _ = q.shape
+        lse = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+        o = attn_fwd(q, k, v, mask, scale=scale, lse=lse, element=element)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.mask, ctx.scale, ctx.element = mask, scale, element
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        do = do if do.stride() == q.stride() else do.as_strided(q.shape, q.stride()).copy_(do)
+        dq, dk, dv = attn_bwd(q, k, v, o, do, lse, ctx.mask, scale=ctx.scale,
+                              element=ctx.element)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
+              scale: float | None = None, element: bool = False) -> torch.Tensor:
+    """Radial attention with autograd support (forward attn_fwd, backward attn_bwd)."""
+    return RadialAttentionFunction.apply(q, k, v, mask, scale, element)

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libradial.so")
-SOURCES = ["radial_mask.cpp", "radial_pairs.cpp", "radial_attn_fwd.hip"]
+SOURCES = ["radial_mask.cpp", "radial_pairs.cpp", "radial_attn_fwd.hip", "radial_attn_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -60,118 +60,21 @@
 #include <atomic>
 
 #include "../../include/radial_attn.h"
+#include "radial_device.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kBlock = 128;        // query rows per group, keys per tile
 constexpr int kThreads = 512;      // 8 wave64: two groups of four
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 // A lane's sum of p over one tile (64 keys) above this means m is stale: rescale.
 // It bounds every p by 2^20 between rescales.
 constexpr float kTileSumLimit = 1048576.0f;
-// Fourth dword of a raw gfx9 buffer descriptor: 32-bit data format, no stride/swizzle.
-constexpr int kBufferFlags = 0x00020000;
 // Union list: one 16-bit entry per key block (kb | in-row-A << 14 | in-row-B << 15).
 // A union of two rows has at most nb entries, so nb <= kMaxBlocks bounds it. With four
 // 32 KiB tile buffers, the list and a few counters fill the 160 KiB of LDS.
 constexpr int kMaxBlocks = 16352;
 constexpr int kListBytes = kMaxBlocks * 2;
-
-template <int D>
-struct Tile {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  static constexpr int kBytes = kBlock * kRowBytes;   // one K or V tile
-  static constexpr int kCopiesPerWave = kBytes / 1024 / 4;  // 1 KiB per copy instruction
-  static_assert(kCopiesPerWave * 4 * 1024 == kBytes, "four waves' copies must cover a tile");
-  // One copy instruction covers 1024 / kRowBytes rows, and the bank swizzle repeats
-  // every 16 rows, so the lane offsets of a wave's copies repeat every kOffsetPeriod
-  // instructions; the repeats differ only by 16 rows, which goes into the descriptor.
-  static constexpr int kOffsetPeriod = kRowBytes / 64;
-  static_assert(4 * kBytes >= 2 * kMaxBlocks, "the two key-block maps must fit in the tile buffers");
-};
-
-// Bank swizzle. The LDS has 64 four-byte banks, so a 256-byte span is one bank cycle:
-// ds_read_b128 serves 16 lanes a cycle and ds_read_b64(_tr) 32 lanes. swz is chosen so
-// that (1) the 16 consecutive rows one K read touches land on 16 distinct 16-byte bank
-// slots, (2) the 4 rows x 4 chunks one transposed V read touches per 32 lanes do too.
-// For 256-byte rows (D = 128) this is swz(r) = 4 (r mod 4) + (r / 4 mod 4). For
-// 128-byte rows (D = 64) two rows share a bank cycle, and swz(r) = 4 (r / 2 mod 2) +
-// (r / 4 mod 4).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
-}
-
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
-}
-
-// Workgroup barrier that orders LDS but leaves tile copies (vector-memory loads into LDS)
-// in flight: it waits for this wave's own LDS reads (a copy issued after it may then
-// overwrite what was read), and the "memory" clobber keeps the compiler from moving
-// LDS accesses across it. Copies are waited for explicitly with wait_copies<N>.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Wait until at most N of this wave's vector-memory loads are outstanding. They
-// complete in issue order, so this waits for all but the N most recent.
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Raw buffer descriptor of a byte range (four scalar dwords): base address, no stride,
-// `bytes` records, 32-bit data format. Reads at or past `bytes` return zero.
-__device__ __forceinline__ i32x4 raw_descriptor(const char* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{static_cast<int>(a & 0xffffffffu), static_cast<int>((a >> 32) & 0xffffu), bytes,
-               kBufferFlags};
-}
-
-// One 1 KiB tile-copy instruction: lane l's 16 bytes at byte_offset of the descriptor's
-// range land at LDS address lds + 16 l (buffer_load_dwordx4 ... lds, LDS base in M0).
-// It is written as inline asm so that the compiler does not track it as a pending LDS
-// write: its own waits would then stop every later LDS read until the copy lands. The
-// kernel orders these copies itself (wait_copies and lds_barrier). The instruction
-// writes no VGPR, and M0 is used by nothing else in this kernel.
-__device__ __forceinline__ void copy_1k(const i32x4& desc, uint32_t lds, int byte_offset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(byte_offset), "s"(desc)
-               : "memory");
-}
-
-// Reductions over the two half-waves: for a symmetric op, op(lo, hi) of the pair that
-// v_permlane32_swap(x, x) returns is the same in every lane.
-__device__ __forceinline__ float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+static_assert(4 * Tile<64>::kBytes >= 2 * kMaxBlocks,
+              "the two key-block maps must fit in the tile buffers");
 
 // Everything one wave needs across the phase loop, gathered so that the two groups can
 // run the same phase code over different (compile-time distinct) LDS buffers.
@@ -199,41 +102,17 @@ struct WaveState {
   int es, ew0m1, q0;
 };
 
-// A pending copy of one K or V tile (128 rows) into a buffer: this wave's quarter of it,
-// issued one 1 KiB instruction at a time.
-template <int D>
-struct Stage {
-  // One descriptor per run of kOffsetPeriod instructions: run j starts 16 j rows into the
-  // tile, so its lane offsets are those of run 0.
-  i32x4 desc[Tile<D>::kCopiesPerWave / Tile<D>::kOffsetPeriod];
-  uint32_t lds;
-};
-
+// This wave's quarter of the copy of key block kb (K or V) into buf.
 template <int D>
 __device__ __forceinline__ Stage<D> stage_tile(const WaveState<D>& w, char* buf, const char* src,
                                                int kb, bool on) {
-  using T = Tile<D>;
-  const int key0 = on ? kb * kBlock : 0;
-  const int rows = on ? (w.n - key0 < kBlock ? w.n - key0 : kBlock) : 0;
-  const int bytes = rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0;
-  Stage<D> st;
-#pragma unroll
-  for (int j = 0; j < T::kCopiesPerWave / T::kOffsetPeriod; ++j) {
-    const int skip = 16 * j * w.row_bytes;
-    st.desc[j] = raw_descriptor(src + static_cast<int64_t>(key0) * w.row_bytes + skip,
-                                bytes > skip ? bytes - skip : 0);
-  }
-  st.lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)buf)) +
-           w.wi * T::kCopiesPerWave * 1024;
-  return st;
+  return stage_rows<D>(buf, src, kb * kBlock, w.n, w.row_bytes, w.wi, on);
 }
 
 // Issue copy instruction t of a pending tile copy.
 template <int D>
 __device__ __forceinline__ void stage_issue(const WaveState<D>& w, const Stage<D>& st, int t) {
-  using T = Tile<D>;
-  if (t < T::kCopiesPerWave)
-    copy_1k(st.desc[t / T::kOffsetPeriod], st.lds + t * 1024, w.copy_off[t % T::kOffsetPeriod]);
+  stage_issue<D>(st, w.copy_off, t);
 }
 
 // The MFMA phase of one group for union tile t: O += P(t-1) V(t-1) (when PV), then
@@ -365,75 +244,11 @@ __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sa
   return (lt[0] + lt[1]) + (lt[2] + lt[3]);
 }
 
-// (a / S, a % S) for 0 <= a < 2^24 and 128 <= S, given inv_s within a few ulp of 1 / S:
-// the float estimate of the quotient is off by at most one, then one correction each way.
-__device__ __forceinline__ void div_frame(int a, int S, float inv_s, int& f, int& s) {
-  f = static_cast<int>(static_cast<float>(a) * inv_s);
-  s = a - f * S;
-  if (s >= S) { ++f; s -= S; }
-  if (s < 0) { --f; s += S; }
-}
-
-// Bits lo .. hi (clamped to 0 .. 31) of a 32-bit word.
-__device__ __forceinline__ uint32_t run_bits(int lo, int hi) {
-  const int a = min(max(lo, 0), 32), b = min(max(hi + 1, 0), 32);  // [a, b)
-  const uint32_t below_b = b >= 32 ? ~0u : (1u << b) - 1u;
-  const uint32_t below_a = a >= 32 ? ~0u : (1u << a) - 1u;
-  return below_b & ~below_a;
-}
-
-// Element masking of union tile kb (the rule of "Radial Attention: A Breakthrough in
-// Efficient Long Video Generation", How Radial Attention Works, applied to single
-// entries, with frame-major coordinates and -inf for masked scores as on the
-// radial-attention-video SKILL.md page, Step 1): key j is allowed for query i iff
-//   |s_i - s_j| <= (W0 - 1) >> floor(log2(|f_i - f_j| + 1)),
-// the integer form of |s_i - s_j| * 2^floor(log2(d + 1)) < W0. A lane holds one query
-// and keys key0 + c, c = 32g + 8(e/4) + e%4 for accumulator entry (g, e), key0 =
-// 128 kb + 4 hl. With S >= 128 those keys lie in at most two frames, kf and kf + 1 (c
-// from cut on), and in each the allowed keys form one run of c: [lo_a, hi_a] and
-// [lo_b, hi_b]. Per group of 32 keys the runs become a 32-bit mask; each entry then
-// takes its bit as 0 or all ones (v_bfe_i32) and selects its score or -inf with it
-// (v_bfi_b32): two VALU instructions and no lane masks. A tile that every lane of the
-// wave keeps whole is left alone.
+// Element masking of union tile kb: this wave's queries on the lanes, the tile's keys
+// on the entries.
 template <int D>
 __device__ __forceinline__ void element_mask(const WaveState<D>& w, int kb, f32x16 (&sacc)[4]) {
-  // S and the first query go through an empty asm so that what is derived from them is
-  // recomputed here, per tile, rather than held in registers across the tile loop.
-  int S = w.es, q0 = w.q0;
-  asm volatile("" : "+s"(S), "+s"(q0));
-  // An approximate reciprocal is enough: div_frame corrects the quotient by one.
-  const float inv_s = __builtin_amdgcn_rcpf(static_cast<float>(S));
-  // Frame and spatial index of the wave's first query and of the tile's first key (both
-  // the same in every lane), then this lane's own: one frame wrap at most, as S >= 128.
-  int fq, sq, kf, ks;
-  div_frame(q0 + 32 * w.wi, S, inv_s, fq, sq);
-  div_frame(kb * kBlock, S, inv_s, kf, ks);
-  sq += w.lane & 31;
-  if (sq >= S) { sq -= S; ++fq; }
-  ks += 4 * w.hl;
-  if (ks >= S) { ks -= S; ++kf; }
-  const int cut = S - ks;  // entries with c >= cut are keys of frame kf + 1
-  const int da = fq > kf ? fq - kf : kf - fq;
-  const int db = fq > kf + 1 ? fq - kf - 1 : kf + 1 - fq;
-  const int ra = w.ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(da) + 1u));
-  const int rb = w.ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(db) + 1u));
-  const int base = sq - ks;  // c of the key at the query's own spatial index, frame kf
-  const int lo_a = max(base - ra, 0), hi_a = min(base + ra, cut - 1);
-  const int lo_b = max(base + S - rb, cut), hi_b = base + S + rb;
-  const bool full = lo_a <= 0 && hi_a >= min(cut, 124) - 1 &&
-                    (cut >= 124 || (lo_b <= cut && hi_b >= 123));
-  if (__builtin_amdgcn_ballot_w64(!full) == 0) return;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const uint32_t bits = run_bits(lo_a - 32 * g, hi_a - 32 * g) |
-                          run_bits(lo_b - 32 * g, hi_b - 32 * g);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t keep =
-          static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(bits), 8 * (e >> 2) + (e & 3), 1));
-      sacc[g][e] = __uint_as_float((keep & __float_as_uint(sacc[g][e])) | (~keep & 0xff800000u));
-    }
-  }
+  element_mask_tile(w.q0 + 32 * w.wi, kb * kBlock, w.es, w.ew0m1, w.lane, sacc);
 }
 
 // Softmax of union tile kb: mask padding keys (and, with E, disallowed entries), turn S
@@ -445,27 +260,8 @@ __device__ __forceinline__ void element_mask(const WaveState<D>& w, int kb, f32x
 template <int D, bool E, typename Hook>
 __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&sacc)[4],
                                              bf16x8 (&pk)[8], Hook&& hook) {
-  const int key_lim = w.n - kb * kBlock;  // keys at or past this index are padding
-  if (key_lim < kBlock) {
-    // Key of accumulator entry (g, i) is 32g + 8(i/4) + (i%4) + 4hl: compare the
-    // constant part against one per-lane limit.
-    // The limit is applied arithmetically, min(s, +inf or -inf), so that the 64 tests
-    // need no lane masks (which would exhaust the scalar registers).
-    // The per-block base goes through an empty asm so that the compiler does not fold
-    // the 64 offsets into 64 distinct constants (scalar registers); the remaining
-    // offsets, 0 .. 27, are inline operands.
-    const int lim = key_lim - 4 * w.hl;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      int base = lim - 1 - 32 * g;
-      asm volatile("" : "+v"(base));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int pad = (base - (8 * (i >> 2) + (i & 3))) >> 31;  // -1: padding
-        sacc[g][i] = fminf(sacc[g][i], __int_as_float(0x7f800000 | (pad & 0x80000000)));
-      }
-    }
-  }
+  // Keys at or past n (only in the last key block) are padding.
+  if (w.n - kb * kBlock < kBlock) pad_mask_tile(kb * kBlock, w.n, w.lane, sacc);
   if constexpr (E) element_mask(w, kb, sacc);
   if (w.first) {
     if constexpr (E) {
@@ -690,15 +486,7 @@ __device__ __forceinline__ void run_item(
   w.hl = w.lane >> 5;          // half-wave
 
   // ---- tile copies: this wave's quarter of a tile, 1 KiB per instruction ----
-  // Copy t of wave wi fills bytes [(wi * kCopiesPerWave + t) KiB, +1 KiB) of a buffer;
-  // lane l writes 16 bytes at l * 16, i.e. chunk position p of row r, and so loads
-  // global chunk p ^ swz(r) of that row.
-#pragma unroll
-  for (int t = 0; t < T::kOffsetPeriod; ++t) {
-    const int ci = (w.wi * T::kCopiesPerWave + t) * 64 + w.lane;
-    const int row = ci / T::kChunks, p = ci % T::kChunks;
-    w.copy_off[t] = row * w.row_bytes + ((p ^ swz<D>(row)) << 4);
-  }
+  copy_offsets<D>(w.wi, w.lane, w.row_bytes, w.copy_off);
 
   // Prologue copy: K of union tile 0, by group 0. The compiler does not see the tile
   // copies, so a barrier never waits for them by itself: every wait for a copy is
@@ -726,29 +514,9 @@ __device__ __forceinline__ void run_item(
   }
 
   // ---- per-lane LDS read offsets for the MFMA operands (bytes) ----
-  // K (A operand of S^T): row 32g + lq, chunk 2s + hl at position (2s + hl) ^ swz(lq).
-  // Since 2s + hl = (s << 1) | hl, that position is ((s ^ (swz >> 1)) << 1) |
-  // ((hl ^ swz) & 1): a lane part plus s XORed with a lane constant.
-  {
-    const int sw = swz<D>(lq);
-    w.k_base = lq * T::kRowBytes + (((w.hl ^ sw) & 1) << 4);
-    w.k_x = (sw >> 1) << 5;
-  }
-  // V^T (A operand of O^T) via ds_read_b64_tr_b16: in 16-lane group gi, source lane sl
-  // points at key 4hl + sl/4 (+ 8 for the second read of a pair, + tile offsets) and
-  // d = 32db + 16(gi&1) + 4(sl&3), i.e. chunk 4db + ch with ch = 2(gi&1) + (sl&3)/2 < 4,
-  // at position (4db + ch) ^ swz(key) = ((db ^ (swz >> 2)) << 2) | ((ch ^ swz) & 3).
-  {
-    const int gi = (w.lane >> 4) & 3, sl = w.lane & 15;
-    const int key = 4 * w.hl + (sl >> 2);
-    const int ch = 2 * (gi & 1) + ((sl & 3) >> 1);
-    const int sw0 = swz<D>(key), sw1 = swz<D>(key + 8);
-    const int rd = key * T::kRowBytes + 8 * (sl & 1);
-    w.v_base0 = rd + (((ch ^ sw0) & 3) << 4);
-    w.v_x0 = (sw0 & ~3) << 4;
-    w.v_base1 = rd + 8 * T::kRowBytes + (((ch ^ sw1) & 3) << 4);
-    w.v_x1 = (sw1 & ~3) << 4;
-  }
+  // K (A operand of S^T) by row reads, V^T (A operand of O^T) by transposed reads.
+  row_read_offsets<D>(w.lane, w.k_base, w.k_x);
+  tr_read_offsets<D>(w.lane, w.v_base0, w.v_x0, w.v_base1, w.v_x1);
 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) w.oacc[i] = f32x16{};

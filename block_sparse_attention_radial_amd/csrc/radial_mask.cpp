@@ -134,3 +134,29 @@ extern "C" const char* radial_error_string(int32_t code) {
     default: return "unknown error code";
   }
 }
+
+// The transposed block mask: for key block c, the query blocks whose rows list it,
+// ascending. A counting sort over the columns; entries outside [0, nb) are dropped.
+extern "C" int32_t radial_transpose_mask(int32_t nb, const int32_t* row_ptr,
+                                         const int32_t* col_idx, int32_t* col_ptr,
+                                         int32_t* row_idx) {
+  if (nb <= 0 || !row_ptr || !col_ptr || !row_idx) return RADIAL_ERR_INVALID_ARG;
+  if (row_ptr[0] != 0) return RADIAL_ERR_INVALID_ARG;
+  for (int32_t r = 0; r < nb; ++r)
+    if (row_ptr[r + 1] < row_ptr[r]) return RADIAL_ERR_INVALID_ARG;
+  if (row_ptr[nb] > 0 && !col_idx) return RADIAL_ERR_INVALID_ARG;
+  std::vector<int32_t> count(static_cast<size_t>(nb) + 1, 0);
+  for (int32_t i = 0; i < row_ptr[nb]; ++i) {
+    const int32_t c = col_idx[i];
+    if (c >= 0 && c < nb) ++count[c + 1];
+  }
+  col_ptr[0] = 0;
+  for (int32_t c = 0; c < nb; ++c) col_ptr[c + 1] = col_ptr[c] + count[c + 1];
+  std::vector<int32_t> fill(col_ptr, col_ptr + nb);
+  for (int32_t r = 0; r < nb; ++r)
+    for (int32_t i = row_ptr[r]; i < row_ptr[r + 1]; ++i) {
+      const int32_t c = col_idx[i];
+      if (c >= 0 && c < nb) row_idx[fill[c]++] = r;
+    }
+  return RADIAL_OK;
+}

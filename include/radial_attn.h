@@ -180,6 +180,55 @@ int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int32_t heads, int32_t seqlen, int32_t head_dim, int64_t stride_b,
                         int64_t stride_h, int64_t stride_s, void* stream);
 
+/*
+ * radial_transpose_mask — the transposed block mask, for the backward pass: for key
+ * block c, the query blocks whose rows list it, in ascending order. Host code.
+ *
+ * nb, row_ptr, col_idx: a block mask in host memory. Entries outside [0, nb) are dropped.
+ * col_ptr:   caller-owned host array of nb + 1 int32; col_ptr[0] = 0 and column c's query
+ *            blocks are row_idx[col_ptr[c] .. col_ptr[c+1]).
+ * row_idx:   caller-owned host array of at least row_ptr[nb] int32.
+ * A radial mask is symmetric at block level, so its transpose equals itself; other
+ * masks need this call.
+ *
+ * Errors: INVALID_ARG (null pointer, nb <= 0, row_ptr not starting at 0 or decreasing).
+ */
+int32_t radial_transpose_mask(int32_t nb, const int32_t* row_ptr, const int32_t* col_idx,
+                              int32_t* col_ptr, int32_t* row_idx);
+
+/*
+ * radial_attn_bwd — gradients of radial_attn_fwd: dq, dk, dv for the output gradient
+ * dout. The pages fine-tune through the attention with LoRA (the radial-attention-video
+ * SKILL.md page, Step 4: loss.backward() through the attention layers). With P the
+ * forward's softmax over each row's key set and D_i = <dout_i, o_i>:
+ *     dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (<dout_i, v_j> - D_i),
+ *     dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i.
+ * P is recomputed from the forward's lse: P_ij = exp(scale <q_i, k_j> - lse_i). The call
+ * is asynchronous on `stream` and runs three kernels (D, then dq, then dk and dv).
+ *
+ * q, k, v, o, dout, dq, dk, dv: device bf16 [batch, heads, seqlen, head_dim] sharing one
+ *             set of element strides (as in radial_attn_fwd); o is the forward's output
+ *             for these q, k, v and mask. dq, dk, dv are written for rows < seqlen.
+ * lse:        the forward's lse output (fp32 [batch, heads, seqlen], contiguous).
+ * delta:      caller-owned device workspace of batch * heads * seqlen fp32 (D_i).
+ * row_ptr, col_idx: the block mask used by the forward (device).
+ * col_ptr, row_idx: its transpose from radial_transpose_mask (device). For a radial mask
+ *             these may be row_ptr and col_idx themselves.
+ * scale, element_tokens_per_frame, element_w0: as passed to the forward.
+ * Accumulation is fp32; P and dS enter the matrix products as bf16.
+ *
+ * Errors: as radial_attn_fwd (INVALID_ARG, UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH,
+ * MISALIGNED: also lse or delta not 4-byte aligned, TOO_LARGE: batch*heads*nb work items
+ * or batch*heads*seqlen rows above 2^31 - 1, HIP).
+ */
+int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, const int32_t* row_ptr, const int32_t* col_idx,
+                        const int32_t* col_ptr, const int32_t* row_idx, int32_t nb,
+                        float scale, int32_t element_tokens_per_frame, int32_t element_w0,
+                        int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
+                        int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream);
+
 /* radial_error_string — a static, human-readable text for a return code. */
 const char* radial_error_string(int32_t code);
 

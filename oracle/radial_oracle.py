@@ -220,7 +220,7 @@ def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
 
 
 def attention_backward(q, k, v, do, row_ptr, col_idx, scale: float, block: int = BLOCK,
-                       element=None):
+                       element=None, query_blocks=None, key_blocks=None):
     """fp64 gradients (dq, dk, dv) of `attention` for the output cotangent do.
 
     This is the vector-Jacobian product of softmax attention over the same key sets
@@ -231,6 +231,10 @@ def attention_backward(q, k, v, do, row_ptr, col_idx, scale: float, block: int =
         dq_i = scale sum_j dS_ij k_j,    dk_j += scale dS_ij q_i.
     The identity sum_j P_ij dP_ij = <do_i, o_i> is what makes dS the softmax Jacobian
     applied to dP. `element` is as in `attention`.
+
+    `query_blocks` / `key_blocks` (optional) restrict the work to the dq rows of those
+    query blocks and the dk, dv rows of those key blocks (the rest is left NaN): only the
+    query blocks listed, and those whose rows hold one of the key blocks, are processed.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -241,7 +245,13 @@ def attention_backward(q, k, v, do, row_ptr, col_idx, scale: float, block: int =
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for qb in range(nb):
+    todo = range(nb)
+    if query_blocks is not None or key_blocks is not None:
+        qs = set(query_blocks or [])
+        ks = set(key_blocks or [])
+        todo = [qb for qb in range(nb) if qb in qs
+                or ks.intersection(np.asarray(col_idx[row_ptr[qb]:row_ptr[qb + 1]]).tolist())]
+    for qb in todo:
         rows = slice(qb * block, min(n, (qb + 1) * block))
         keys = row_keys(row_ptr, col_idx, qb, n, block)
         x = scale * (q[..., rows, :] @ np.swapaxes(k[..., keys, :], -1, -2))
@@ -259,6 +269,16 @@ def attention_backward(q, k, v, do, row_ptr, col_idx, scale: float, block: int =
         dq[..., rows, :] = scale * (ds @ k[..., keys, :])
         dk[..., keys, :] += scale * (np.swapaxes(ds, -1, -2) @ q[..., rows, :])
         dv[..., keys, :] += np.swapaxes(p, -1, -2) @ g
+    if query_blocks is not None or key_blocks is not None:
+        keep_q = np.zeros(n, dtype=bool)
+        keep_k = np.zeros(n, dtype=bool)
+        for qb in query_blocks or []:
+            keep_q[qb * block:(qb + 1) * block] = True
+        for kb in key_blocks or []:
+            keep_k[kb * block:(kb + 1) * block] = True
+        dq[..., ~keep_q, :] = np.nan
+        dk[..., ~keep_k, :] = np.nan
+        dv[..., ~keep_k, :] = np.nan
     return dq, dk, dv
 
 

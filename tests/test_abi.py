@@ -27,7 +27,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(
         ["radial_mask_dims", "radial_build_mask", "radial_build_pairs", "radial_attn_fwd",
-         "radial_error_string"])
+         "radial_transpose_mask", "radial_attn_bwd", "radial_error_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,3 +134,68 @@ def test_python_wrapper_checks_before_the_library():
         radial.attn_fwd(q.float(), q.float(), q.float(), m)
     with pytest.raises(ValueError):
         radial.attn_fwd(q, q[:, :, :128], q, m)
+
+
+def bwd(**kw):
+    """Call radial_attn_bwd with valid-looking defaults, overridden by kw."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, do=0x50000, lse=0x60000,
+             dq=0x70000, dk=0x80000, dv=0x90000, delta=0xa0000, row_ptr=0xb0000,
+             col_idx=0xc0000, col_ptr=0xd0000, row_idx=0xe0000, nb=8, scale=0.125,
+             elem_s=0, elem_w0=0, batch=1, heads=2, seqlen=1000, head_dim=128,
+             stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_s=128, stream=None)
+    a.update(kw)
+    return radial.lib().radial_attn_bwd(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+        a["delta"], a["row_ptr"], a["col_idx"], a["col_ptr"], a["row_idx"], a["nb"],
+        a["scale"], a["elem_s"], a["elem_w0"], a["batch"], a["heads"], a["seqlen"],
+        a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    *[(dict(**{name: None}), INVALID) for name in (
+        "q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta", "row_ptr", "col_idx",
+        "col_ptr", "row_idx")],
+    (dict(batch=0), INVALID), (dict(seqlen=0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(elem_s=64, elem_w0=10), INVALID), (dict(elem_s=256, elem_w0=0), INVALID),
+    (dict(head_dim=96), HEADDIM), (dict(nb=9), SHAPE), (dict(stride_s=64), INVALID),
+    (dict(dk=0x80008), MISALIGNED), (dict(lse=0x60002), MISALIGNED),
+    (dict(delta=0xa0001), MISALIGNED), (dict(stride_s=132), MISALIGNED),
+    (dict(batch=1 << 12, heads=1 << 12, seqlen=1 << 20, nb=1 << 13,
+          stride_h=(1 << 20) * 128, stride_b=(1 << 32) * 128), TOO_LARGE),
+])
+def test_attn_bwd_validation(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_transpose_mask_errors_and_a_small_case():
+    import ctypes
+    lib = radial.lib()
+    rp = (ctypes.c_int32 * 4)(0, 2, 3, 5)
+    ci = (ctypes.c_int32 * 5)(0, 2, 1, 0, 7)  # 7 is outside [0, 3): dropped
+    cp = (ctypes.c_int32 * 4)()
+    ri = (ctypes.c_int32 * 5)()
+    assert lib.radial_transpose_mask(3, rp, ci, cp, ri) == OK
+    assert list(cp) == [0, 2, 3, 4] and list(ri)[:4] == [0, 2, 1, 0]
+    assert lib.radial_transpose_mask(0, rp, ci, cp, ri) == INVALID
+    assert lib.radial_transpose_mask(3, None, ci, cp, ri) == INVALID
+    assert lib.radial_transpose_mask(3, rp, None, cp, ri) == INVALID
+    assert lib.radial_transpose_mask(3, rp, ci, None, ri) == INVALID
+    assert lib.radial_transpose_mask(3, rp, ci, cp, None) == INVALID
+    bad = (ctypes.c_int32 * 4)(0, 3, 2, 5)
+    assert lib.radial_transpose_mask(3, bad, ci, cp, ri) == INVALID
+
+
+def test_transpose_mask_matches_oracle():
+    import numpy as np
+    from oracle import radial_oracle as ro
+    rng = np.random.default_rng(7)
+    m = rng.random((37, 37)) < 0.25
+    rp, ci = ro.csr(m)
+    mask = radial.Mask(torch_int(rp), torch_int(ci), 1, 37 * 128, 1).transposed()
+    cp, ri = ro.transpose_csr(rp, ci, 37)
+    assert mask.col_ptr.tolist() == cp.tolist() and mask.row_idx.tolist() == ri.tolist()
+
+
+def torch_int(x):
+    import torch
+    return torch.from_numpy(x.astype("int32"))

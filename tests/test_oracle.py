@@ -543,3 +543,19 @@ def test_transpose_csr_vs_dense():
     cp, ri = ro.transpose_csr(rp, ci, 23)
     rp_t, ci_t = ro.csr(m.T.copy())
     assert np.array_equal(cp, rp_t) and np.array_equal(ri, ci_t)
+
+
+def test_backward_restriction_matches_full():
+    F, S, w0 = 5, 300, 40
+    n = F * S
+    q, k, v, do = (rand((n, 8), s) for s in (67, 68, 69, 70))
+    rp, ci = ro.csr(ro.block_mask(F, S, w0))
+    full = ro.attention_backward(q, k, v, do, rp, ci, scale=0.4)
+    part = ro.attention_backward(q, k, v, do, rp, ci, scale=0.4, query_blocks=[1, 5],
+                                 key_blocks=[0, 7, 11])
+    rows_q = np.r_[128:256, 640:768]
+    rows_k = np.r_[0:128, 896:1024, 1408:n]
+    assert np.array_equal(part[0][rows_q], full[0][rows_q])
+    for a, b in zip(part[1:], full[1:]):
+        assert np.array_equal(a[rows_k], b[rows_k])
+    assert np.isnan(part[0][0]).all() and np.isnan(part[1][200]).all()
