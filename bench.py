@@ -2,7 +2,7 @@
 """Radial attention forward pass on one MI355X: effective TFLOP/s on active blocks.
 
     python bench.py [--steps K] [--warmup W] [--workload wan|hunyuan|long4x|small|tiny]
-                    [--element]
+                    [--element] [--backward]
 
 A step is one call of the block-sparse forward kernel over the whole workload
 (every batch, head and query block), with Q/K/V already resident in HBM. The static mask
@@ -11,7 +11,10 @@ untimed warm-up steps, exactly K steps are timed with HIP events on the stream t
 kernel runs on, between device synchronisations. The same kernel with the all-active
 mask gives the dense baseline. The CPU oracle is timed beside it on a bounded sample.
 Rank 0 prints one JSON line. --element times element masking instead (the radial rule on
-single entries inside the active blocks; the oracle runs the same option).
+single entries inside the active blocks; the oracle runs the same option). --backward
+times the backward pass (dq, dk, dv from the forward's o and lse, and a seeded dO),
+counting 2.5 times the forward's work (the usual five products against two), and its
+dense baseline and CPU oracle likewise.
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -29,7 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_radial_amd", "csrc", "radial_attn_fwd.hip")
+# The forward kernel's sources: its traffic counters are valid while these are unchanged.
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_radial_amd", "csrc", f)
+               for f in ("radial_attn_fwd.hip", "radial_device.h")]
 
 
 def log(*a):
@@ -37,8 +42,12 @@ def log(*a):
 
 
 def kernel_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the forward kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_bytes(workload_name: str):
@@ -74,7 +83,7 @@ def time_launches(fn, steps: int, warmup: int):
     return start.elapsed_time(stop) / steps, wall
 
 
-def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False):
+def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False, do=None):
     """Time the fp64 CPU oracle over heads 0, 1, ... (each head's query blocks in a seeded
     order) until about `seconds` of work has run. Report the same active-tile flop rate
     as the GPU."""
@@ -93,11 +102,17 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False):
     for h in range(wl.batch * wl.heads):
         b, hh = divmod(h, wl.heads)
         qh, kh, vh = (x[b, hh].double().cpu().numpy() for x in (q, k, v))
+        doh = None if do is None else do[b, hh].double().cpu().numpy()
         heads += 1
         t0 = time.perf_counter()
         for qb in order:
-            ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)],
-                         element=(wl.tokens_per_frame, wl.w0) if element else None)
+            if do is None:
+                ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)],
+                             element=(wl.tokens_per_frame, wl.w0) if element else None)
+            else:  # the backward of this query block (its dq and its share of dk, dv)
+                ro.attention_backward(qh, kh, vh, doh, rp, ci, wl.scale,
+                                      element=(wl.tokens_per_frame, wl.w0) if element else None,
+                                      query_blocks=[int(qb)])
             blocks += 1
             tiles += int(rp[qb + 1] - rp[qb])
             if elapsed + time.perf_counter() - t0 >= seconds:
@@ -105,7 +120,7 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False):
         elapsed += time.perf_counter() - t0
         if elapsed >= seconds:
             break
-    flops = 4 * wl.head_dim * 128 * 128 * tiles
+    flops = 4 * wl.head_dim * 128 * 128 * tiles * (2.5 if do is not None else 1)
     threads = [d.get("num_threads", 0) for d in threadpool_info()
                if d.get("user_api") == "blas"]
     return {
@@ -130,6 +145,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--element", action="store_true",
                     help="element masking inside the active blocks (block semantics otherwise)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dq, dk, dv) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale "
                          "HBM traffic counters against a kernel of known size")
@@ -172,18 +189,34 @@ def main():
     log(f"workload {wl.name}: n={wl.n} nb={mask.nb} nnz={mask.nnz} "
         f"({mask.nnz / mask.nb ** 2:.3f} of blocks), mask build {mask_ms:.2f} ms")
 
-    ms, wall = time_launches(lambda: radial.attn_fwd(q, k, v, mdev, out=o, element=args.element),
-                             args.steps, args.warmup)
+    work = 2.5 if args.backward else 1.0
+    flops = int(flops * work)
+    do = None
+    if args.backward:
+        gen = torch.Generator(device=dev).manual_seed(1)
+        do = torch.randn(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+
+        def step(m):
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            out = radial.attn_fwd(q, k, v, m, lse=lse, element=args.element)
+            torch.cuda.synchronize()
+            return lambda: radial.attn_bwd(q, k, v, out, do, lse, m, element=args.element)
+        run = step(mdev)
+    else:
+        run = lambda: radial.attn_fwd(q, k, v, mdev, out=o, element=args.element)  # noqa: E731
+    ms, wall = time_launches(run, args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"sparse{' (element masking)' if args.element else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
+    log(f"{'backward' if args.backward else 'sparse'}"
+        f"{' (element masking)' if args.element else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
 
     dense = None
     if not args.no_dense:
         dmask = radial.dense_mask(wl.n, device=dev)
         dsteps = max(3, args.steps // 2)
-        dms, _ = time_launches(lambda: radial.attn_fwd(q, k, v, dmask, out=o),
-                               dsteps, min(args.warmup, 2))
-        dflops = 4 * wl.head_dim * 128 * 128 * dmask.nnz * bh
+        drun = step(dmask) if args.backward else (
+            lambda: radial.attn_fwd(q, k, v, dmask, out=o))
+        dms, _ = time_launches(drun, dsteps, min(args.warmup, 2))
+        dflops = 4 * wl.head_dim * 128 * 128 * dmask.nnz * bh * work
         dense = {"ms": dms, "tflops": dflops / (dms * 1e-3) / 1e12, "steps": dsteps,
                  "speedup": dms / ms, "ideal_speedup": dmask.nnz / mask.nnz}
         log(f"dense:  {dms:.3f} ms/step, {dense['tflops']:.1f} TFLOP/s; "
@@ -191,10 +224,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds, args.element)
+        cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds, args.element, do)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
-    traffic = traffic_bytes(wl.name + ("-element" if args.element else ""))
+    traffic = None if args.backward else traffic_bytes(wl.name + ("-element" if args.element else ""))
     line = {
         "metric": "active-block attention TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 1 GPU",
         "value": round(tflops, 3),
@@ -214,6 +247,7 @@ def main():
             "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
             "block": 128, "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2,
             "semantics": "element" if args.element else "block",
+            "pass": "backward" if args.backward else "forward",
         },
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "speedup_vs_dense": None if dense is None else round(dense["speedup"], 3),

@@ -180,7 +180,7 @@ def dense_mask(seqlen: int, device="cpu") -> Mask:
     nb = (seqlen + BLOCK - 1) // BLOCK
     row_ptr = torch.arange(0, nb * nb + 1, nb, dtype=torch.int32, device=device)
     col_idx = torch.arange(nb, dtype=torch.int32, device=device).repeat(nb)
-    return Mask(row_ptr, col_idx, 1, seqlen, 2**31 - 1)
+    return Mask(row_ptr, col_idx, 1, seqlen, 2**31 - 1, None, row_ptr, col_idx)
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
