@@ -34,6 +34,9 @@ _SIGNATURES = {
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 6
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_attn_fwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32] + [
+        ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 4 + [ctypes.c_int64] * 2
+        + [ctypes.c_void_p]),
     "radial_transpose_mask": (ctypes.c_int32, [ctypes.c_int32] + [ctypes.c_void_p] * 4),
     "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_int32] * 4
@@ -298,3 +301,94 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
               scale: float | None = None, element: bool = False) -> torch.Tensor:
     """Radial attention with autograd support (forward attn_fwd, backward attn_bwd)."""
     return RadialAttentionFunction.apply(q, k, v, mask, scale, element)
+
+
+@dataclass
+class VarlenMask:
+    """The block masks of a varlen batch, concatenated as radial_attn_fwd_varlen takes
+    them: sample b's row_ptr (rebased to index the concatenated col_idx) follows those of
+    the samples before it, and likewise its pair table."""
+
+    seq_tokens: list
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+    tokens_per_frame: int
+    w0: int
+    pairs: torch.Tensor | None = None
+    npairs: list | None = None
+
+    @property
+    def batch(self) -> int:
+        return len(self.seq_tokens)
+
+    def to(self, device) -> "VarlenMask":
+        return VarlenMask(list(self.seq_tokens), self.row_ptr.to(device), self.col_idx.to(device),
+                          self.tokens_per_frame, self.w0,
+                          None if self.pairs is None else self.pairs.to(device),
+                          None if self.npairs is None else list(self.npairs))
+
+
+def concat_masks(masks: list) -> VarlenMask:
+    """One VarlenMask from per-sample masks of one frame length and W0 (host tensors)."""
+    if not masks:
+        raise ValueError("a varlen batch needs at least one sample")
+    S, w0 = masks[0].tokens_per_frame, masks[0].w0
+    if any(m.tokens_per_frame != S or m.w0 != w0 for m in masks):
+        raise ValueError("the samples must share the frame length and W0")
+    rps, off = [], 0
+    for m in masks:
+        rps.append(m.row_ptr.to("cpu", torch.int32) + off)
+        off += m.nnz
+    with_pairs = all(m.pairs is not None for m in masks)
+    return VarlenMask([m.n for m in masks], torch.cat(rps),
+                      torch.cat([m.col_idx.to("cpu", torch.int32) for m in masks]), S, w0,
+                      torch.cat([m.pairs.to("cpu") for m in masks]) if with_pairs else None,
+                      [m.pairs.shape[0] for m in masks] if with_pairs else None)
+
+
+def build_varlen_mask(frames: list, tokens_per_frame: int, w0: int, pairs: bool = True):
+    """The radial masks of videos with the given frame counts (one frame length, one W0)."""
+    return concat_masks([build_mask(f, tokens_per_frame, w0, pairs=pairs) for f in frames])
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: VarlenMask,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | None = None, element: bool = False) -> torch.Tensor:
+    """Radial attention forward on a packed batch: q, k, v of shape [total_tokens, H, D]
+    (bf16, on the GPU), sample b holding the next mask.seq_tokens[b] tokens. `lse`
+    (optional) is fp32 [H, total_tokens]. Asynchronous on torch's current stream."""
+    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share the shape [total_tokens, H, D]")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.stride() != k.stride() or q.stride() != v.stride() or q.stride(-1) != 1:
+        raise ValueError("q, k, v must share strides with a contiguous last axis")
+    total, H, D = q.shape
+    if sum(mask.seq_tokens) != total:
+        raise ValueError("the samples' lengths must add up to q's token count")
+    if mask.row_ptr.device != q.device or mask.col_idx.device != q.device or (
+            mask.pairs is not None and mask.pairs.device != q.device):
+        raise ValueError("the mask must be on the same device as q (VarlenMask.to(device))")
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.stride() != q.stride() or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape, strides and dtype")
+    if lse is not None and (lse.shape != (H, total) or lse.dtype != torch.float32
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [H, total_tokens] tensor on q's device")
+    if scale is None:
+        scale = D ** -0.5
+    if element and mask.tokens_per_frame < BLOCK:
+        raise ValueError("element masking needs a frame length of at least 128 tokens")
+    elem_s, elem_w0 = (mask.tokens_per_frame, mask.w0) if element else (0, 0)
+    seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
+    npr = None if mask.npairs is None else (ctypes.c_int32 * mask.batch)(*mask.npairs)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check("radial_attn_fwd_varlen", lib().radial_attn_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), seq, mask.batch, mask.row_ptr.data_ptr(),
+        mask.col_idx.data_ptr(), None if mask.pairs is None else mask.pairs.data_ptr(), npr,
+        float(scale), elem_s, elem_w0, H, D, q.stride(1), q.stride(0), stream))
+    return out

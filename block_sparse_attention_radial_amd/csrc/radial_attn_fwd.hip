@@ -374,17 +374,17 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
 }
 
 // One work item: the two query-block rows of pair p (from the pair table, or 2p and
-// 2p+1) of one (batch, head). smem holds two K and two V buffers at fixed offsets, then
-// the union list; counts holds the per-wave sums of the list compaction, then the union
-// length.
+// 2p+1) of one (batch, head). q, k, v, o point at row 0 of this (batch, head), lse (if
+// not null) at its row 0's entry; the ids [first_id, first_id + np) are this head's
+// items. smem holds two K and two V buffers at fixed offsets, then the union list;
+// counts holds the per-wave sums of the list compaction, then the union length.
 template <int D, bool E>
 __device__ __forceinline__ void run_item(
-    int pid, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
+    int pid, int first_id, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int np, int nb,
-    int heads, int n, float c, int64_t stride_b, int64_t stride_h, int stride_s, int es,
-    int ew0) {
+    int n, float c, int stride_s, int es, int ew0) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -393,21 +393,17 @@ __device__ __forceinline__ void run_item(
   uint16_t* const list = reinterpret_cast<uint16_t*>(smem + 4 * T::kBytes);
 
   // Work mapping. Item ids are taken by the XCDs round-robin (XCD = id % 8), in id order
-  // on each XCD (see radial_fwd_kernel). Ids [bh * np, (bh + 1) * np) all belong to head
-  // bh (np query block pairs per head), so the whole chip works on one or two heads at a
-  // time and their K/V stays in the shared Infinity Cache. Inside a head, the ids that
-  // land on XCD x take one contiguous run of pairs, in order, so neighbouring query
-  // blocks (which read mostly the same K/V tiles) share that XCD's L2.
-  const int bh = pid / np;
-  const int first_id = bh * np;
+  // on each XCD (see radial_fwd_kernel). The ids of one head are contiguous, so the whole
+  // chip works on one or two heads at a time and their K/V stays in the shared Infinity
+  // Cache. Inside a head, the ids that land on XCD x take one contiguous run of pairs, in
+  // order, so neighbouring query blocks (which read mostly the same K/V tiles) share that
+  // XCD's L2.
   const int xcd = pid & 7;
   int seg = 0;  // pairs of this head taken by XCDs 0 .. xcd-1
   for (int y = 0; y < xcd; ++y)
     seg += ((first_id + np - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
   const int first_here = first_id + ((xcd - first_id) & 7);  // first id of this head on xcd
   const int pair = seg + ((pid - first_here) >> 3);
-  const int b = bh / heads, h = bh - b * heads;
-  const int64_t base = b * stride_b + h * stride_h;
   // The pair's rows. A row outside [0, nb) (the second row of an odd nb's last pair, or
   // an absent entry of the table) adds no key blocks and has no queries: -1.
   int ra = 2 * pair, rb = 2 * pair + 1;
@@ -474,8 +470,8 @@ __device__ __forceinline__ void run_item(
   const int U = counts[8];
 
   WaveState<D> w;
-  w.kh = reinterpret_cast<const char*>(k + base);
-  w.vh = reinterpret_cast<const char*>(v + base);
+  w.kh = reinterpret_cast<const char*>(k);
+  w.vh = reinterpret_cast<const char*>(v);
   w.nb = nb;
   w.n = n;
   w.c = c;
@@ -501,7 +497,7 @@ __device__ __forceinline__ void run_item(
   // ---- Q^T as the MFMA B operand: d = 16s + 8hl .. +7 of this lane's query ----
   {
     const int rows = n - q0 < kBlock ? n - q0 : kBlock;
-    const auto rq = make_rsrc(q + base + static_cast<int64_t>(q0 < n ? q0 : 0) * stride_s,
+    const auto rq = make_rsrc(q + static_cast<int64_t>(q0 < n ? q0 : 0) * stride_s,
                               rows > 0 ? (rows - 1) * w.row_bytes + T::kRowBytes : 0);
     const int off = (w.wi * 32 + lq) * w.row_bytes + w.hl * 16;
 #pragma unroll
@@ -540,7 +536,7 @@ __device__ __forceinline__ void run_item(
   const float inv = 1.0f / l_tot;
   const int qrow = q0 + w.wi * 32 + lq;
   if (qrow < n) {
-    __bf16* orow = o + base + static_cast<int64_t>(qrow) * stride_s;
+    __bf16* orow = o + static_cast<int64_t>(qrow) * stride_s;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -551,7 +547,7 @@ __device__ __forceinline__ void run_item(
             __builtin_convertvector(x, bf16x4);
       }
     if (lse != nullptr && w.hl == 0)
-      lse[static_cast<int64_t>(bh) * n + qrow] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      lse[qrow] = (w.m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
@@ -578,6 +574,14 @@ __device__ int g_work[kCounterSlots][16];
 // finished whole items after the rest, and under the chip's power limit the XCDs run
 // at different clocks, so a fixed share per XCD left the faster ones idle at the end.
 // The last workgroup to finish resets the counters.
+// One sample of a varlen batch: its first token in the packed sequence, its tokens and
+// query blocks, where its row_ptr array starts in the concatenated one, where its pairs
+// start in the concatenated pair table, its pair count, and its first work item.
+struct VarlenSample {
+  int tok0, n, nb, rp0, pr0, np, it0, pad;
+};
+constexpr int kMaxVarlen = 64;
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -592,6 +596,10 @@ struct FwdArgs {
   int elem_s, elem_w0;
   float c;
   int items, slot;
+  // varlen: 0 for a uniform batch, else the number of samples in `plan` (q, k, v, o are
+  // then one packed sequence of n tokens, and lse is [heads, n])
+  int varlen;
+  VarlenSample plan[kMaxVarlen];
 };
 typedef __attribute__((address_space(4))) const FwdArgs* ArgsPtr;
 
@@ -618,6 +626,7 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.c = ap->c;
   a.items = ap->items;
   a.slot = ap->slot;
+  a.varlen = ap->varlen;
   return a;
 }
 
@@ -660,9 +669,41 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     __syncthreads();  // every wave read the previous item's id before run_item's barriers
     const int item = __builtin_amdgcn_readfirstlane(next_item);
     if (item < 0) break;
-    run_item<D, E>(item, tid, smem, counts, a.q, a.k, a.v, a.o, a.lse, a.row_ptr, a.col_idx,
-                   a.pairs, a.npairs, a.nb, a.heads, a.n, a.c, a.stride_b, a.stride_h,
-                   a.stride_s, a.elem_s, a.elem_w0);
+    // The item's (batch, head), and its head's first item.
+    int64_t base;
+    float* lse_row = nullptr;
+    const int32_t* row_ptr = a.row_ptr;
+    const int32_t* pairs = a.pairs;
+    int np = a.npairs, nb = a.nb, n = a.n, first_id;
+    if (a.varlen == 0) {
+      const int bh = item / np;
+      first_id = bh * np;
+      const int b = bh / a.heads, h = bh - b * a.heads;
+      base = b * a.stride_b + h * a.stride_h;
+      if (a.lse != nullptr) lse_row = a.lse + static_cast<int64_t>(bh) * n;
+    } else {
+      // The last sample whose first item is at most `item` (plan read from the
+      // kernel-argument segment with scalar loads).
+      int lo = 0, hi = a.varlen - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ap->plan[mid].it0 <= item) lo = mid;
+        else hi = mid - 1;
+      }
+      const int tok0 = ap->plan[lo].tok0, it0 = ap->plan[lo].it0;
+      np = ap->plan[lo].np;
+      nb = ap->plan[lo].nb;
+      n = ap->plan[lo].n;
+      row_ptr += ap->plan[lo].rp0;
+      if (pairs != nullptr) pairs += 2 * ap->plan[lo].pr0;
+      const int h = (item - it0) / np;
+      first_id = it0 + h * np;
+      base = static_cast<int64_t>(tok0) * a.stride_s + h * a.stride_h;
+      if (a.lse != nullptr) lse_row = a.lse + static_cast<int64_t>(h) * a.n + tok0;
+    }
+    run_item<D, E>(item, first_id, tid, smem, counts, a.q + base, a.k + base, a.v + base,
+                   a.o + base, lse_row, row_ptr, a.col_idx, pairs, np, nb, n, a.c, a.stride_s,
+                   a.elem_s, a.elem_w0);
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -700,38 +741,11 @@ int cu_count() {
 std::atomic<uint32_t> g_next_slot{0};
 std::atomic<uint32_t> g_next_capture_slot{0};
 
-}  // namespace
-
-extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
-                                   float* lse, const int32_t* row_ptr, const int32_t* col_idx,
-                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
-                                   int32_t element_tokens_per_frame, int32_t element_w0, int32_t batch, int32_t heads,
-                                   int32_t seqlen, int32_t head_dim, int64_t stride_b,
-                                   int64_t stride_h, int64_t stride_s, void* stream) {
-  if (!q || !k || !v || !o || !row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
-  if (batch <= 0 || heads <= 0 || seqlen <= 0 || nb <= 0) return RADIAL_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
-  // Element masking: a frame spans at least one 128-key tile, and W0 >= 1 keeps the
-  // diagonal allowed.
-  if (element_tokens_per_frame != 0 &&
-      (element_tokens_per_frame < kBlock || element_w0 < 1))
-    return RADIAL_ERR_INVALID_ARG;
-  if (head_dim != 64 && head_dim != 128) return RADIAL_ERR_UNSUPPORTED_HEAD_DIM;
-  if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
-  if (stride_s < head_dim || stride_h < 0 || stride_b < 0) return RADIAL_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return RADIAL_ERR_MISALIGNED;
-  if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
-  if (pairs == nullptr) npairs = (nb + 1) / 2;
-  else if (npairs < (nb + 1) / 2 || npairs > nb) return RADIAL_ERR_INVALID_ARG;
-  const int64_t items = static_cast<int64_t>(batch) * heads * npairs;
-  // A tile of 128 rows is addressed with 32-bit byte offsets from its first row, and
-  // the union list holds one 16-bit entry per key block.
-  if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock || nb > kMaxBlocks)
-    return RADIAL_ERR_TOO_LARGE;
+// The launch shared by the uniform and the varlen entry points: a persistent grid of one
+// workgroup per CU (a multiple of 8, at most one per item) and a counter slot.
+int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, bool elem, void* stream) {
   const int cus = cu_count();
   if (cus < 0) return RADIAL_ERR_HIP;
-  // A multiple of 8 workgroups (one per XCD and round), at most one per CU and per item.
   const int64_t per_xcd = std::min<int64_t>(std::max(cus / 8, 1), (items + 7) / 8);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
@@ -740,24 +754,9 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   const bool captured = capture == hipStreamCaptureStatusActive;
   const uint32_t turn = (captured ? g_next_capture_slot : g_next_slot)
                             .fetch_add(1, std::memory_order_relaxed);
-  const int slot = static_cast<int>((captured ? kHalf : 0u) + turn % kHalf);
-
-  // Base-2 score scale. It is kept >= FLT_MIN so a padding score of -inf stays -inf
-  // after scaling (never -inf * 0 = NaN). For scale = 0 every finite score times FLT_MIN
-  // rounds away against m, giving p = 2^-m for each real key: the mean of V over the key
-  // set, which is the scale-0 softmax.
-  const float c = fmaxf(scale * kLog2e, FLT_MIN);
+  args.slot = static_cast<int>((captured ? kHalf : 0u) + turn % kHalf);
+  args.items = static_cast<int>(items);
   const dim3 grid(static_cast<uint32_t>(8 * per_xcd)), block(kThreads);
-  const int it = static_cast<int>(items);
-  const auto* qq = static_cast<const __bf16*>(q);
-  const auto* kk = static_cast<const __bf16*>(k);
-  const auto* vv = static_cast<const __bf16*>(v);
-  auto* oo = static_cast<__bf16*>(o);
-  const FwdArgs args{qq,       kk,       vv,    oo,     lse,    row_ptr,
-                     col_idx,  pairs,    stride_b, stride_h, npairs, nb,
-                     heads,    seqlen,   static_cast<int>(stride_s),
-                     element_tokens_per_frame, element_w0, c, it, slot};
-  const bool elem = element_tokens_per_frame != 0;
   if (head_dim == 128) {
     if (elem)
       hipLaunchKernelGGL((radial_fwd_kernel<128, true>), grid, block, 0, st, args);
@@ -770,4 +769,101 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
       hipLaunchKernelGGL((radial_fwd_kernel<64, false>), grid, block, 0, st, args);
   }
   return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
+}
+
+// Base-2 score scale. It is kept >= FLT_MIN so a padding score of -inf stays -inf after
+// scaling (never -inf * 0 = NaN). For scale = 0 every finite score times FLT_MIN rounds
+// away against m, giving p = 2^-m for each real key: the mean of V over the key set,
+// which is the scale-0 softmax.
+float base2_scale(float scale) { return fmaxf(scale * kLog2e, FLT_MIN); }
+
+// Checks shared by both entry points.
+int32_t check_common(const void* q, const void* k, const void* v, const void* o,
+                     const int32_t* row_ptr, const int32_t* col_idx, int32_t heads, float scale,
+                     int32_t element_tokens_per_frame, int32_t element_w0, int32_t head_dim) {
+  if (!q || !k || !v || !o || !row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
+  if (heads <= 0) return RADIAL_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
+  // Element masking: a frame spans at least one 128-key tile, and W0 >= 1 keeps the
+  // diagonal allowed.
+  if (element_tokens_per_frame != 0 &&
+      (element_tokens_per_frame < kBlock || element_w0 < 1))
+    return RADIAL_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return RADIAL_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return RADIAL_ERR_MISALIGNED;
+  return RADIAL_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
+                                   int32_t element_tokens_per_frame, int32_t element_w0,
+                                   int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
+                                   int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                                   void* stream) {
+  const int32_t err = check_common(q, k, v, o, row_ptr, col_idx, heads, scale,
+                                   element_tokens_per_frame, element_w0, head_dim);
+  if (err != RADIAL_OK) return err;
+  if (batch <= 0 || seqlen <= 0 || nb <= 0) return RADIAL_ERR_INVALID_ARG;
+  if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
+  if (stride_s < head_dim || stride_h < 0 || stride_b < 0) return RADIAL_ERR_INVALID_ARG;
+  if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
+  if (pairs == nullptr) npairs = (nb + 1) / 2;
+  else if (npairs < (nb + 1) / 2 || npairs > nb) return RADIAL_ERR_INVALID_ARG;
+  const int64_t items = static_cast<int64_t>(batch) * heads * npairs;
+  // A tile of 128 rows is addressed with 32-bit byte offsets from its first row, and
+  // the union list holds one 16-bit entry per key block.
+  if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock || nb > kMaxBlocks)
+    return RADIAL_ERR_TOO_LARGE;
+  FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+               static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
+               pairs, stride_b, stride_h, npairs, nb, heads, seqlen,
+               static_cast<int>(stride_s), element_tokens_per_frame, element_w0,
+               base2_scale(scale), 0, 0, 0, {}};
+  return launch_fwd(args, items, head_dim, element_tokens_per_frame != 0, stream);
+}
+
+extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                                          float* lse, const int32_t* seq_tokens, int32_t batch,
+                                          const int32_t* row_ptr, const int32_t* col_idx,
+                                          const int32_t* pairs, const int32_t* npairs,
+                                          float scale, int32_t element_tokens_per_frame,
+                                          int32_t element_w0, int32_t heads, int32_t head_dim,
+                                          int64_t stride_h, int64_t stride_s, void* stream) {
+  const int32_t err = check_common(q, k, v, o, row_ptr, col_idx, heads, scale,
+                                   element_tokens_per_frame, element_w0, head_dim);
+  if (err != RADIAL_OK) return err;
+  if (!seq_tokens || batch <= 0 || (pairs != nullptr && npairs == nullptr))
+    return RADIAL_ERR_INVALID_ARG;
+  if (batch > kMaxVarlen) return RADIAL_ERR_TOO_LARGE;
+  if (stride_s < head_dim || stride_h < 0) return RADIAL_ERR_INVALID_ARG;
+  if ((stride_s | stride_h) & 7) return RADIAL_ERR_MISALIGNED;
+  if (stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
+  FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+               static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
+               pairs, 0, stride_h, 0, 0, heads, 0, static_cast<int>(stride_s),
+               element_tokens_per_frame, element_w0, base2_scale(scale), 0, 0, batch, {}};
+  int64_t tok = 0, rows = 0, prs = 0, items = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = seq_tokens[b];
+    if (n <= 0) return RADIAL_ERR_INVALID_ARG;
+    const int32_t nb = (n + kBlock - 1) / kBlock;
+    if (nb > kMaxBlocks) return RADIAL_ERR_TOO_LARGE;
+    const int32_t np = pairs == nullptr ? (nb + 1) / 2 : npairs[b];
+    if (np < (nb + 1) / 2 || np > nb) return RADIAL_ERR_INVALID_ARG;
+    if (tok > INT32_MAX || rows > INT32_MAX || prs > INT32_MAX || items > INT32_MAX)
+      return RADIAL_ERR_TOO_LARGE;
+    args.plan[b] = VarlenSample{static_cast<int>(tok), n, nb, static_cast<int>(rows),
+                                static_cast<int>(prs), np, static_cast<int>(items), 0};
+    tok += n;
+    rows += nb + 1;
+    prs += np;
+    items += static_cast<int64_t>(heads) * np;
+  }
+  if (tok > INT32_MAX || items > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  args.n = static_cast<int>(tok);  // the packed sequence; lse is [heads, n]
+  return launch_fwd(args, items, head_dim, element_tokens_per_frame != 0, stream);
 }

@@ -181,6 +181,40 @@ int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int64_t stride_h, int64_t stride_s, void* stream);
 
 /*
+ * radial_attn_fwd_varlen — radial_attn_fwd over a batch of videos of different lengths
+ * (each sample its own frame count, so its own mask), packed into one sequence. The
+ * call is asynchronous on `stream`.
+ *
+ * q, k, v, o: device bf16 [total_tokens, heads, head_dim] (any layout with element
+ *             strides stride_s between tokens and stride_h between heads, shared by all
+ *             four, head_dim contiguous). Sample b holds tokens [t_b, t_b + seq_tokens[b])
+ *             with t_b the sum of the lengths before it.
+ * lse:        optional device fp32 [heads, total_tokens], contiguous.
+ * seq_tokens: host array of batch lengths (each >= 1); 1 <= batch <= 64.
+ * row_ptr, col_idx: the samples' block masks (device), concatenated: sample b's nb_b + 1
+ *             row_ptr entries follow those of samples 0 .. b-1 (nb_b = ceil(len / 128)),
+ *             and their values index the concatenated col_idx. Column indices count key
+ *             blocks within the sample.
+ * pairs, npairs: optional pair tables (device, concatenated: sample b's npairs[b] pairs
+ *             follow those of the samples before it) and their host array of counts;
+ *             null for the adjacent pairs of every sample.
+ * Other arguments as radial_attn_fwd; element masking uses each sample's own token
+ * indices. The kernel, its work counters and its numerics are radial_attn_fwd's.
+ *
+ * Errors: INVALID_ARG (null pointer, batch <= 0, a length <= 0, pairs without npairs, a
+ * pair count outside [ceil(nb_b / 2), nb_b], heads <= 0, stride_s < head_dim, bad scale
+ * or element arguments), UNSUPPORTED_HEAD_DIM, MISALIGNED, TOO_LARGE (batch above 64,
+ * a sample above 16352 blocks, totals past int32), HIP.
+ */
+int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                               float* lse, const int32_t* seq_tokens, int32_t batch,
+                               const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* pairs, const int32_t* npairs, float scale,
+                               int32_t element_tokens_per_frame, int32_t element_w0,
+                               int32_t heads, int32_t head_dim, int64_t stride_h,
+                               int64_t stride_s, void* stream);
+
+/*
  * radial_transpose_mask — the transposed block mask, for the backward pass: for key
  * block c, the query blocks whose rows list it, in ascending order. Host code.
  *

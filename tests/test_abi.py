@@ -27,7 +27,8 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(
         ["radial_mask_dims", "radial_build_mask", "radial_build_pairs", "radial_attn_fwd",
-         "radial_transpose_mask", "radial_attn_bwd", "radial_error_string"])
+         "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
+         "radial_error_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -199,3 +200,36 @@ def test_transpose_mask_matches_oracle():
 def torch_int(x):
     import torch
     return torch.from_numpy(x.astype("int32"))
+
+
+def varlen(**kw):
+    """Call radial_attn_fwd_varlen with valid-looking defaults, overridden by kw."""
+    import ctypes
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, seq=[1000, 300], batch=2,
+             row_ptr=0x50000, col_idx=0x60000, pairs=None, npairs=None, scale=0.125,
+             elem_s=0, elem_w0=0, heads=2, head_dim=128, stride_h=128, stride_s=256,
+             stream=None)
+    a.update(kw)
+    seq = None if a["seq"] is None else (ctypes.c_int32 * len(a["seq"]))(*a["seq"])
+    npr = None if a["npairs"] is None else (ctypes.c_int32 * len(a["npairs"]))(*a["npairs"])
+    return radial.lib().radial_attn_fwd_varlen(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], seq, a["batch"], a["row_ptr"], a["col_idx"],
+        a["pairs"], npr, a["scale"], a["elem_s"], a["elem_w0"], a["heads"], a["head_dim"],
+        a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(row_ptr=None), INVALID), (dict(seq=None), INVALID),
+    (dict(batch=0), INVALID), (dict(seq=[1000, 0]), INVALID), (dict(heads=0), INVALID),
+    (dict(pairs=0x70000), INVALID),                              # pairs without counts
+    (dict(pairs=0x70000, npairs=[9, 2]), INVALID),               # 9 pairs for 8 blocks
+    (dict(pairs=0x70000, npairs=[3, 2]), INVALID),               # 3 < ceil(8 / 2)
+    (dict(stride_s=64), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(elem_s=64, elem_w0=5), INVALID), (dict(head_dim=80), HEADDIM),
+    (dict(v=0x30004), MISALIGNED), (dict(stride_h=132), MISALIGNED),
+    (dict(seq=[100] * 65, batch=65), TOO_LARGE),
+    (dict(seq=[16353 * 128], batch=1), TOO_LARGE),
+])
+def test_attn_fwd_varlen_validation(kw, code):
+    # Every case here fails a host check: none may reach a launch (the pointers are fake).
+    assert varlen(**kw) == code

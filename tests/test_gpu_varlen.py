@@ -1,0 +1,81 @@
+"""GPU tests of the varlen forward: a packed batch of videos with different frame counts.
+
+Each sample runs the same kernel arithmetic as attn_fwd on that sample alone, so the
+packed result must equal the per-sample results bit for bit (block and element
+semantics, with and without pair tables); the samples are also checked against the
+fp64 oracle (bar as in test_gpu_parity: max-abs 2e-2, mean-abs 2e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_radial_amd as radial
+from oracle import radial_oracle as ro
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    radial.lib()
+
+
+def packed_inputs(total, H, D, seed, layout="thd"):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    if layout == "thd":  # [total, H, D] contiguous
+        return [torch.randn(total, H, D, generator=g, device="cuda").to(torch.bfloat16)
+                for _ in range(3)]
+    # [H, total, D] storage viewed as [total, H, D]
+    return [torch.randn(H, total, D, generator=g, device="cuda").to(torch.bfloat16).transpose(0, 1)
+            for _ in range(3)]
+
+
+CASES = [
+    # frames, S, W0, H, D, pairs, element, layout
+    ([21, 8, 3], 1560, 1560, 2, 128, True, False, "thd"),
+    ([5, 12, 1, 7], 1000, 300, 3, 64, False, False, "thd"),
+    ([6, 2, 9], 300, 40, 2, 128, True, True, "htd"),
+    ([4], 256, 256, 1, 64, True, False, "thd"),
+]
+
+
+@pytest.mark.parametrize("frames,S,w0,H,D,pairs,element,layout", CASES)
+def test_varlen_equals_per_sample(frames, S, w0, H, D, pairs, element, layout):
+    masks = [radial.build_mask(f, S, w0, pairs=pairs) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = packed_inputs(total, H, D, seed=len(frames) + D, layout=layout)
+    lse = torch.empty(H, total, dtype=torch.float32, device="cuda")
+    out = radial.attn_fwd_varlen(q, k, v, vm, lse=lse, element=element)
+    t0 = 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        # The sample alone, as [1, H, n, D] views of the packed tensors.
+        qs, ks, vs = (x[sl].permute(1, 0, 2).unsqueeze(0) for x in (q, k, v))
+        ls = torch.empty(1, H, m.n, dtype=torch.float32, device="cuda")
+        os = radial.attn_fwd(qs, ks, vs, m.to("cuda"), lse=ls, element=element)
+        torch.cuda.synchronize()
+        assert torch.equal(out[sl].permute(1, 0, 2).unsqueeze(0), os)
+        assert torch.equal(lse[:, sl], ls[0])
+        t0 += m.n
+
+
+def test_varlen_parity_against_oracle():
+    frames, S, w0, H, D = [6, 3, 11], 1000, 100, 2, 128
+    masks = [radial.build_mask(f, S, w0) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = packed_inputs(total, H, D, seed=21)
+    out = radial.attn_fwd_varlen(q, k, v, vm)
+    torch.cuda.synchronize()
+    t0 = 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        f64 = lambda x: x[sl].permute(1, 0, 2).to("cpu", torch.float64).numpy()  # noqa: E731
+        ref, _ = ro.attention(f64(q), f64(k), f64(v), m.row_ptr.numpy(), m.col_idx.numpy(),
+                              D ** -0.5)
+        err = np.abs(f64(out) - ref)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
+        t0 += m.n
