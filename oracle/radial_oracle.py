@@ -32,6 +32,14 @@ The pages leave some steps open. This module takes the plainest reading of each:
 5. The backward pass (`attention_backward`) is the vector-Jacobian product of the
    same softmax attention over the same key sets; the pages use it for LoRA
    fine-tuning (the SKILL.md page, Step 4: loss.backward() through the attention).
+6. The 2-D grid variant (the SKILL.md page, Step 1, its grid-distance helper): a frame is
+   a latent grid of H rows and W columns stored row by row (S = H * W), so spatial index
+   s sits at row s // W and column s % W, and the spatial distance is the Manhattan
+   distance |row_q - row_k| + |col_q - col_k|. The helper takes a square grid of side
+   sqrt(S); here the caller gives W, and H = S / W. Everything else stays as in reading
+   1: allowed(q, k) <=> distance * 2**floor(log2(d + 1)) < W0. W = S (one row) is the
+   1-D rule of reading 2. The page's other helper, which folds the temporal distance
+   into one combined distance with constants lost from the text, is not used.
 
 Parity pins for every function here are in tests/test_oracle.py. Each pin checks the
 function against something other than itself: brute force with exact rationals, closed
@@ -64,19 +72,35 @@ def token_coords(frames: int, tokens_per_frame: int):
     return t // tokens_per_frame, t % tokens_per_frame
 
 
-def allowed(fq, sq, fk, sk, w0):
-    """Element rule: |s_q - s_k| * 2**floor(log2(|f_q - f_k| + 1)) < W0 (reading 1)."""
-    fq, sq, fk, sk = (np.asarray(x, dtype=np.int64) for x in (fq, sq, fk, sk))
-    return np.abs(sq - sk) * (np.int64(1) << band(np.abs(fq - fk))) < w0
+def spatial_distance(sq, sk, grid_w=None):
+    """In-frame distance: |s_q - s_k| (reading 2), or with a grid width W the Manhattan
+    distance between (s // W, s % W) positions (reading 6)."""
+    sq, sk = np.asarray(sq, dtype=np.int64), np.asarray(sk, dtype=np.int64)
+    if grid_w is None:
+        return np.abs(sq - sk)
+    return np.abs(sq // grid_w - sk // grid_w) + np.abs(sq % grid_w - sk % grid_w)
 
 
-def element_mask(frames: int, tokens_per_frame: int, w0: int) -> np.ndarray:
+def check_grid(tokens_per_frame: int, grid_w):
+    if grid_w is not None and (grid_w < 1 or tokens_per_frame % grid_w):
+        raise ValueError("the grid width must divide the tokens per frame")
+
+
+def allowed(fq, sq, fk, sk, w0, grid_w=None):
+    """Element rule: distance(s_q, s_k) * 2**floor(log2(|f_q - f_k| + 1)) < W0 (reading 1;
+    the distance of reading 2, or of reading 6 with a grid width)."""
+    fq, fk = np.asarray(fq, dtype=np.int64), np.asarray(fk, dtype=np.int64)
+    return spatial_distance(sq, sk, grid_w) * (np.int64(1) << band(np.abs(fq - fk))) < w0
+
+
+def element_mask(frames: int, tokens_per_frame: int, w0: int, grid_w=None) -> np.ndarray:
     """The n x n boolean mask with the rule applied to every (query, key) pair.
 
     Only for small n, because it materialises n**2 booleans.
     """
+    check_grid(tokens_per_frame, grid_w)
     f, s = token_coords(frames, tokens_per_frame)
-    return allowed(f[:, None], s[:, None], f[None, :], s[None, :], w0)
+    return allowed(f[:, None], s[:, None], f[None, :], s[None, :], w0, grid_w)
 
 
 # --------------------------------------------------------------------------------------
@@ -118,15 +142,17 @@ def _frame_pieces(n: int, tokens_per_frame: int, block: int):
 
 
 def block_counts(frames: int, tokens_per_frame: int, w0: int,
-                 block: int = BLOCK) -> np.ndarray:
+                 block: int = BLOCK, grid_w=None) -> np.ndarray:
     """Allowed-element count per (query block, key block), for any size.
 
     The rule depends only on the band of |f_q - f_k| and on (s_q, s_k). So for each band
     value that occurs, the S x S in-frame mask is tabulated and turned into a
     summed-area table with cumsum. An element count over any rectangle of that mask
     then costs four lookups. A block pair is a union of rectangles, one per (query
-    frame piece, key frame piece). The count is an exact integer.
+    frame piece, key frame piece). The count is an exact integer. `grid_w` selects the
+    2-D grid distance (reading 6).
     """
+    check_grid(tokens_per_frame, grid_w)
     S = tokens_per_frame
     n = frames * S
     nb = num_blocks(n, block)
@@ -134,7 +160,7 @@ def block_counts(frames: int, tokens_per_frame: int, w0: int,
     max_band = int(band(frames - 1))
     sat = np.zeros((max_band + 1, S + 1, S + 1), dtype=np.int64)
     for kk in range(max_band + 1):
-        inframe = np.abs(s[:, None] - s[None, :]) * (np.int64(1) << kk) < w0
+        inframe = spatial_distance(s[:, None], s[None, :], grid_w) * (np.int64(1) << kk) < w0
         sat[kk, 1:, 1:] = inframe.astype(np.int64).cumsum(axis=0).cumsum(axis=1)
 
     pieces = _frame_pieces(n, S, block)
@@ -148,9 +174,9 @@ def block_counts(frames: int, tokens_per_frame: int, w0: int,
 
 
 def block_mask(frames: int, tokens_per_frame: int, w0: int,
-               block: int = BLOCK) -> np.ndarray:
+               block: int = BLOCK, grid_w=None) -> np.ndarray:
     """Block (a, b) is active iff it holds at least one allowed element (reading 3)."""
-    return block_counts(frames, tokens_per_frame, w0, block) > 0
+    return block_counts(frames, tokens_per_frame, w0, block, grid_w) > 0
 
 
 def csr(bmask: np.ndarray):
@@ -179,6 +205,17 @@ def row_keys(row_ptr, col_idx, qb: int, n: int, block: int = BLOCK) -> np.ndarra
 # Attention over the active key set
 # --------------------------------------------------------------------------------------
 
+def element_allowed(element, rows: slice, keys) -> np.ndarray:
+    """The element rule between the query rows `rows` and the key tokens `keys`;
+    element = (tokens_per_frame, w0) or (tokens_per_frame, w0, grid_w)."""
+    S, w0, *grid = element
+    grid_w = grid[0] if grid else None
+    check_grid(S, grid_w)
+    qi = np.arange(rows.start, rows.stop, dtype=np.int64)[:, None]
+    kj = np.asarray(keys, dtype=np.int64)[None, :]
+    return allowed(qi // S, qi % S, kj // S, kj % S, w0, grid_w)
+
+
 def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
               query_blocks=None, element=None):
     """fp64 softmax attention, each query block over the keys of its active blocks.
@@ -193,7 +230,8 @@ def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
     element = (tokens_per_frame, w0) switches to element semantics: inside K_i, only the
     keys j that the element rule allows for (i, j) take part (the SKILL.md page, Step 1:
     masked positions are -inf before the softmax). The block mask stays the set of
-    blocks visited; the rule removes single entries inside them.
+    blocks visited; the rule removes single entries inside them. A third entry,
+    (tokens_per_frame, w0, grid_w), takes the 2-D grid distance (reading 6).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -207,10 +245,7 @@ def attention(q, k, v, row_ptr, col_idx, scale: float, block: int = BLOCK,
         keys = row_keys(row_ptr, col_idx, qb, n, block)
         x = scale * (q[..., rows, :] @ np.swapaxes(k[..., keys, :], -1, -2))
         if element is not None:
-            S, w0 = element
-            qi = np.arange(rows.start, rows.stop, dtype=np.int64)[:, None]
-            kj = keys[None, :]
-            x = np.where(allowed(qi // S, qi % S, kj // S, kj % S, w0), x, -np.inf)
+            x = np.where(element_allowed(element, rows, keys), x, -np.inf)
         m = x.max(axis=-1, keepdims=True)
         p = np.exp(x - m)
         denom = p.sum(axis=-1, keepdims=True)
@@ -256,10 +291,7 @@ def attention_backward(q, k, v, do, row_ptr, col_idx, scale: float, block: int =
         keys = row_keys(row_ptr, col_idx, qb, n, block)
         x = scale * (q[..., rows, :] @ np.swapaxes(k[..., keys, :], -1, -2))
         if element is not None:
-            S, w0 = element
-            qi = np.arange(rows.start, rows.stop, dtype=np.int64)[:, None]
-            kj = keys[None, :]
-            x = np.where(allowed(qi // S, qi % S, kj // S, kj % S, w0), x, -np.inf)
+            x = np.where(element_allowed(element, rows, keys), x, -np.inf)
         p = np.exp(x - x.max(axis=-1, keepdims=True))
         p /= p.sum(axis=-1, keepdims=True)
         o = p @ v[..., keys, :]
