@@ -2,7 +2,7 @@
 """Radial attention forward pass on one MI355X: effective TFLOP/s on active blocks.
 
     python bench.py [--steps K] [--warmup W] [--workload wan|hunyuan|long4x|small|tiny]
-                    [--element] [--backward]
+                    [--element] [--backward] [--varlen F1,F2,...]
 
 A step is one call of the block-sparse forward kernel over the whole workload
 (every batch, head and query block), with Q/K/V already resident in HBM. The static mask
@@ -14,7 +14,9 @@ Rank 0 prints one JSON line. --element times element masking instead (the radial
 single entries inside the active blocks; the oracle runs the same option). --backward
 times the backward pass (dq, dk, dv from the forward's o and lse, and a seeded dO),
 counting 2.5 times the forward's work (the usual five products against two), and its
-dense baseline and CPU oracle likewise.
+dense baseline and CPU oracle likewise. --varlen F1,F2,... times one packed launch over
+videos of those frame counts (the workload's frame length, W0, heads and head_dim),
+beside the same samples run as separate launches one after another.
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -134,6 +136,98 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False, do=No
     }
 
 
+def bench_varlen(args, wl, dev):
+    """One packed launch over videos of the given frame counts, against the same samples
+    launched one by one (each as a strided [1, H, n, D] view of the packed tensors)."""
+    import torch
+
+    import block_sparse_attention_radial_amd as radial
+    from block_sparse_attention_radial_amd.inputs import Workload, draw_packed_qkv
+
+    frames = [int(f) for f in args.varlen.split(",")]
+    t0 = time.perf_counter()
+    masks = [radial.build_mask(f, wl.tokens_per_frame, wl.w0) for f in frames]
+    vmask = radial.concat_masks(masks)
+    mask_ms = (time.perf_counter() - t0) * 1e3
+    vdev = vmask.to(dev)
+    mdevs = [m.to(dev) for m in masks]
+    total = sum(m.n for m in masks)
+    q, k, v = draw_packed_qkv(total, wl.heads, wl.head_dim, wl.sigma, seed=0, device=dev)
+    o = torch.empty_like(q)
+    nnz = sum(m.nnz for m in masks)
+    flops = 4 * wl.head_dim * 128 * 128 * nnz * wl.heads
+    log(f"varlen {wl.name} frames {frames}: {total} tokens, {nnz} active blocks, "
+        f"mask build {mask_ms:.2f} ms")
+
+    run = lambda: radial.attn_fwd_varlen(q, k, v, vdev, out=o, element=args.element)  # noqa: E731
+    ms, wall = time_launches(run, args.steps, args.warmup)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"packed: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
+
+    views, t0 = [], 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        views.append(tuple(x[sl].permute(1, 0, 2).unsqueeze(0) for x in (q, k, v, o)))
+        t0 += m.n
+
+    def separate():
+        for (qs, ks, vs, os_), md in zip(views, mdevs):
+            radial.attn_fwd(qs, ks, vs, md, out=os_, element=args.element)
+    sms, _ = time_launches(separate, args.steps, args.warmup)
+    log(f"separate launches: {sms:.3f} ms/step ({flops / (sms * 1e-3) / 1e12:.1f} TFLOP/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # The oracle on the first sample alone (its own [1, H, n, D] views).
+        swl = Workload(f"{wl.name}-sample0", 1, wl.heads, wl.head_dim, frames[0],
+                       wl.tokens_per_frame, wl.w0, wl.sigma)
+        qs, ks, vs, _ = views[0]
+        cpu = cpu_baseline(swl, qs, ks, vs, masks[0], args.cpu_seconds, args.element)
+        log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
+
+    line = result_line(args, tflops, ms, wall, {
+        "workload": f"varlen-{wl.name}", "batch": len(frames), "heads": wl.heads,
+        "head_dim": wl.head_dim, "frames": frames, "tokens_per_frame": wl.tokens_per_frame,
+        "seq_len": total, "w0": wl.w0, "block": 128, "active_blocks": nnz,
+        "total_blocks": sum(m.nb ** 2 for m in masks),
+        "semantics": "element" if args.element else "block", "pass": "forward"},
+        traffic=None, cpu=cpu)
+    line["separate_launches_ms"] = round(sms, 4)
+    line["speedup_vs_separate"] = round(sms / ms, 3)
+    line["mask_build_ms"] = round(mask_ms, 3)
+    print(json.dumps(line), flush=True)
+
+
+def result_line(args, tflops, ms, wall, config, traffic, cpu):
+    """The JSON result line, without the dense baseline fields."""
+    return {
+        "metric": "active-block attention TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 1 GPU",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) q/k/v in bf16 at the workload's shape",
+        "config": config,
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +241,8 @@ def main():
                     help="element masking inside the active blocks (block semantics otherwise)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv) instead of the forward")
+    ap.add_argument("--varlen", default="", metavar="F1,F2,...",
+                    help="time a packed batch of videos with these frame counts")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale "
                          "HBM traffic counters against a kernel of known size")
@@ -177,6 +273,9 @@ def main():
     radial.lib()
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.varlen:
+        bench_varlen(args, wl, dev)
+        return
 
     t0 = time.perf_counter()
     mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
@@ -228,42 +327,17 @@ def main():
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
     traffic = None if args.backward else traffic_bytes(wl.name + ("-element" if args.element else ""))
-    line = {
-        "metric": "active-block attention TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 1 GPU",
-        "value": round(tflops, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) q/k/v in bf16 at the workload's shape",
-        "config": {
-            "workload": wl.name, "batch": wl.batch, "heads": wl.heads,
-            "head_dim": wl.head_dim, "frames": wl.frames,
-            "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
-            "block": 128, "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2,
-            "semantics": "element" if args.element else "block",
-            "pass": "backward" if args.backward else "forward",
-        },
-        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "speedup_vs_dense": None if dense is None else round(dense["speedup"], 3),
-        "dense": None if dense is None else {k_: round(v_, 4) for k_, v_ in dense.items()},
-        "mask_build_ms": round(mask_ms, 3),
-        "wall_s_timed": round(wall, 4),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-        },
-        "cpu_baseline": cpu,
-    }
+    line = result_line(args, tflops, ms, wall, {
+        "workload": wl.name, "batch": wl.batch, "heads": wl.heads,
+        "head_dim": wl.head_dim, "frames": wl.frames,
+        "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
+        "block": 128, "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2,
+        "semantics": "element" if args.element else "block",
+        "pass": "backward" if args.backward else "forward",
+    }, traffic=traffic, cpu=cpu)
+    line["speedup_vs_dense"] = None if dense is None else round(dense["speedup"], 3)
+    line["dense"] = None if dense is None else {k_: round(v_, 4) for k_, v_ in dense.items()}
+    line["mask_build_ms"] = round(mask_ms, 3)
     print(json.dumps(line), flush=True)
 
 

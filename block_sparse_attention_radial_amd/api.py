@@ -28,18 +28,22 @@ _SIGNATURES = {
         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "radial_build_mask": (ctypes.c_int32, [ctypes.c_int32] * 4 + [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
+    "radial_mask_dims_grid": (ctypes.c_int32, [ctypes.c_int32] * 5 + [
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "radial_build_mask_grid": (ctypes.c_int32, [ctypes.c_int32] * 5 + [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
     "radial_build_pairs": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int32, ctypes.c_void_p,
                                             ctypes.POINTER(ctypes.c_int32)]),
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
-        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 6
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_attn_fwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32] + [
-        ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 4 + [ctypes.c_int64] * 2
+        ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 5 + [ctypes.c_int64] * 2
         + [ctypes.c_void_p]),
     "radial_transpose_mask": (ctypes.c_int32, [ctypes.c_int32] + [ctypes.c_void_p] * 4),
     "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
-        ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_int32] * 4
+        ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_error_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
@@ -92,7 +96,9 @@ class Mask:
     `pairs` (optional, int32 [npairs, 2]) says which rows the kernel computes together
     (build_pairs); None means rows 2p and 2p + 1. It changes the time, not the result.
     `col_ptr` / `row_idx` (optional) are the transposed mask the backward pass walks;
-    `transposed()` builds them when absent.
+    `transposed()` builds them when absent. `grid_w` is 0 for the 1-D spatial distance,
+    or the width of the latent grid a frame is stored as (rows of grid_w tokens; the
+    spatial distance is then the Manhattan distance on the grid).
     """
 
     row_ptr: torch.Tensor
@@ -103,6 +109,7 @@ class Mask:
     pairs: torch.Tensor | None = None
     col_ptr: torch.Tensor | None = None
     row_idx: torch.Tensor | None = None
+    grid_w: int = 0
 
     @property
     def n(self) -> int:
@@ -124,7 +131,7 @@ class Mask:
         mv = lambda t: None if t is None else t.to(device)  # noqa: E731
         return Mask(self.row_ptr.to(device), self.col_idx.to(device), self.frames,
                     self.tokens_per_frame, self.w0, mv(self.pairs), mv(self.col_ptr),
-                    mv(self.row_idx))
+                    mv(self.row_idx), self.grid_w)
 
     def transposed(self) -> "Mask":
         """This mask with col_ptr / row_idx filled in (radial_transpose_mask, on the host,
@@ -141,10 +148,24 @@ class Mask:
         return self
 
 
-def mask_dims(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK):
+def _grid_rows(tokens_per_frame: int, grid_w: int | None) -> int:
+    if grid_w is None:
+        return 1
+    if grid_w <= 0 or tokens_per_frame % grid_w:
+        raise ValueError("the grid width must divide the tokens per frame")
+    return tokens_per_frame // grid_w
+
+
+def mask_dims(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK,
+              grid_w: int | None = None):
     nb, nnz = ctypes.c_int32(), ctypes.c_int64()
-    _check("radial_mask_dims", lib().radial_mask_dims(
-        frames, tokens_per_frame, w0, block, ctypes.byref(nb), ctypes.byref(nnz)))
+    if grid_w is None:
+        _check("radial_mask_dims", lib().radial_mask_dims(
+            frames, tokens_per_frame, w0, block, ctypes.byref(nb), ctypes.byref(nnz)))
+    else:
+        _check("radial_mask_dims_grid", lib().radial_mask_dims_grid(
+            frames, _grid_rows(tokens_per_frame, grid_w), grid_w, w0, block,
+            ctypes.byref(nb), ctypes.byref(nnz)))
     return nb.value, nnz.value
 
 
@@ -164,18 +185,25 @@ def build_pairs(row_ptr: torch.Tensor, col_idx: torch.Tensor,
 
 
 def build_mask(frames: int, tokens_per_frame: int, w0: int, block: int = BLOCK,
-               pairs: bool = True) -> Mask:
+               pairs: bool = True, grid_w: int | None = None) -> Mask:
     """The static radial block mask for a frames x tokens_per_frame video (host tensors),
-    with its pair table unless `pairs` is False."""
-    nb, nnz = mask_dims(frames, tokens_per_frame, w0, block)
+    with its pair table unless `pairs` is False. `grid_w` switches to the 2-D grid
+    distance on frames of tokens_per_frame / grid_w rows of grid_w tokens."""
+    nb, nnz = mask_dims(frames, tokens_per_frame, w0, block, grid_w)
     row_ptr = torch.empty(nb + 1, dtype=torch.int32)
     col_idx = torch.empty(max(nnz, 1), dtype=torch.int32)
-    _check("radial_build_mask", lib().radial_build_mask(
-        frames, tokens_per_frame, w0, block, row_ptr.data_ptr(), col_idx.data_ptr(), nnz))
+    if grid_w is None:
+        _check("radial_build_mask", lib().radial_build_mask(
+            frames, tokens_per_frame, w0, block, row_ptr.data_ptr(), col_idx.data_ptr(), nnz))
+    else:
+        _check("radial_build_mask_grid", lib().radial_build_mask_grid(
+            frames, _grid_rows(tokens_per_frame, grid_w), grid_w, w0, block,
+            row_ptr.data_ptr(), col_idx.data_ptr(), nnz))
     col_idx = col_idx[:nnz]
     table = build_pairs(row_ptr, col_idx, tokens_per_frame) if pairs else None
     # The radial mask is symmetric at block level: its transpose is itself.
-    return Mask(row_ptr, col_idx, frames, tokens_per_frame, w0, table, row_ptr, col_idx)
+    return Mask(row_ptr, col_idx, frames, tokens_per_frame, w0, table, row_ptr, col_idx,
+                grid_w or 0)
 
 
 def dense_mask(seqlen: int, device="cpu") -> Mask:
@@ -186,6 +214,15 @@ def dense_mask(seqlen: int, device="cpu") -> Mask:
     return Mask(row_ptr, col_idx, 1, seqlen, 2**31 - 1, None, row_ptr, col_idx)
 
 
+def _element_args(mask, element: bool):
+    """(frame length, W0, grid width) for radial_attn_*: zeros for block semantics."""
+    if not element:
+        return 0, 0, 0
+    if mask.tokens_per_frame < BLOCK:
+        raise ValueError("element masking needs a frame length of at least 128 tokens")
+    return mask.tokens_per_frame, mask.w0, mask.grid_w
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
              scale: float | None = None, out: torch.Tensor | None = None,
              lse: torch.Tensor | None = None, element: bool = False) -> torch.Tensor:
@@ -194,8 +231,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
     Any layout with a contiguous last axis and strides shared by q, k, v and out works,
     e.g. a [B, n, H, D] buffer viewed as [B, H, n, D]. `lse` (optional, fp32 [B, H, n],
     contiguous) receives the natural-log log-sum-exp of every row. `element` applies the
-    radial rule to single entries inside the active blocks, with the mask's frame length
-    and W0 (block semantics otherwise). The call is asynchronous on torch's current
+    radial rule to single entries inside the active blocks, with the mask's frame length,
+    W0 and distance (its grid width; block semantics otherwise). The call is asynchronous on torch's current
     stream.
     """
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
@@ -223,9 +260,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         raise ValueError("lse must be a contiguous float32 [B, H, n] tensor on q's device")
     if scale is None:
         scale = D ** -0.5
-    if element and mask.tokens_per_frame < BLOCK:
-        raise ValueError("element masking needs a frame length of at least 128 tokens")
-    elem_s, elem_w0 = (mask.tokens_per_frame, mask.w0) if element else (0, 0)
+    elem_s, elem_w0, elem_gw = _element_args(mask, element)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check("radial_attn_fwd", lib().radial_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -233,7 +268,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb,
         None if mask.pairs is None else mask.pairs.data_ptr(),
         0 if mask.pairs is None else mask.pairs.shape[0], float(scale), elem_s, elem_w0,
-        B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
+        elem_gw, B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
     return out
 
 
@@ -260,9 +295,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError("the mask must be on the same device as q (Mask.to(device))")
     if scale is None:
         scale = D ** -0.5
-    if element and mask.tokens_per_frame < BLOCK:
-        raise ValueError("element masking needs a frame length of at least 128 tokens")
-    elem_s, elem_w0 = (mask.tokens_per_frame, mask.w0) if element else (0, 0)
+    elem_s, elem_w0, elem_gw = _element_args(mask, element)
     dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
                   for _ in range(3))
     delta = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
@@ -272,7 +305,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
         mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.col_ptr.data_ptr(),
         mask.row_idx.data_ptr(), mask.nb, float(scale), elem_s, elem_w0,
-        B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
+        elem_gw, B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
     return dq, dk, dv
 
 
@@ -316,6 +349,7 @@ class VarlenMask:
     w0: int
     pairs: torch.Tensor | None = None
     npairs: list | None = None
+    grid_w: int = 0
 
     @property
     def batch(self) -> int:
@@ -325,16 +359,17 @@ class VarlenMask:
         return VarlenMask(list(self.seq_tokens), self.row_ptr.to(device), self.col_idx.to(device),
                           self.tokens_per_frame, self.w0,
                           None if self.pairs is None else self.pairs.to(device),
-                          None if self.npairs is None else list(self.npairs))
+                          None if self.npairs is None else list(self.npairs), self.grid_w)
 
 
 def concat_masks(masks: list) -> VarlenMask:
-    """One VarlenMask from per-sample masks of one frame length and W0 (host tensors)."""
+    """One VarlenMask from per-sample masks of one frame length, W0 and distance (host
+    tensors)."""
     if not masks:
         raise ValueError("a varlen batch needs at least one sample")
-    S, w0 = masks[0].tokens_per_frame, masks[0].w0
-    if any(m.tokens_per_frame != S or m.w0 != w0 for m in masks):
-        raise ValueError("the samples must share the frame length and W0")
+    S, w0, gw = masks[0].tokens_per_frame, masks[0].w0, masks[0].grid_w
+    if any(m.tokens_per_frame != S or m.w0 != w0 or m.grid_w != gw for m in masks):
+        raise ValueError("the samples must share the frame length, W0 and grid width")
     rps, off = [], 0
     for m in masks:
         rps.append(m.row_ptr.to("cpu", torch.int32) + off)
@@ -343,12 +378,15 @@ def concat_masks(masks: list) -> VarlenMask:
     return VarlenMask([m.n for m in masks], torch.cat(rps),
                       torch.cat([m.col_idx.to("cpu", torch.int32) for m in masks]), S, w0,
                       torch.cat([m.pairs.to("cpu") for m in masks]) if with_pairs else None,
-                      [m.pairs.shape[0] for m in masks] if with_pairs else None)
+                      [m.pairs.shape[0] for m in masks] if with_pairs else None, gw)
 
 
-def build_varlen_mask(frames: list, tokens_per_frame: int, w0: int, pairs: bool = True):
-    """The radial masks of videos with the given frame counts (one frame length, one W0)."""
-    return concat_masks([build_mask(f, tokens_per_frame, w0, pairs=pairs) for f in frames])
+def build_varlen_mask(frames: list, tokens_per_frame: int, w0: int, pairs: bool = True,
+                      grid_w: int | None = None):
+    """The radial masks of videos with the given frame counts (one frame length, one W0,
+    one distance)."""
+    return concat_masks([build_mask(f, tokens_per_frame, w0, pairs=pairs, grid_w=grid_w)
+                         for f in frames])
 
 
 def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: VarlenMask,
@@ -380,9 +418,7 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Var
         raise ValueError("lse must be a contiguous float32 [H, total_tokens] tensor on q's device")
     if scale is None:
         scale = D ** -0.5
-    if element and mask.tokens_per_frame < BLOCK:
-        raise ValueError("element masking needs a frame length of at least 128 tokens")
-    elem_s, elem_w0 = (mask.tokens_per_frame, mask.w0) if element else (0, 0)
+    elem_s, elem_w0, elem_gw = _element_args(mask, element)
     seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
     npr = None if mask.npairs is None else (ctypes.c_int32 * mask.batch)(*mask.npairs)
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -390,5 +426,5 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Var
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         None if lse is None else lse.data_ptr(), seq, mask.batch, mask.row_ptr.data_ptr(),
         mask.col_idx.data_ptr(), None if mask.pairs is None else mask.pairs.data_ptr(), npr,
-        float(scale), elem_s, elem_w0, H, D, q.stride(1), q.stride(0), stream))
+        float(scale), elem_s, elem_w0, elem_gw, H, D, q.stride(1), q.stride(0), stream))
     return out

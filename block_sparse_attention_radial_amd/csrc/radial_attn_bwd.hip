@@ -55,7 +55,7 @@ struct BwdArgs {
   const int32_t* row_idx;
   int64_t stride_b, stride_h;
   int nb, heads, n, stride_s;
-  int elem_s, elem_w0;
+  int elem_s, elem_gw, elem_w0;  // element masking: frame length, grid width, W0
   float c;      // scale * log2(e)
   float scale;
 };
@@ -140,7 +140,7 @@ __device__ __forceinline__ void store_rows(__bf16* dst_row, const f32x16 (&acc)[
 }
 
 // ---- 2. dQ ----
-template <int D, bool E>
+template <int D, int E>
 __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const BwdArgs a) {
   using T = Tile<D>;
   constexpr int NDB = D / 32, NS = D / 16;
@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
       }
     }
     if (n - kb * kBlock < kBlock) pad_mask_tile(kb * kBlock, n, lane, sacc);
-    if constexpr (E) element_mask_tile(q0 + 32 * wi, kb * kBlock, a.elem_s, a.elem_w0 - 1, lane, sacc);
+    if constexpr (E != 0)
+      element_mask_any<E>(q0 + 32 * wi, kb * kBlock, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane, sacc);
 
     // P^T = 2^(c s - lse2), dS^T = P^T (dP^T - D), packed as the B operands of dQ^T.
     bf16x8 dsk[8];
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
 }
 
 // ---- 3. dK, dV ----
-template <int D, bool E>
+template <int D, int E>
 __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const BwdArgs a) {
   using T = Tile<D>;
   constexpr int NDB = D / 32, NS = D / 16;
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
     }
     // Entries are queries here: padding rows and the element rule mask them.
     if (n - qb * kBlock < kBlock) pad_mask_tile(qb * kBlock, n, lane, sacc);
-    if constexpr (E) element_mask_tile(k0 + 32 * wi, qb * kBlock, a.elem_s, a.elem_w0 - 1, lane, sacc);
+    if constexpr (E != 0)
+      element_mask_any<E>(k0 + 32 * wi, qb * kBlock, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane, sacc);
 
     // P = 2^(c s - lse2) and dS = P (dP - D), per entry (query 32g + 8(e/4) + 4hl + e%4),
     // packed as the B operands of dV^T and dK^T.
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
 
 bool aligned(const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; }
 
-template <int D, bool E>
+template <int D, int E>
 void launch_bwd(const BwdArgs& args, int rows_total, int items, hipStream_t st) {
   constexpr int kRowsPerBlock = kBwdThreads / (D / 8);
   hipLaunchKernelGGL((radial_bwd_delta_kernel<D>), dim3((rows_total + kRowsPerBlock - 1) / kRowsPerBlock),
@@ -410,7 +412,8 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
                                    const int32_t* col_idx, const int32_t* col_ptr,
                                    const int32_t* row_idx, int32_t nb, float scale,
                                    int32_t element_tokens_per_frame, int32_t element_w0,
-                                   int32_t batch, int32_t heads, int32_t seqlen,
+                                   int32_t element_grid_w, int32_t batch, int32_t heads,
+                                   int32_t seqlen,
                                    int32_t head_dim, int64_t stride_b, int64_t stride_h,
                                    int64_t stride_s, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta || !row_ptr ||
@@ -418,7 +421,7 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
     return RADIAL_ERR_INVALID_ARG;
   if (batch <= 0 || heads <= 0 || seqlen <= 0 || nb <= 0) return RADIAL_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
-  if (element_tokens_per_frame != 0 && (element_tokens_per_frame < kBlock || element_w0 < 1))
+  if (!element_args_valid(element_tokens_per_frame, element_w0, element_grid_w))
     return RADIAL_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return RADIAL_ERR_UNSUPPORTED_HEAD_DIM;
   if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
@@ -455,18 +458,21 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
   args.n = seqlen;
   args.stride_s = static_cast<int>(stride_s);
   args.elem_s = element_tokens_per_frame;
+  args.elem_gw = element_grid_w;
   args.elem_w0 = element_w0;
   args.c = scale * kLog2e;
   args.scale = scale;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const bool elem = element_tokens_per_frame != 0;
+  const int mode = element_tokens_per_frame == 0 ? 0 : (element_grid_w == 0 ? 1 : 2);
   const int it = static_cast<int>(items), rt = static_cast<int>(rows_total);
   if (head_dim == 128) {
-    if (elem) launch_bwd<128, true>(args, rt, it, st);
-    else launch_bwd<128, false>(args, rt, it, st);
+    if (mode == 2) launch_bwd<128, 2>(args, rt, it, st);
+    else if (mode == 1) launch_bwd<128, 1>(args, rt, it, st);
+    else launch_bwd<128, 0>(args, rt, it, st);
   } else {
-    if (elem) launch_bwd<64, true>(args, rt, it, st);
-    else launch_bwd<64, false>(args, rt, it, st);
+    if (mode == 2) launch_bwd<64, 2>(args, rt, it, st);
+    else if (mode == 1) launch_bwd<64, 1>(args, rt, it, st);
+    else launch_bwd<64, 0>(args, rt, it, st);
   }
   return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
 }

@@ -99,7 +99,7 @@ struct WaveState {
   bool first;  // some lane of this wave has no reference m yet
   // element rule (element masking only): frame length, W0 - 1, and the first query of
   // the group's row
-  int es, ew0m1, q0;
+  int es, egw, ew0m1, q0;
 };
 
 // This wave's quarter of the copy of key block kb (K or V) into buf.
@@ -220,12 +220,12 @@ __device__ __forceinline__ float tile_max(const WaveState<D>& w, const f32x16 (&
 // p = 2^(c s - m) for this lane's 64 scores, packed as bf16 into pk (the B operands of
 // the PV steps: pk[u] holds the 8 p of accumulator entries 8 (u & 1) .. + 7 of S^T block
 // u >> 1). Returns the lane's sum of p (fp32). hook(u) runs after each step.
-template <int D, bool E, typename Hook>
+template <int D, int E, typename Hook>
 __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sacc)[4],
                                         bf16x8 (&pk)[8], Hook&& hook) {
   // With element masking a lane can still lack m (every key so far masked, m = -inf);
   // its scores are all -inf too, and m = 0 keeps their p at 0 rather than NaN.
-  const float neg_m = E && w.m_run == -INFINITY ? 0.f : -w.m_run;
+  const float neg_m = E != 0 && w.m_run == -INFINITY ? 0.f : -w.m_run;
   // Four independent partial sums (one per step mod 4), each fed by a small tree, so
   // that the adds do not form one long dependency chain.
   float lt[4] = {0.f, 0.f, 0.f, 0.f};
@@ -244,11 +244,11 @@ __device__ __forceinline__ float tile_p(const WaveState<D>& w, const f32x16 (&sa
   return (lt[0] + lt[1]) + (lt[2] + lt[3]);
 }
 
-// Element masking of union tile kb: this wave's queries on the lanes, the tile's keys
-// on the entries.
-template <int D>
+// Element masking of union tile kb (E = 1: 1-D distance, E = 2: grid distance): this
+// wave's queries on the lanes, the tile's keys on the entries.
+template <int D, int E>
 __device__ __forceinline__ void element_mask(const WaveState<D>& w, int kb, f32x16 (&sacc)[4]) {
-  element_mask_tile(w.q0 + 32 * w.wi, kb * kBlock, w.es, w.ew0m1, w.lane, sacc);
+  element_mask_any<E>(w.q0 + 32 * w.wi, kb * kBlock, w.es, w.egw, w.ew0m1, w.lane, sacc);
 }
 
 // Softmax of union tile kb: mask padding keys (and, with E, disallowed entries), turn S
@@ -257,14 +257,14 @@ __device__ __forceinline__ void element_mask(const WaveState<D>& w, int kb, f32x
 // exceeds kTileSumLimit (or is not finite), m is moved to the new row maximum, O and l
 // are rescaled and P is redone. With E a lane whose keys have all been masked so far
 // has m = -inf and takes m from the first tile that gives it a finite maximum.
-template <int D, bool E, typename Hook>
+template <int D, int E, typename Hook>
 __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&sacc)[4],
                                              bf16x8 (&pk)[8], Hook&& hook) {
   // Keys at or past n (only in the last key block) are padding.
   if (w.n - kb * kBlock < kBlock) pad_mask_tile(kb * kBlock, w.n, w.lane, sacc);
-  if constexpr (E) element_mask(w, kb, sacc);
+  if constexpr (E != 0) element_mask<D, E>(w, kb, sacc);
   if (w.first) {
-    if constexpr (E) {
+    if constexpr (E != 0) {
       const float tm = tile_max(w, sacc);
       if (w.m_run == -INFINITY) w.m_run = tm;
       w.first = __builtin_amdgcn_ballot_w64(w.m_run == -INFINITY) != 0;
@@ -277,7 +277,7 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
   if (__builtin_amdgcn_ballot_w64(!(lt <= kTileSumLimit)) != 0) {
     const float m_new = fmaxf(w.m_run, tile_max(w, sacc));
     // A lane still without m (both -inf) keeps its zero O and l.
-    const float alpha = E && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
+    const float alpha = E != 0 && m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(w.m_run - m_new);
     w.m_run = m_new;
     w.l_run *= alpha;
 #pragma unroll
@@ -303,7 +303,7 @@ constexpr uint32_t kInA = 1u << 14, kInB = 1u << 15, kKbMask = kInA - 1;
 // t % 2; the copies of phase 2t overwrite tiles t-1 (K) and t-2 (V), whose last reads were
 // in phase 2t-1. One loop iteration runs tile t's MFMA phase and then its softmax, so S
 // is live only inside an iteration; P is carried to the next iteration's P V.
-template <int D, int G, bool E>
+template <int D, int G, int E>
 __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list, int U,
                                           char* __restrict__ k0, char* __restrict__ k1,
                                           char* __restrict__ v0, char* __restrict__ v1) {
@@ -378,13 +378,13 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
 // not null) at its row 0's entry; the ids [first_id, first_id + np) are this head's
 // items. smem holds two K and two V buffers at fixed offsets, then the union list;
 // counts holds the per-wave sums of the list compaction, then the union length.
-template <int D, bool E>
+template <int D, int E>
 __device__ __forceinline__ void run_item(
     int pid, int first_id, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int np, int nb,
-    int n, float c, int stride_s, int es, int ew0) {
+    int n, float c, int stride_s, int es, int egw, int ew0) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -518,10 +518,11 @@ __device__ __forceinline__ void run_item(
   for (int i = 0; i < D / 32; ++i) w.oacc[i] = f32x16{};
   // reference max of c * s, base-2 units (set by the first tile; -inf = not yet, which
   // element masking can prolong)
-  w.m_run = E ? -INFINITY : 0.f;
+  w.m_run = E != 0 ? -INFINITY : 0.f;
   w.l_run = 0.f;   // sum of p over this lane's keys
   w.first = true;
   w.es = es;
+  w.egw = egw;
   w.ew0m1 = ew0 - 1;
   w.q0 = q0;
 
@@ -593,7 +594,7 @@ struct FwdArgs {
   const int32_t* pairs;
   int64_t stride_b, stride_h;
   int npairs, nb, heads, n, stride_s;
-  int elem_s, elem_w0;
+  int elem_s, elem_gw, elem_w0;
   float c;
   int items, slot;
   // varlen: 0 for a uniform batch, else the number of samples in `plan` (q, k, v, o are
@@ -622,6 +623,7 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.n = ap->n;
   a.stride_s = ap->stride_s;
   a.elem_s = ap->elem_s;
+  a.elem_gw = ap->elem_gw;
   a.elem_w0 = ap->elem_w0;
   a.c = ap->c;
   a.items = ap->items;
@@ -630,7 +632,7 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   return a;
 }
 
-template <int D, bool E>
+template <int D, int E>
 __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs args) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + kListBytes];
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     }
     run_item<D, E>(item, first_id, tid, smem, counts, a.q + base, a.k + base, a.v + base,
                    a.o + base, lse_row, row_ptr, a.col_idx, pairs, np, nb, n, a.c, a.stride_s,
-                   a.elem_s, a.elem_w0);
+                   a.elem_s, a.elem_gw, a.elem_w0);
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -743,7 +745,7 @@ std::atomic<uint32_t> g_next_capture_slot{0};
 
 // The launch shared by the uniform and the varlen entry points: a persistent grid of one
 // workgroup per CU (a multiple of 8, at most one per item) and a counter slot.
-int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, bool elem, void* stream) {
+int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, void* stream) {
   const int cus = cu_count();
   if (cus < 0) return RADIAL_ERR_HIP;
   const int64_t per_xcd = std::min<int64_t>(std::max(cus / 8, 1), (items + 7) / 8);
@@ -757,16 +759,21 @@ int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, bool elem, void* 
   args.slot = static_cast<int>((captured ? kHalf : 0u) + turn % kHalf);
   args.items = static_cast<int>(items);
   const dim3 grid(static_cast<uint32_t>(8 * per_xcd)), block(kThreads);
+  const int mode = args.elem_s == 0 ? 0 : (args.elem_gw == 0 ? 1 : 2);
   if (head_dim == 128) {
-    if (elem)
-      hipLaunchKernelGGL((radial_fwd_kernel<128, true>), grid, block, 0, st, args);
+    if (mode == 2)
+      hipLaunchKernelGGL((radial_fwd_kernel<128, 2>), grid, block, 0, st, args);
+    else if (mode == 1)
+      hipLaunchKernelGGL((radial_fwd_kernel<128, 1>), grid, block, 0, st, args);
     else
-      hipLaunchKernelGGL((radial_fwd_kernel<128, false>), grid, block, 0, st, args);
+      hipLaunchKernelGGL((radial_fwd_kernel<128, 0>), grid, block, 0, st, args);
   } else {
-    if (elem)
-      hipLaunchKernelGGL((radial_fwd_kernel<64, true>), grid, block, 0, st, args);
+    if (mode == 2)
+      hipLaunchKernelGGL((radial_fwd_kernel<64, 2>), grid, block, 0, st, args);
+    else if (mode == 1)
+      hipLaunchKernelGGL((radial_fwd_kernel<64, 1>), grid, block, 0, st, args);
     else
-      hipLaunchKernelGGL((radial_fwd_kernel<64, false>), grid, block, 0, st, args);
+      hipLaunchKernelGGL((radial_fwd_kernel<64, 0>), grid, block, 0, st, args);
   }
   return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
 }
@@ -780,14 +787,12 @@ float base2_scale(float scale) { return fmaxf(scale * kLog2e, FLT_MIN); }
 // Checks shared by both entry points.
 int32_t check_common(const void* q, const void* k, const void* v, const void* o,
                      const int32_t* row_ptr, const int32_t* col_idx, int32_t heads, float scale,
-                     int32_t element_tokens_per_frame, int32_t element_w0, int32_t head_dim) {
+                     int32_t element_tokens_per_frame, int32_t element_w0,
+                     int32_t element_grid_w, int32_t head_dim) {
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
   if (heads <= 0) return RADIAL_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
-  // Element masking: a frame spans at least one 128-key tile, and W0 >= 1 keeps the
-  // diagonal allowed.
-  if (element_tokens_per_frame != 0 &&
-      (element_tokens_per_frame < kBlock || element_w0 < 1))
+  if (!element_args_valid(element_tokens_per_frame, element_w0, element_grid_w))
     return RADIAL_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return RADIAL_ERR_UNSUPPORTED_HEAD_DIM;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -801,11 +806,13 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
                                    float* lse, const int32_t* row_ptr, const int32_t* col_idx,
                                    int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
                                    int32_t element_tokens_per_frame, int32_t element_w0,
-                                   int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
+                                   int32_t element_grid_w, int32_t batch, int32_t heads,
+                                   int32_t seqlen, int32_t head_dim,
                                    int64_t stride_b, int64_t stride_h, int64_t stride_s,
                                    void* stream) {
   const int32_t err = check_common(q, k, v, o, row_ptr, col_idx, heads, scale,
-                                   element_tokens_per_frame, element_w0, head_dim);
+                                   element_tokens_per_frame, element_w0, element_grid_w,
+                                   head_dim);
   if (err != RADIAL_OK) return err;
   if (batch <= 0 || seqlen <= 0 || nb <= 0) return RADIAL_ERR_INVALID_ARG;
   if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
@@ -821,9 +828,9 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
                pairs, stride_b, stride_h, npairs, nb, heads, seqlen,
-               static_cast<int>(stride_s), element_tokens_per_frame, element_w0,
-               base2_scale(scale), 0, 0, 0, {}};
-  return launch_fwd(args, items, head_dim, element_tokens_per_frame != 0, stream);
+               static_cast<int>(stride_s), element_tokens_per_frame, element_grid_w,
+               element_w0, base2_scale(scale), 0, 0, 0, {}};
+  return launch_fwd(args, items, head_dim, stream);
 }
 
 extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
@@ -831,10 +838,12 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
                                           const int32_t* row_ptr, const int32_t* col_idx,
                                           const int32_t* pairs, const int32_t* npairs,
                                           float scale, int32_t element_tokens_per_frame,
-                                          int32_t element_w0, int32_t heads, int32_t head_dim,
+                                          int32_t element_w0, int32_t element_grid_w,
+                                          int32_t heads, int32_t head_dim,
                                           int64_t stride_h, int64_t stride_s, void* stream) {
   const int32_t err = check_common(q, k, v, o, row_ptr, col_idx, heads, scale,
-                                   element_tokens_per_frame, element_w0, head_dim);
+                                   element_tokens_per_frame, element_w0, element_grid_w,
+                                   head_dim);
   if (err != RADIAL_OK) return err;
   if (!seq_tokens || batch <= 0 || (pairs != nullptr && npairs == nullptr))
     return RADIAL_ERR_INVALID_ARG;
@@ -845,7 +854,8 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
   FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
                pairs, 0, stride_h, 0, 0, heads, 0, static_cast<int>(stride_s),
-               element_tokens_per_frame, element_w0, base2_scale(scale), 0, 0, batch, {}};
+               element_tokens_per_frame, element_grid_w, element_w0, base2_scale(scale), 0, 0,
+               batch, {}};
   int64_t tok = 0, rows = 0, prs = 0, items = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t n = seq_tokens[b];
@@ -865,5 +875,5 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
   }
   if (tok > INT32_MAX || items > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
   args.n = static_cast<int>(tok);  // the packed sequence; lse is [heads, n]
-  return launch_fwd(args, items, head_dim, element_tokens_per_frame != 0, stream);
+  return launch_fwd(args, items, head_dim, stream);
 }

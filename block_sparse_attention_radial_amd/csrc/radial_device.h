@@ -200,6 +200,23 @@ __device__ __forceinline__ void tr_read_offsets(int lane, int& base0, int& x0, i
   x1 = (sw1 & ~3) << 4;
 }
 
+// Element masking limits. Token indices stay below 2^21 (16352 blocks of 128), so no
+// spatial distance reaches 2^22: a radius is clamped to kMaxReach without changing the
+// rule, and a frame length is at most kMaxFrame, which keeps every position sum below
+// 2^24 in magnitude.
+constexpr int kMaxReach = 1 << 22;
+constexpr int kMaxFrame = 1 << 22;
+
+// Host check of the element-masking arguments: tokens_per_frame = 0 is block semantics
+// (the others are then ignored); otherwise a frame of 128 .. kMaxFrame tokens (at least
+// one key tile), W0 >= 1 (the diagonal stays allowed) and a grid width of 0 (the 1-D
+// distance) or a divisor of the frame length.
+inline bool element_args_valid(int32_t s, int32_t w0, int32_t grid_w) {
+  if (s == 0) return true;
+  if (s < kBlock || s > kMaxFrame || w0 < 1) return false;
+  return grid_w == 0 || (grid_w > 0 && s % grid_w == 0);
+}
+
 // (a / S, a % S) for 0 <= a < 2^24 and 128 <= S, given inv_s within a few ulp of 1 / S:
 // the float estimate of the quotient is off by at most one, then one correction each way.
 __device__ __forceinline__ void div_frame(int a, int S, float inv_s, int& f, int& s) {
@@ -252,8 +269,8 @@ __device__ __forceinline__ void element_mask_tile(int own0, int ent0, int S, int
   const int cut = S - ks;  // entries with c >= cut are tokens of frame kf + 1
   const int da = fq > kf ? fq - kf : kf - fq;
   const int db = fq > kf + 1 ? fq - kf - 1 : kf + 1 - fq;
-  const int ra = ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(da) + 1u));
-  const int rb = ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(db) + 1u));
+  const int ra = min(ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(da) + 1u)), kMaxReach);
+  const int rb = min(ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(db) + 1u)), kMaxReach);
   const int base = sq - ks;  // c of the entry at the lane's own spatial index, frame kf
   const int lo_a = max(base - ra, 0), hi_a = min(base + ra, cut - 1);
   const int lo_b = max(base + S - rb, cut), hi_b = base + S + rb;
@@ -271,6 +288,80 @@ __device__ __forceinline__ void element_mask_tile(int own0, int ent0, int S, int
       sacc[g][e] = __uint_as_float((keep & __float_as_uint(sacc[g][e])) | (~keep & 0xff800000u));
     }
   }
+}
+
+// Element masking with the 2-D grid distance (the radial-attention-video SKILL.md page,
+// Step 1, its grid-distance helper): a frame of S tokens is a grid of S / W rows of W
+// columns stored row by row, and tokens a and b may meet iff
+//   |y_a - y_b| + |x_a - x_b| <= (W0 - 1) >> floor(log2(|f_a - f_b| + 1)).
+// Lanes and entries are laid out as in element_mask_tile, and the rule is symmetric as
+// well. The tile's 128 entries are walked as segments of one grid row each (the same in
+// every lane): in key row y of frame f, the lane's token reaches the columns
+// [x - t, x + t], t = r(f) - |y_own - y|, which is one run of tile positions. The runs
+// go into the lane's four 32-bit words and are applied as there. There are at most
+// ceil(128 / W) + 1 segments; a frame ends at a row end, so frames add none. Divisions
+// use the float reciprocal with one correction (all indices are below 2^21).
+__device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S, int W,
+                                                       int ew0m1, int lane,
+                                                       f32x16 (&sacc)[4]) {
+  asm volatile("" : "+s"(S), "+s"(W), "+s"(own0));
+  const float inv_s = __builtin_amdgcn_rcpf(static_cast<float>(S));
+  const float inv_w = __builtin_amdgcn_rcpf(static_cast<float>(W));
+  int fq, sq, yq, xq;  // this lane's token
+  div_frame(own0 + (lane & 31), S, inv_s, fq, sq);
+  div_frame(sq, W, inv_w, yq, xq);
+  int fk, sk, yk, x0;  // the tile's first entry (the same in every lane)
+  div_frame(ent0, S, inv_s, fk, sk);
+  div_frame(sk, W, inv_w, yk, x0);
+  int row_end = sk - x0 + W;  // in-frame index one past the segment's row
+  const int sh = 4 * (lane >> 5);  // this lane's entries sit sh positions later
+  uint32_t bits[4] = {0u, 0u, 0u, 0u};
+  for (int c = 0; c < kBlock;) {
+    const int len = min(W - x0, kBlock - c);
+    const int d = fq > fk ? fq - fk : fk - fq;
+    const int r = min(ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(d) + 1u)), kMaxReach);
+    const int t = r - (yq > yk ? yq - yk : yk - yq);
+    // Tile positions of columns [xq - t, xq + t] of this row, clipped to the segment, in
+    // this lane's bit numbering; empty when t < 0.
+    const int lo = max(c + xq - t - x0, c) - sh;
+    const int hi = t < 0 ? lo - 1 : min(c + xq + t - x0, c + len - 1) - sh;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if (c <= 32 * g + 35 && c + len > 32 * g)  // the words the segment can reach
+        bits[g] |= run_bits(lo - 32 * g, hi - 32 * g);
+    c += len;
+    x0 = 0;
+    ++yk;
+    row_end += W;
+    if (row_end > S) {  // the next row is row 0 of the next frame
+      row_end = W;
+      yk = 0;
+      ++fk;
+    }
+  }
+  const uint32_t mine = 0x0f0f0f0fu;  // the bits of this lane's 16 entries of a word
+  const bool full = (bits[0] & bits[1] & bits[2] & bits[3] & mine) == mine;
+  if (__builtin_amdgcn_ballot_w64(!full) == 0) return;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t keep = static_cast<uint32_t>(
+          __builtin_amdgcn_sbfe(static_cast<int>(bits[g]), 8 * (e >> 2) + (e & 3), 1));
+      sacc[g][e] = __uint_as_float((keep & __float_as_uint(sacc[g][e])) | (~keep & 0xff800000u));
+    }
+  }
+}
+
+// Element masking of a tile: E = 1 takes the 1-D distance, E = 2 the grid distance with
+// grid width gw.
+template <int E>
+__device__ __forceinline__ void element_mask_any(int own0, int ent0, int S, int gw, int ew0m1,
+                                                 int lane, f32x16 (&sacc)[4]) {
+  if constexpr (E == 2)
+    element_mask_grid_tile(own0, ent0, S, gw, ew0m1, lane, sacc);
+  else
+    element_mask_tile(own0, ent0, S, ew0m1, lane, sacc);
 }
 
 // Padding of the entries of a tile in accumulator layout: entry (g, e) of a lane is

@@ -30,6 +30,7 @@ class Workload:
     w0: int
     sigma: float
     block: int = 128
+    grid_w: int | None = None  # frames as grids of this width (2-D distance); None: 1-D
 
     @property
     def n(self) -> int:
@@ -57,6 +58,13 @@ WORKLOADS: dict[str, Workload] = {
     "hunyuan": Workload("hunyuanvideo-shaped", 1, 24, 128, 33, 3600, 3600, 1.0),
     # Wan-shaped heads with a 4x longer video: 84 frames x 1560 tokens.
     "long4x": Workload("4x-long-wan-shaped", 1, 40, 128, 84, 1560, 1560, 1.0),
+    # The same token grids with the 2-D grid distance: Wan's 1560 tokens per frame as
+    # 30 rows of 52, HunyuanVideo's 3600 as 45 rows of 80. W0 = rows + columns - 1 is the
+    # smallest window that keeps a frame dense at frame distance 0 (the 1-D workloads'
+    # W0 = S does the same for the 1-D distance).
+    "wan-grid": Workload("wan2.1-14b-shaped-grid", 1, 40, 128, 21, 1560, 81, 1.0, grid_w=52),
+    "hunyuan-grid": Workload("hunyuanvideo-shaped-grid", 1, 24, 128, 33, 3600, 124, 1.0,
+                             grid_w=80),
 }
 
 
@@ -89,3 +97,13 @@ def draw_qkv(wl: Workload, seed: int = 0, device: str | torch.device = "cpu",
              heads: range | None = None):
     """The same draws as `draw_qkv_f32`, rounded to bf16 (round-to-nearest-even)."""
     return tuple(x.to(torch.bfloat16) for x in draw_qkv_f32(wl, seed, device, heads))
+
+
+def draw_packed_qkv(total: int, heads: int, head_dim: int, sigma: float = 1.0, seed: int = 0,
+                    device: str | torch.device = "cpu"):
+    """Packed (varlen) q, k, v of shape [total_tokens, H, D]: N(0, sigma^2) fp32 draws from
+    one generator seeded with `seed`, in the order q, k, v, rounded to bf16."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return tuple((torch.randn((total, heads, head_dim), generator=g, dtype=torch.float32,
+                              device=device) * sigma).to(torch.bfloat16) for _ in range(3))

@@ -79,6 +79,26 @@ int32_t radial_build_mask(int32_t frames, int32_t tokens_per_frame, int32_t w0, 
                           int32_t* row_ptr, int32_t* col_idx, int64_t nnz_capacity);
 
 /*
+ * radial_mask_dims_grid, radial_build_mask_grid — the same two calls for the 2-D grid
+ * variant of the rule (the radial-attention-video SKILL.md page, Step 1, its grid-distance
+ * helper): each frame is a latent grid of grid_h rows of grid_w columns stored row by row
+ * (tokens_per_frame = grid_h * grid_w; in-frame index s sits at row s / grid_w, column
+ * s % grid_w), and the spatial distance is the Manhattan distance between grid positions:
+ *
+ *   key allowed <=> (|y_q - y_k| + |x_q - x_k|) * 2^floor(log2(|f_q - f_k| + 1)) < W0.
+ *
+ * grid_h = 1 gives the 1-D masks of radial_mask_dims / radial_build_mask. Arguments,
+ * outputs and errors are as there, with grid_h and grid_w in place of tokens_per_frame:
+ * INVALID_ARG if frames, grid_h, grid_w or w0 is <= 0; TOO_LARGE if
+ * frames * grid_h * grid_w or the active-block count does not fit in int32.
+ */
+int32_t radial_mask_dims_grid(int32_t frames, int32_t grid_h, int32_t grid_w, int32_t w0,
+                              int32_t block, int32_t* nb_out, int64_t* nnz_out);
+int32_t radial_build_mask_grid(int32_t frames, int32_t grid_h, int32_t grid_w, int32_t w0,
+                               int32_t block, int32_t* row_ptr, int32_t* col_idx,
+                               int64_t nnz_capacity);
+
+/*
  * radial_build_pairs — choose the pairs of query-block rows that the forward kernel
  * computes together. Host code, deterministic.
  *
@@ -133,9 +153,10 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  *             treated as absent rows (never read or written), and a row listed twice is
  *             computed twice.
  * scale:      softmax scale, finite and >= 0 (head_dim^-0.5 is the usual value).
- * element_tokens_per_frame, element_w0: 0 for block semantics (every real key of an
- *             active block takes part). A frame length >= 128 and W0 >= 1 switch on
- *             element masking: inside the active blocks, key j takes part for query i
+ * element_tokens_per_frame, element_w0, element_grid_w: 0 for block semantics
+ *             (every real key of an active block takes part; the other two are then
+ *             ignored). A frame length of 128 .. 2^22 and W0 >= 1 switch on element
+ *             masking: inside the active blocks, key j takes part for query i
  *             only if |s_i - s_j| * 2^floor(log2(|f_i - f_j| + 1)) < W0, with
  *             f = t / frame length and s = t % frame length (frame-major tokens), the
  *             rule of "Radial Attention: A Breakthrough in Efficient Long Video
@@ -145,7 +166,10 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  *             allows outside the CSR's blocks is not visited. Every row must keep at
  *             least one allowed key (the diagonal always is when the CSR comes from
  *             radial_build_mask with the same frame length and W0); a row with none
- *             gets NaN.
+ *             gets NaN. element_grid_w = 0 takes that 1-D distance |s_i - s_j|; a
+ *             divisor W of the frame length takes the grid distance of
+ *             radial_build_mask_grid instead (frames of frame length / W rows of W
+ *             tokens, |y_i - y_j| + |x_i - x_j| with y = s / W, x = s % W).
  * stream:     a hipStream_t, or null for the default stream.
  *
  * Keys at or past seqlen in the last block are excluded. Rows at or past seqlen are
@@ -167,7 +191,8 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  *
  * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim, a pair
  * table with npairs outside [ceil(nb / 2), nb], element masking with a frame length
- * other than 0 below 128 or with W0 < 1),
+ * other than 0 below 128 or above 2^22, with W0 < 1, or with a grid width that is
+ * negative or does not divide the frame length),
  * UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH, MISALIGNED (q/k/v/o not 16-byte aligned, or a
  * stride not a multiple of 8 elements), TOO_LARGE (batch*heads*pairs work items
  * above 2^31 - 1, nb above 16352, or a 128-row tile past 2^31 bytes), HIP (the device
@@ -176,7 +201,8 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
 int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,
                         const int32_t* pairs, int32_t npairs, float scale,
-                        int32_t element_tokens_per_frame, int32_t element_w0, int32_t batch,
+                        int32_t element_tokens_per_frame, int32_t element_w0,
+                        int32_t element_grid_w, int32_t batch,
                         int32_t heads, int32_t seqlen, int32_t head_dim, int64_t stride_b,
                         int64_t stride_h, int64_t stride_s, void* stream);
 
@@ -211,6 +237,7 @@ int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void
                                const int32_t* row_ptr, const int32_t* col_idx,
                                const int32_t* pairs, const int32_t* npairs, float scale,
                                int32_t element_tokens_per_frame, int32_t element_w0,
+                               int32_t element_grid_w,
                                int32_t heads, int32_t head_dim, int64_t stride_h,
                                int64_t stride_s, void* stream);
 
@@ -248,7 +275,7 @@ int32_t radial_transpose_mask(int32_t nb, const int32_t* row_ptr, const int32_t*
  * row_ptr, col_idx: the block mask used by the forward (device).
  * col_ptr, row_idx: its transpose from radial_transpose_mask (device). For a radial mask
  *             these may be row_ptr and col_idx themselves.
- * scale, element_tokens_per_frame, element_w0: as passed to the forward.
+ * scale, element_tokens_per_frame, element_w0, element_grid_w: as passed to the forward.
  * Accumulation is fp32; P and dS enter the matrix products as bf16.
  *
  * Errors: as radial_attn_fwd (INVALID_ARG, UNSUPPORTED_HEAD_DIM, SHAPE_MISMATCH,
@@ -260,6 +287,7 @@ int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void*
                         float* delta, const int32_t* row_ptr, const int32_t* col_idx,
                         const int32_t* col_ptr, const int32_t* row_idx, int32_t nb,
                         float scale, int32_t element_tokens_per_frame, int32_t element_w0,
+                        int32_t element_grid_w,
                         int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
                         int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream);
 

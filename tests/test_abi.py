@@ -26,7 +26,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(
-        ["radial_mask_dims", "radial_build_mask", "radial_build_pairs", "radial_attn_fwd",
+        ["radial_mask_dims", "radial_build_mask", "radial_mask_dims_grid",
+         "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd",
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
          "radial_error_string"])
 
@@ -83,18 +84,39 @@ def test_build_mask_errors():
     assert e.value.code == INVALID
 
 
+def test_grid_mask_errors():
+    lib = radial.lib()
+    nb, nnz = ctypes.c_int32(-9), ctypes.c_int64(-9)
+    args = (ctypes.byref(nb), ctypes.byref(nnz))
+    assert lib.radial_mask_dims_grid(0, 30, 52, 81, 128, *args) == INVALID
+    assert lib.radial_mask_dims_grid(4, 0, 52, 81, 128, *args) == INVALID
+    assert lib.radial_mask_dims_grid(4, 30, -1, 81, 128, *args) == INVALID
+    assert lib.radial_mask_dims_grid(4, 30, 52, 0, 128, *args) == INVALID
+    assert lib.radial_mask_dims_grid(4, 30, 52, 81, 64, *args) == INVALID
+    assert lib.radial_mask_dims_grid(1 << 10, 1 << 11, 1 << 11, 5, 128, *args) == TOO_LARGE
+    assert lib.radial_mask_dims_grid(4, 30, 52, 81, 128, None, None) == INVALID
+    assert lib.radial_mask_dims_grid(2, 16, 16, 31, 128, *args) == OK
+    assert (nb.value, nnz.value) == (4, 16)  # W0 = 31 > 15 + 15: every block at any distance
+    rp = (ctypes.c_int32 * 5)()
+    ci = (ctypes.c_int32 * 16)()
+    assert lib.radial_build_mask_grid(2, 16, 16, 31, 128, rp, ci, 15) == CAPACITY
+    assert lib.radial_build_mask_grid(2, 16, 16, 31, 128, None, ci, 16) == INVALID
+    assert lib.radial_build_mask_grid(2, 16, 16, 31, 128, rp, ci, 16) == OK
+    assert list(rp) == [0, 4, 8, 12, 16]
+
+
 def fwd(**kw):
     """Call radial_attn_fwd with valid-looking defaults, overridden by kw."""
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, row_ptr=0x50000,
              col_idx=0x60000, nb=8, pairs=None, npairs=0, scale=0.125, elem_s=0, elem_w0=0,
-             batch=1, heads=2,
+             elem_gw=0, batch=1, heads=2,
              seqlen=1000, head_dim=128, stride_b=2 * 1000 * 128, stride_h=1000 * 128,
              stride_s=128, stream=None)
     a.update(kw)
     return radial.lib().radial_attn_fwd(
         a["q"], a["k"], a["v"], a["o"], a["lse"], a["row_ptr"], a["col_idx"], a["nb"],
-        a["pairs"], a["npairs"], a["scale"], a["elem_s"], a["elem_w0"], a["batch"], a["heads"],
-        a["seqlen"],
+        a["pairs"], a["npairs"], a["scale"], a["elem_s"], a["elem_w0"], a["elem_gw"],
+        a["batch"], a["heads"], a["seqlen"],
         a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
 
 
@@ -117,9 +139,12 @@ def fwd(**kw):
     # A pair table must hold between ceil(nb / 2) and nb pairs.
     (dict(pairs=0x70000, npairs=3), INVALID), (dict(pairs=0x70000, npairs=9), INVALID),
     (dict(pairs=0x70000, npairs=-1), INVALID),
-    # Element masking needs a frame of at least one tile and W0 >= 1.
+    # Element masking needs a frame of one tile up to 2^22 tokens, W0 >= 1 and a grid
+    # width of 0 or a divisor of the frame length.
     (dict(elem_s=100, elem_w0=50), INVALID), (dict(elem_s=-5, elem_w0=50), INVALID),
-    (dict(elem_s=256, elem_w0=0), INVALID),
+    (dict(elem_s=256, elem_w0=0), INVALID), (dict(elem_s=(1 << 22) + 1, elem_w0=5), INVALID),
+    (dict(elem_s=1560, elem_w0=81, elem_gw=50), INVALID),
+    (dict(elem_s=1560, elem_w0=81, elem_gw=-52), INVALID),
 ])
 def test_attn_fwd_validation(kw, code):
     assert fwd(**kw) == code
@@ -142,13 +167,13 @@ def bwd(**kw):
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, do=0x50000, lse=0x60000,
              dq=0x70000, dk=0x80000, dv=0x90000, delta=0xa0000, row_ptr=0xb0000,
              col_idx=0xc0000, col_ptr=0xd0000, row_idx=0xe0000, nb=8, scale=0.125,
-             elem_s=0, elem_w0=0, batch=1, heads=2, seqlen=1000, head_dim=128,
+             elem_s=0, elem_w0=0, elem_gw=0, batch=1, heads=2, seqlen=1000, head_dim=128,
              stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_s=128, stream=None)
     a.update(kw)
     return radial.lib().radial_attn_bwd(
         a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
         a["delta"], a["row_ptr"], a["col_idx"], a["col_ptr"], a["row_idx"], a["nb"],
-        a["scale"], a["elem_s"], a["elem_w0"], a["batch"], a["heads"], a["seqlen"],
+        a["scale"], a["elem_s"], a["elem_w0"], a["elem_gw"], a["batch"], a["heads"], a["seqlen"],
         a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
 
 
@@ -158,7 +183,7 @@ def bwd(**kw):
         "col_ptr", "row_idx")],
     (dict(batch=0), INVALID), (dict(seqlen=0), INVALID), (dict(scale=-1.0), INVALID),
     (dict(elem_s=64, elem_w0=10), INVALID), (dict(elem_s=256, elem_w0=0), INVALID),
-    (dict(head_dim=96), HEADDIM), (dict(nb=9), SHAPE), (dict(stride_s=64), INVALID),
+    (dict(elem_s=1560, elem_w0=81, elem_gw=7), INVALID), (dict(head_dim=96), HEADDIM), (dict(nb=9), SHAPE), (dict(stride_s=64), INVALID),
     (dict(dk=0x80008), MISALIGNED), (dict(lse=0x60002), MISALIGNED),
     (dict(delta=0xa0001), MISALIGNED), (dict(stride_s=132), MISALIGNED),
     (dict(batch=1 << 12, heads=1 << 12, seqlen=1 << 20, nb=1 << 13,
@@ -207,14 +232,15 @@ def varlen(**kw):
     import ctypes
     a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, seq=[1000, 300], batch=2,
              row_ptr=0x50000, col_idx=0x60000, pairs=None, npairs=None, scale=0.125,
-             elem_s=0, elem_w0=0, heads=2, head_dim=128, stride_h=128, stride_s=256,
+             elem_s=0, elem_w0=0, elem_gw=0, heads=2, head_dim=128, stride_h=128, stride_s=256,
              stream=None)
     a.update(kw)
     seq = None if a["seq"] is None else (ctypes.c_int32 * len(a["seq"]))(*a["seq"])
     npr = None if a["npairs"] is None else (ctypes.c_int32 * len(a["npairs"]))(*a["npairs"])
     return radial.lib().radial_attn_fwd_varlen(
         a["q"], a["k"], a["v"], a["o"], a["lse"], seq, a["batch"], a["row_ptr"], a["col_idx"],
-        a["pairs"], npr, a["scale"], a["elem_s"], a["elem_w0"], a["heads"], a["head_dim"],
+        a["pairs"], npr, a["scale"], a["elem_s"], a["elem_w0"], a["elem_gw"], a["heads"],
+        a["head_dim"],
         a["stride_h"], a["stride_s"], a["stream"])
 
 
@@ -225,7 +251,8 @@ def varlen(**kw):
     (dict(pairs=0x70000, npairs=[9, 2]), INVALID),               # 9 pairs for 8 blocks
     (dict(pairs=0x70000, npairs=[3, 2]), INVALID),               # 3 < ceil(8 / 2)
     (dict(stride_s=64), INVALID), (dict(scale=float("nan")), INVALID),
-    (dict(elem_s=64, elem_w0=5), INVALID), (dict(head_dim=80), HEADDIM),
+    (dict(elem_s=64, elem_w0=5), INVALID), (dict(elem_s=300, elem_w0=5, elem_gw=7), INVALID),
+    (dict(head_dim=80), HEADDIM),
     (dict(v=0x30004), MISALIGNED), (dict(stride_h=132), MISALIGNED),
     (dict(seq=[100] * 65, batch=65), TOO_LARGE),
     (dict(seq=[16353 * 128], batch=1), TOO_LARGE),

@@ -5,7 +5,9 @@ frame length S >= 128, the kernel forms q = trunc(float32(a) * r) with r an appr
 float32 reciprocal of S (v_rcp_f32, within a few ulp), then corrects q by one in either
 direction from the remainder. This test emulates those float32 steps with numpy and
 checks (q, a - qS) against integer division, for every a < 2^21, for reciprocals up to
-+-2 ulp off, and for frame lengths from 128 up to 2^21.
++-2 ulp off, and for frame lengths from 128 up to 2^21. The grid distance splits an
+in-frame index (also below 2^21) by the grid width the same way, so widths from 1 up
+are checked too.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,11 @@ FRAMES = [128, 129, 130, 255, 256, 300, 1000, 1024, 1560, 3600, 4095, 65535, 1 <
           (1 << 21) - 1]
 
 
-@pytest.mark.parametrize("S", FRAMES + np.random.default_rng(0).integers(128, 1 << 21, 12).tolist())
+GRID_WIDTHS = [1, 2, 3, 5, 7, 8, 13, 31, 52, 80, 97, 127]
+
+
+@pytest.mark.parametrize("S", FRAMES + GRID_WIDTHS +
+                         np.random.default_rng(0).integers(128, 1 << 21, 12).tolist())
 def test_float_quotient_with_one_correction_is_exact(S):
     base = np.float32(1.0) / np.float32(S)
     for ulp in range(-2, 3):

@@ -1,0 +1,191 @@
+"""GPU parity of the 2-D grid variant (frames as H x W latent grids, Manhattan spatial
+distance) against the oracle, on the same seeded inputs.
+
+Block semantics needs no kernel change (the grid mask is just another CSR); element
+semantics runs the kernels' grid tile mask. Bars as for the 1-D rule: forward max-abs
+2e-2, mean-abs 2e-3, lse within 1e-3; gradients relative to their size (max 2e-2 of
+max |ref|, mean 5e-3 of mean |ref|). A grid of one row is the 1-D rule, so there the
+two element paths must agree bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_radial_amd as radial
+from block_sparse_attention_radial_amd.inputs import WORKLOADS, Workload, draw_packed_qkv, draw_qkv
+from oracle import radial_oracle as ro
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    radial.lib()
+
+
+def f64(x):
+    return x.detach().to("cpu", torch.float64).numpy()
+
+
+def check(o_gpu, o_ref, rows=None):
+    got = f64(o_gpu)
+    if rows is not None:
+        got, o_ref = got[..., rows, :], o_ref[..., rows, :]
+    err = np.abs(got - o_ref)
+    assert np.isfinite(got).all()
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+def check_rel(got, ref):
+    got = f64(got)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    assert err.max() <= 2e-2 * np.abs(ref).max(), (err.max(), np.abs(ref).max())
+    assert err.mean() <= 5e-3 * np.abs(ref).mean(), (err.mean(), np.abs(ref).mean())
+
+
+SMALL = [
+    # name, B, H, D, F, grid rows, grid columns, W0
+    ("rows-of-50", 1, 2, 128, 6, 20, 50, 12),      # ragged n = 6000
+    ("rows-of-16", 1, 2, 64, 4, 16, 16, 10),       # eight rows per tile
+    ("rows-of-8", 2, 1, 128, 3, 25, 8, 7),         # sixteen segments per tile
+    ("wide-rows", 1, 2, 128, 4, 3, 200, 30),       # rows longer than a tile
+    ("frame-straddle", 1, 2, 64, 7, 10, 13, 6),    # 130-token frames
+    ("huge-window", 1, 1, 128, 5, 12, 25, 2**31 - 1),  # every pair allowed
+]
+
+
+@pytest.mark.parametrize("element", [False, True], ids=["block", "element"])
+@pytest.mark.parametrize("name,B,H,D,F,gh,gw,w0", SMALL, ids=[c[0] for c in SMALL])
+def test_grid_parity_small(name, B, H, D, F, gh, gw, w0, element):
+    S = gh * gw
+    wl = Workload(name, B, H, D, F, S, w0, 1.0, grid_w=gw)
+    q, k, v = draw_qkv(wl, seed=11)
+    mask = radial.build_mask(F, S, w0, grid_w=gw)
+    lse = torch.empty(B, H, wl.n, dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), lse=lse, element=element)
+    torch.cuda.synchronize()
+    ref, ref_lse = ro.attention(f64(q), f64(k), f64(v), mask.row_ptr.numpy(),
+                                mask.col_idx.numpy(), wl.scale,
+                                element=(S, w0, gw) if element else None)
+    check(o, ref)
+    assert np.abs(f64(lse) - ref_lse).max() < 1e-3
+
+
+def test_grid_of_one_row_equals_the_1d_element_path():
+    wl = Workload("one-row", 1, 2, 128, 6, 300, 40, 1.0)
+    q, k, v = (x.cuda() for x in draw_qkv(wl, seed=12))
+    m1 = radial.build_mask(6, 300, 40)
+    m2 = radial.build_mask(6, 300, 40, grid_w=300)
+    assert torch.equal(m1.col_idx, m2.col_idx)
+    o1 = radial.attn_fwd(q, k, v, m1.to("cuda"), element=True)
+    o2 = radial.attn_fwd(q, k, v, m2.to("cuda"), element=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_grid_element_differs_from_the_1d_rule():
+    """The same W0 on the same frames: the grid distance keeps other entries."""
+    wl = Workload("differs", 1, 1, 128, 4, 1000, 30, 1.0)
+    q, k, v = (x.cuda() for x in draw_qkv(wl, seed=13))
+    m1 = radial.build_mask(4, 1000, 30).to("cuda")
+    m2 = radial.build_mask(4, 1000, 30, grid_w=40).to("cuda")
+    o1 = radial.attn_fwd(q, k, v, m1, element=True)
+    o2 = radial.attn_fwd(q, k, v, m2, element=True)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() > 0.05
+
+
+def test_grid_scale_zero_is_mean_over_allowed_keys():
+    """scale = 0: each output row is the plain mean of V over the keys the grid rule
+    allows, which pins the kept set exactly."""
+    F, gh, gw, w0, D = 4, 12, 20, 9, 64
+    S = gh * gw
+    wl = Workload("scale0", 1, 1, D, F, S, w0, 1.0, grid_w=gw)
+    q, k, v = draw_qkv(wl, seed=14)
+    mask = radial.build_mask(F, S, w0, grid_w=gw)
+    o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), scale=0.0, element=True)
+    torch.cuda.synchronize()
+    allowed = ro.element_mask(F, S, w0, grid_w=gw)
+    vv = f64(v)[0, 0]
+    ref = (allowed @ vv) / allowed.sum(axis=1, keepdims=True)
+    check(o[0, 0], ref)
+
+
+@pytest.mark.parametrize("element", [False, True], ids=["block", "element"])
+def test_grid_full_size_sampled_wan(element):
+    """Wan's token grid (21 frames of 30 x 52) on three heads, sampled query blocks."""
+    wl = WORKLOADS["wan-grid"]
+    heads = range(3)
+    q, k, v = draw_qkv(wl, seed=0, device="cuda", heads=heads)
+    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w)
+    o = radial.attn_fwd(q, k, v, mask.to("cuda"), element=element)
+    torch.cuda.synchronize()
+    qbs = [0, 1, 97, 128, 200, wl.nb - 1]
+    ref, _ = ro.attention(f64(q), f64(k), f64(v), mask.row_ptr.numpy(), mask.col_idx.numpy(),
+                          wl.scale, query_blocks=qbs,
+                          element=(wl.tokens_per_frame, wl.w0, wl.grid_w) if element else None)
+    rows = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in qbs])
+    check(o, ref, rows=rows)
+
+
+BWD = [
+    # name, D, F, grid rows, grid columns, W0
+    ("rows-of-50", 128, 6, 20, 50, 12),
+    ("rows-of-8", 64, 3, 25, 8, 7),
+    ("frame-straddle", 128, 7, 10, 13, 6),
+]
+
+
+@pytest.mark.parametrize("name,D,F,gh,gw,w0", BWD, ids=[c[0] for c in BWD])
+def test_grid_element_backward(name, D, F, gh, gw, w0):
+    S = gh * gw
+    wl = Workload(name, 1, 2, D, F, S, w0, 1.0, grid_w=gw)
+    q, k, v = draw_qkv(wl, seed=15)
+    g = torch.Generator().manual_seed(16)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    mask = radial.build_mask(F, S, w0, grid_w=gw)
+    md = mask.to("cuda")
+    qc, kc, vc, dc = (x.cuda() for x in (q, k, v, do))
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(qc, kc, vc, md, lse=lse, element=True)
+    grads = radial.attn_bwd(qc, kc, vc, o, dc, lse, md, element=True)
+    torch.cuda.synchronize()
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), mask.row_ptr.numpy(),
+                                mask.col_idx.numpy(), wl.scale, element=(S, w0, gw))
+    for got, r in zip(grads, ref):
+        check_rel(got, r)
+
+
+def test_grid_varlen_equals_per_sample():
+    frames, gh, gw, w0, H, D = [7, 3, 5], 12, 25, 9, 2, 128
+    S = gh * gw
+    masks = [radial.build_mask(f, S, w0, grid_w=gw) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = draw_packed_qkv(total, H, D, seed=17, device="cuda")
+    out = radial.attn_fwd_varlen(q, k, v, vm, element=True)
+    t0 = 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        qs, ks, vs = (x[sl].permute(1, 0, 2).unsqueeze(0) for x in (q, k, v))
+        os_ = radial.attn_fwd(qs, ks, vs, m.to("cuda"), element=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out[sl].permute(1, 0, 2).unsqueeze(0), os_)
+        t0 += m.n
+
+
+def test_1d_element_with_a_huge_window_is_block_dense():
+    """W0 = 2^31 - 1 with the 1-D distance: every entry of the active blocks is kept."""
+    wl = Workload("huge", 1, 2, 128, 5, 300, 2**31 - 1, 1.0)
+    q, k, v = draw_qkv(wl, seed=18)
+    mask = radial.build_mask(5, 300, 2**31 - 1)
+    o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), element=True)
+    torch.cuda.synchronize()
+    ref, _ = ro.attention(f64(q), f64(k), f64(v), mask.row_ptr.numpy(), mask.col_idx.numpy(),
+                          wl.scale, element=(300, 2**31 - 1))
+    check(o, ref)

@@ -96,3 +96,75 @@ def test_dense_mask_helper():
     m = radial.dense_mask(1000)
     rp, ci = ro.full_csr(1000)
     assert np.array_equal(m.row_ptr.numpy(), rp) and np.array_equal(m.col_idx.numpy(), ci)
+
+
+# --------------------------------------------------------------------------------------
+# 2-D grid distance (frames as H x W grids)
+# --------------------------------------------------------------------------------------
+
+def assert_same_grid(F, H, W, w0):
+    m = radial.build_mask(F, H * W, w0, grid_w=W, pairs=False)
+    orp, oci = ro.csr(ro.block_mask(F, H * W, w0, grid_w=W))
+    assert np.array_equal(m.row_ptr.numpy(), orp), (F, H, W, w0)
+    assert np.array_equal(m.col_idx.numpy(), oci), (F, H, W, w0)
+    assert m.grid_w == W
+
+
+def test_grid_workload_bit_exact():
+    wl = WORKLOADS["wan-grid"]
+    assert_same_grid(wl.frames, wl.tokens_per_frame // wl.grid_w, wl.grid_w, wl.w0)
+
+
+@pytest.mark.slow
+def test_grid_large_workload_bit_exact():
+    wl = WORKLOADS["hunyuan-grid"]
+    assert_same_grid(wl.frames, wl.tokens_per_frame // wl.grid_w, wl.grid_w, wl.w0)
+
+
+@pytest.mark.parametrize("F,H,W,w0", [
+    (6, 20, 50, 12),     # 1000-token frames, narrow window
+    (8, 25, 40, 30),     # rows of 40: a block spans three or four rows
+    (12, 10, 10, 5),     # frames shorter than a block
+    (1, 50, 100, 1),     # one frame, window 1: the diagonal only
+    (3, 1, 300, 20),     # one row: the 1-D rule
+    (3, 300, 1, 20),     # one column: the 1-D rule as well
+    (5, 9, 37, 10**6),   # huge window: block-dense
+    (40, 8, 8, 2),       # many short frames
+    (4, 3, 200, 7),      # rows longer than a block
+    (2, 130, 7, 60),     # rows much shorter than a block
+    (21, 30, 52, 80),    # one below the Wan grid window
+])
+def test_grid_edge_shapes_bit_exact(F, H, W, w0):
+    assert_same_grid(F, H, W, w0)
+
+
+def test_grid_random_sweep_bit_exact():
+    rng = np.random.default_rng(1)
+    for _ in range(30):
+        F = int(rng.integers(1, 13))
+        H = int(rng.integers(1, 41))
+        W = int(rng.integers(1, 61))
+        w0 = int(rng.integers(1, 2 * (H + W) + 2))
+        assert_same_grid(F, H, W, w0)
+
+
+def test_grid_of_one_row_is_the_1d_builder():
+    for F, S, w0 in [(21, 1560, 1560), (6, 1000, 100), (5, 333, 7)]:
+        a = radial.build_mask(F, S, w0, pairs=False)
+        b = radial.build_mask(F, S, w0, pairs=False, grid_w=S)
+        assert np.array_equal(a.row_ptr.numpy(), b.row_ptr.numpy())
+        assert np.array_equal(a.col_idx.numpy(), b.col_idx.numpy())
+
+
+def test_grid_dims_agree_with_build():
+    for F, H, W, w0 in [(21, 30, 52, 81), (6, 20, 50, 12), (1, 1, 1, 1)]:
+        nb, nnz = radial.mask_dims(F, H * W, w0, grid_w=W)
+        m = radial.build_mask(F, H * W, w0, grid_w=W)
+        assert (nb, nnz) == (m.nb, m.nnz)
+
+
+def test_grid_width_must_divide_the_frame():
+    with pytest.raises(ValueError):
+        radial.build_mask(4, 100, 10, grid_w=7)
+    with pytest.raises(ValueError):
+        radial.build_mask(4, 100, 10, grid_w=0)
