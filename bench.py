@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Radial attention forward pass on one MI355X: effective TFLOP/s on active blocks.
 
-    python bench.py [--steps K] [--warmup W] [--workload wan|hunyuan|long4x|small|tiny]
-                    [--element] [--backward] [--varlen F1,F2,...]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload wan|hunyuan|long4x|small|tiny|wan-grid|hunyuan-grid]
+                    [--element] [--backward] [--rule] [--varlen F1,F2,...]
 
 A step is one call of the block-sparse forward kernel over the whole workload
 (every batch, head and query block), with Q/K/V already resident in HBM. The static mask
@@ -16,7 +17,9 @@ times the backward pass (dq, dk, dv from the forward's o and lse, and a seeded d
 counting 2.5 times the forward's work (the usual five products against two), and its
 dense baseline and CPU oracle likewise. --varlen F1,F2,... times one packed launch over
 videos of those frame counts (the workload's frame length, W0, heads and head_dim),
-beside the same samples run as separate launches one after another.
+beside the same samples run as separate launches one after another. --rule times the
+forward with the block mask derived in the kernel from the rule instead of read from the
+CSR (the same key blocks, so the same work is counted).
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -95,10 +98,11 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False, do=No
     from oracle import radial_oracle as ro
 
     t0 = time.perf_counter()
-    ro.block_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+    ro.block_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w)
     mask_s = time.perf_counter() - t0
 
     rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
+    rule = (wl.tokens_per_frame, wl.w0) + ((wl.grid_w,) if wl.grid_w else ())
     order = np.random.default_rng(0).permutation(wl.nb)
     blocks, tiles, heads, elapsed = 0, 0, 0, 0.0
     for h in range(wl.batch * wl.heads):
@@ -110,10 +114,10 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False, do=No
         for qb in order:
             if do is None:
                 ro.attention(qh, kh, vh, rp, ci, wl.scale, query_blocks=[int(qb)],
-                             element=(wl.tokens_per_frame, wl.w0) if element else None)
+                             element=rule if element else None)
             else:  # the backward of this query block (its dq and its share of dk, dv)
                 ro.attention_backward(qh, kh, vh, doh, rp, ci, wl.scale,
-                                      element=(wl.tokens_per_frame, wl.w0) if element else None,
+                                      element=rule if element else None,
                                       query_blocks=[int(qb)])
             blocks += 1
             tiles += int(rp[qb + 1] - rp[qb])
@@ -146,7 +150,7 @@ def bench_varlen(args, wl, dev):
 
     frames = [int(f) for f in args.varlen.split(",")]
     t0 = time.perf_counter()
-    masks = [radial.build_mask(f, wl.tokens_per_frame, wl.w0) for f in frames]
+    masks = [radial.build_mask(f, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w) for f in frames]
     vmask = radial.concat_masks(masks)
     mask_ms = (time.perf_counter() - t0) * 1e3
     vdev = vmask.to(dev)
@@ -180,7 +184,7 @@ def bench_varlen(args, wl, dev):
     if not args.no_cpu_baseline:
         # The oracle on the first sample alone (its own [1, H, n, D] views).
         swl = Workload(f"{wl.name}-sample0", 1, wl.heads, wl.head_dim, frames[0],
-                       wl.tokens_per_frame, wl.w0, wl.sigma)
+                       wl.tokens_per_frame, wl.w0, wl.sigma, grid_w=wl.grid_w)
         qs, ks, vs, _ = views[0]
         cpu = cpu_baseline(swl, qs, ks, vs, masks[0], args.cpu_seconds, args.element)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
@@ -188,7 +192,7 @@ def bench_varlen(args, wl, dev):
     line = result_line(args, tflops, ms, wall, {
         "workload": f"varlen-{wl.name}", "batch": len(frames), "heads": wl.heads,
         "head_dim": wl.head_dim, "frames": frames, "tokens_per_frame": wl.tokens_per_frame,
-        "seq_len": total, "w0": wl.w0, "block": 128, "active_blocks": nnz,
+        "seq_len": total, "w0": wl.w0, "grid_w": wl.grid_w, "block": 128, "active_blocks": nnz,
         "total_blocks": sum(m.nb ** 2 for m in masks),
         "semantics": "element" if args.element else "block", "pass": "forward"},
         traffic=None, cpu=cpu)
@@ -241,6 +245,8 @@ def main():
                     help="element masking inside the active blocks (block semantics otherwise)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv) instead of the forward")
+    ap.add_argument("--rule", action="store_true",
+                    help="derive the block mask in the kernel from the rule (no CSR read)")
     ap.add_argument("--varlen", default="", metavar="F1,F2,...",
                     help="time a packed batch of videos with these frame counts")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -278,9 +284,15 @@ def main():
         return
 
     t0 = time.perf_counter()
-    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w)
     mask_ms = (time.perf_counter() - t0) * 1e3
     mdev = mask.to(dev)
+    if args.rule:
+        if args.backward:
+            print("--rule times the forward only", file=sys.stderr)
+            sys.exit(2)
+        mdev = radial.rule_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w,
+                                pairs=True).to(dev)
     q, k, v = draw_qkv(wl, seed=0, device=dev)
     o = torch.empty_like(q)
     bh = wl.batch * wl.heads
@@ -326,14 +338,17 @@ def main():
         cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds, args.element, do)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
-    traffic = None if args.backward else traffic_bytes(wl.name + ("-element" if args.element else ""))
+    traffic = None if args.backward or args.rule else traffic_bytes(
+        wl.name + ("-element" if args.element else ""))
     line = result_line(args, tflops, ms, wall, {
         "workload": wl.name, "batch": wl.batch, "heads": wl.heads,
         "head_dim": wl.head_dim, "frames": wl.frames,
         "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
+        "grid_w": wl.grid_w,
         "block": 128, "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2,
         "semantics": "element" if args.element else "block",
         "pass": "backward" if args.backward else "forward",
+        "mask": "rule (in-kernel)" if args.rule else "csr",
     }, traffic=traffic, cpu=cpu)
     line["speedup_vs_dense"] = None if dense is None else round(dense["speedup"], 3)
     line["dense"] = None if dense is None else {k_: round(v_, 4) for k_, v_ in dense.items()}

@@ -7,11 +7,12 @@
 The mask builder and the kernels live in libradial.so (C ABI: include/radial_attn.h),
 built in-tree by `python -m block_sparse_attention_radial_amd.build`.
 """
-from .api import (BLOCK, Mask, RadialAttentionFunction, RadialError, VarlenMask, attention,
-                  attn_bwd, attn_fwd, attn_fwd_varlen, build_mask, build_pairs,
-                  build_varlen_mask, concat_masks, dense_mask, error_string, lib, mask_dims)
+from .api import (BLOCK, Mask, RadialAttentionFunction, RadialError, RuleMask, VarlenMask,
+                  attention, attn_bwd, attn_fwd, attn_fwd_varlen, build_mask, build_pairs,
+                  build_varlen_mask, concat_masks, dense_mask, error_string, lib, mask_dims,
+                  rule_mask)
 
-__all__ = ["BLOCK", "Mask", "RadialAttentionFunction", "RadialError", "VarlenMask", "attention",
-           "attn_bwd", "attn_fwd", "attn_fwd_varlen", "build_mask", "build_pairs",
+__all__ = ["BLOCK", "Mask", "RadialAttentionFunction", "RadialError", "RuleMask", "VarlenMask",
+           "attention", "attn_bwd", "attn_fwd", "attn_fwd_varlen", "build_mask", "build_pairs",
            "build_varlen_mask", "concat_masks", "dense_mask", "error_string", "lib",
-           "mask_dims"]
+           "mask_dims", "rule_mask"]

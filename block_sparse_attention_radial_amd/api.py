@@ -38,6 +38,9 @@ _SIGNATURES = {
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_attn_fwd_rule": (ctypes.c_int32, [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 5 + [
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 3
+        + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_attn_fwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32] + [
         ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 5 + [ctypes.c_int64] * 2
         + [ctypes.c_void_p]),
@@ -223,7 +226,54 @@ def _element_args(mask, element: bool):
     return mask.tokens_per_frame, mask.w0, mask.grid_w
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
+@dataclass
+class RuleMask:
+    """The radial mask given by its rule alone: no CSR is stored, the kernel derives each
+    row's key blocks on the fly (radial_attn_fwd_rule). `grid_w` is 0 for the 1-D
+    distance or the grid width; `pairs` (optional int32 [npairs, 2]) is a pair table from
+    build_pairs, as in Mask."""
+
+    frames: int
+    tokens_per_frame: int
+    w0: int
+    grid_w: int = 0
+    pairs: torch.Tensor | None = None
+    _built: Mask | None = None
+
+    @property
+    def n(self) -> int:
+        return self.frames * self.tokens_per_frame
+
+    @property
+    def nb(self) -> int:
+        return (self.n + BLOCK - 1) // BLOCK
+
+    def to(self, device) -> "RuleMask":
+        return RuleMask(self.frames, self.tokens_per_frame, self.w0, self.grid_w,
+                        None if self.pairs is None else self.pairs.to(device), self._built)
+
+    def built(self, device="cpu") -> Mask:
+        """The CSR this rule gives (radial_build_mask / radial_build_mask_grid), cached,
+        on `device`: what the backward pass walks."""
+        if self._built is None:
+            self._built = build_mask(self.frames, self.tokens_per_frame, self.w0,
+                                     pairs=False, grid_w=self.grid_w or None)
+        return self._built.to(device)
+
+
+def rule_mask(frames: int, tokens_per_frame: int, w0: int, grid_w: int | None = None,
+              pairs: bool = False) -> RuleMask:
+    """A RuleMask; with `pairs`, its pair table is built on the host from the CSR (which
+    is then kept for the backward pass)."""
+    _grid_rows(tokens_per_frame, grid_w)
+    m = RuleMask(frames, tokens_per_frame, w0, grid_w or 0)
+    if pairs:
+        m._built = build_mask(frames, tokens_per_frame, w0, pairs=True, grid_w=grid_w)
+        m.pairs = m._built.pairs
+    return m
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask | RuleMask",
              scale: float | None = None, out: torch.Tensor | None = None,
              lse: torch.Tensor | None = None, element: bool = False) -> torch.Tensor:
     """Radial attention forward on q, k, v of shape [B, H, n, D] (bf16, on the GPU).
@@ -232,7 +282,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
     e.g. a [B, n, H, D] buffer viewed as [B, H, n, D]. `lse` (optional, fp32 [B, H, n],
     contiguous) receives the natural-log log-sum-exp of every row. `element` applies the
     radial rule to single entries inside the active blocks, with the mask's frame length,
-    W0 and distance (its grid width; block semantics otherwise). The call is asynchronous on torch's current
+    W0 and distance (its grid width; block semantics otherwise). With a RuleMask the
+    kernel derives the key blocks from the rule instead of reading a CSR. The call is asynchronous on torch's current
     stream.
     """
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
@@ -241,7 +292,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         raise TypeError("q, k, v must be bfloat16")
     if not (q.is_cuda and k.device == q.device and v.device == q.device):
         raise ValueError("q, k, v must be on the same GPU")
-    if mask.row_ptr.device != q.device or mask.col_idx.device != q.device or (
+    rule = isinstance(mask, RuleMask)
+    if (not rule and (mask.row_ptr.device != q.device or mask.col_idx.device != q.device)) or (
             mask.pairs is not None and mask.pairs.device != q.device):
         raise ValueError("the mask must be on the same device as q (Mask.to(device))")
     if mask.pairs is not None and (mask.pairs.dtype != torch.int32 or mask.pairs.dim() != 2
@@ -251,6 +303,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
     if q.stride() != k.stride() or q.stride() != v.stride() or q.stride(-1) != 1:
         raise ValueError("q, k, v must share strides with a contiguous last axis")
     B, H, n, D = q.shape
+    if rule and n != mask.n:
+        raise ValueError("q's sequence length must be frames * tokens_per_frame")
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     elif out.shape != q.shape or out.stride() != q.stride() or out.dtype != q.dtype:
@@ -262,6 +316,15 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
         scale = D ** -0.5
     elem_s, elem_w0, elem_gw = _element_args(mask, element)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if rule:
+        _check("radial_attn_fwd_rule", lib().radial_attn_fwd_rule(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), mask.frames, mask.tokens_per_frame,
+            mask.grid_w, mask.w0, int(bool(element)),
+            None if mask.pairs is None else mask.pairs.data_ptr(),
+            0 if mask.pairs is None else mask.pairs.shape[0], float(scale), B, H, D,
+            q.stride(0), q.stride(1), q.stride(2), stream))
+        return out
     _check("radial_attn_fwd", lib().radial_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         None if lse is None else lse.data_ptr(),
@@ -273,11 +336,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
-             do: torch.Tensor, lse: torch.Tensor, mask: Mask, scale: float | None = None,
+             do: torch.Tensor, lse: torch.Tensor, mask: "Mask | RuleMask",
+             scale: float | None = None,
              element: bool = False):
     """Gradients (dq, dk, dv) of attn_fwd for the output gradient `do`, from the forward's
     output `o` and log-sum-exp `lse` (all on the GPU; layouts as for attn_fwd). The call
-    is asynchronous on torch's current stream."""
+    is asynchronous on torch's current stream. A RuleMask is walked as the CSR its rule
+    gives (built on the host once)."""
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, do)):
         raise ValueError("q, k, v, o, do must share the shape [B, H, n, D]")
     if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, do)):
@@ -289,6 +354,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     B, H, n, D = q.shape
     if lse.shape != (B, H, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be the forward's contiguous float32 [B, H, n] output")
+    if isinstance(mask, RuleMask):
+        mask = mask.built(q.device)
     mask = mask.transposed()
     if any(t.device != q.device for t in (mask.row_ptr, mask.col_idx, mask.col_ptr,
                                           mask.row_idx)):
@@ -330,7 +397,7 @@ class RadialAttentionFunction(torch.autograd.Function):
         return dq, dk, dv, None, None, None
 
 
-def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask,
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask | RuleMask",
               scale: float | None = None, element: bool = False) -> torch.Tensor:
     """Radial attention with autograd support (forward attn_fwd, backward attn_bwd)."""
     return RadialAttentionFunction.apply(q, k, v, mask, scale, element)

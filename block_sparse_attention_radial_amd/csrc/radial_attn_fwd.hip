@@ -290,6 +290,63 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
 // Union-list entry bits.
 constexpr uint32_t kInA = 1u << 14, kInB = 1u << 15, kKbMask = kInA - 1;
 
+// The radial rule for deriving a row's key blocks in the kernel instead of reading them
+// from a CSR: frames of s tokens as grids of gw columns (gw = s for the 1-D distance),
+// base window w0. s = 0: the mask is read from the CSR.
+struct MaskRule {
+  int s, gw, w0;
+};
+typedef __attribute__((address_space(4))) const MaskRule* RulePtr;
+
+// Sets f[kb] for the key blocks of columns [lo, hi] (clipped to the row) of the grid row
+// whose first token is row0.
+__device__ __forceinline__ void mark_run(uint8_t* f, int row0, int lo, int hi, int gw) {
+  lo = max(lo, 0);
+  hi = min(hi, gw - 1);
+  if (lo > hi) return;
+  for (int kb = (row0 + lo) / kBlock; kb <= (row0 + hi) / kBlock; ++kb) f[kb] = 1;
+}
+
+// Marks in f the key blocks of query block `row` under the radial rule (the same sweep
+// as the host builder, radial_build_mask_grid): for a query frame f_q, a key frame f_k
+// at band k and a key grid row y, the radius is r = (W0 - 1) >> k, and the row is
+// reached in at most two runs of columns, from the query block's partial first grid
+// row, its whole middle rows and its partial last row. One (query frame piece, key
+// frame, key row) per thread and step; byte marks are idempotent, so threads that mark
+// the same block do not conflict. n = F * s tokens.
+__device__ __noinline__ void mark_rule_row(uint8_t* f, int row, int n, int s, int gw, int w0,
+                                           int tid) {
+  const int frames = n / s, rows = s / gw;
+  const int t0 = row * kBlock, t1 = min(n, t0 + kBlock);
+  const int fq0 = t0 / s, fq1 = (t1 - 1) / s;
+  const int per_piece = frames * rows;
+  const int items = (fq1 - fq0 + 1) * per_piece;
+  for (int it = tid; it < items; it += kThreads) {
+    const int p = it / per_piece, rem = it - p * per_piece;
+    const int fk = rem / rows, yk = rem - fk * rows;
+    const int fq = fq0 + p;
+    const int a = max(t0 - fq * s, 0), b = min(t1 - fq * s, s) - 1;  // the piece, in frame
+    const int ya = a / gw, xa = a - ya * gw, yb = b / gw, xb = b - yb * gw;
+    const int d = fq > fk ? fq - fk : fk - fq;
+    const int r = min((w0 - 1) >> (31 - __builtin_clz(static_cast<unsigned>(d) + 1u)),
+                      kMaxReach);
+    const int ta = r - (yk > ya ? yk - ya : ya - yk);
+    const int tb = r - (yk > yb ? yk - yb : yb - yk);
+    const int row0 = fk * s + yk * gw;
+    if (ya == yb) {
+      if (ta >= 0) mark_run(f, row0, xa - ta, xb + ta, gw);
+      continue;
+    }
+    const int dm = yk <= ya ? ya + 1 - yk : (yk >= yb ? yk - yb + 1 : 0);
+    if (yb - ya >= 2 && dm <= r) {  // a whole middle row is within reach
+      mark_run(f, row0, 0, gw - 1, gw);
+      continue;
+    }
+    if (ta >= 0) mark_run(f, row0, xa - ta, gw - 1, gw);
+    if (tb >= 0) mark_run(f, row0, 0, xb + tb, gw);
+  }
+}
+
 // The phase loop of group G (G = 0: query block 2p, G = 1: query block 2p+1) over the U
 // union tiles. Phase 2t is group 0's MFMA phase for tile t and group 1's softmax phase
 // for tile t-1; phase 2t+1 is the other way round. Each phase ends at a workgroup
@@ -384,7 +441,7 @@ __device__ __forceinline__ void run_item(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int np, int nb,
-    int n, float c, int stride_s, int es, int egw, int ew0) {
+    int n, float c, int stride_s, int es, int egw, int ew0, RulePtr rule) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -422,28 +479,34 @@ __device__ __forceinline__ void run_item(
                      ? (grp == 0 ? ra : rb) * kBlock
                      : n;
 
-  // ---- union list of the two CSR rows ----
+  // ---- union list of the two rows ----
   // The rows' key blocks are marked in two byte maps over [0, nb) (in the tile buffers,
-  // which are free until the first copy), then every thread compacts a contiguous run
-  // of nb / 512 key blocks into the list at its offset from a workgroup prefix sum. The
-  // list comes out ascending, each block once; column indices outside [0, nb) are
-  // skipped.
+  // which are free until the first copy), from the CSR or, with a rule, derived here;
+  // then every thread compacts a contiguous run of nb / 512 key blocks into the list at
+  // its offset from a workgroup prefix sum. The list comes out ascending, each block
+  // once; column indices outside [0, nb) are skipped.
   {
     const int lane = tid & 63, wv = tid >> 6;
-    const int a0 = ra >= 0 ? row_ptr[ra] : 0, a1 = ra >= 0 ? row_ptr[ra + 1] : 0;
-    const int b0 = rb >= 0 ? row_ptr[rb] : 0, b1 = rb >= 0 ? row_ptr[rb + 1] : 0;
     uint8_t* const fa = reinterpret_cast<uint8_t*>(smem);
     uint8_t* const fb = fa + kMaxBlocks;
     for (int i = tid; i < 2 * kMaxBlocks / 16; i += kThreads)
       reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int i = a0 + tid; i < a1; i += kThreads) {
-      const int x = col_idx[i];
-      if (static_cast<unsigned>(x) < static_cast<unsigned>(nb)) fa[x] = 1;
-    }
-    for (int i = b0 + tid; i < b1; i += kThreads) {
-      const int x = col_idx[i];
-      if (static_cast<unsigned>(x) < static_cast<unsigned>(nb)) fb[x] = 1;
+    const int rule_s = rule->s;
+    if (rule_s > 0) {
+      if (ra >= 0) mark_rule_row(fa, ra, n, rule_s, rule->gw, rule->w0, tid);
+      if (rb >= 0) mark_rule_row(fb, rb, n, rule_s, rule->gw, rule->w0, tid);
+    } else {
+      const int a0 = ra >= 0 ? row_ptr[ra] : 0, a1 = ra >= 0 ? row_ptr[ra + 1] : 0;
+      const int b0 = rb >= 0 ? row_ptr[rb] : 0, b1 = rb >= 0 ? row_ptr[rb + 1] : 0;
+      for (int i = a0 + tid; i < a1; i += kThreads) {
+        const int x = col_idx[i];
+        if (static_cast<unsigned>(x) < static_cast<unsigned>(nb)) fa[x] = 1;
+      }
+      for (int i = b0 + tid; i < b1; i += kThreads) {
+        const int x = col_idx[i];
+        if (static_cast<unsigned>(x) < static_cast<unsigned>(nb)) fb[x] = 1;
+      }
     }
     __syncthreads();
     const int per = (nb + kThreads - 1) / kThreads;
@@ -595,6 +658,7 @@ struct FwdArgs {
   int64_t stride_b, stride_h;
   int npairs, nb, heads, n, stride_s;
   int elem_s, elem_gw, elem_w0;
+  MaskRule rule;  // rule.s > 0: key blocks derived in the kernel (row_ptr/col_idx unused)
   float c;
   int items, slot;
   // varlen: 0 for a uniform batch, else the number of samples in `plan` (q, k, v, o are
@@ -705,7 +769,7 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     }
     run_item<D, E>(item, first_id, tid, smem, counts, a.q + base, a.k + base, a.v + base,
                    a.o + base, lse_row, row_ptr, a.col_idx, pairs, np, nb, n, a.c, a.stride_s,
-                   a.elem_s, a.elem_gw, a.elem_w0);
+                   a.elem_s, a.elem_gw, a.elem_w0, &ap->rule);
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -786,10 +850,10 @@ float base2_scale(float scale) { return fmaxf(scale * kLog2e, FLT_MIN); }
 
 // Checks shared by both entry points.
 int32_t check_common(const void* q, const void* k, const void* v, const void* o,
-                     const int32_t* row_ptr, const int32_t* col_idx, int32_t heads, float scale,
+                     int32_t heads, float scale,
                      int32_t element_tokens_per_frame, int32_t element_w0,
                      int32_t element_grid_w, int32_t head_dim) {
-  if (!q || !k || !v || !o || !row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o) return RADIAL_ERR_INVALID_ARG;
   if (heads <= 0) return RADIAL_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
   if (!element_args_valid(element_tokens_per_frame, element_w0, element_grid_w))
@@ -810,9 +874,9 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
                                    int32_t seqlen, int32_t head_dim,
                                    int64_t stride_b, int64_t stride_h, int64_t stride_s,
                                    void* stream) {
-  const int32_t err = check_common(q, k, v, o, row_ptr, col_idx, heads, scale,
-                                   element_tokens_per_frame, element_w0, element_grid_w,
-                                   head_dim);
+  if (!row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
+  const int32_t err = check_common(q, k, v, o, heads, scale, element_tokens_per_frame,
+                                   element_w0, element_grid_w, head_dim);
   if (err != RADIAL_OK) return err;
   if (batch <= 0 || seqlen <= 0 || nb <= 0) return RADIAL_ERR_INVALID_ARG;
   if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
@@ -829,7 +893,42 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
                static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
                pairs, stride_b, stride_h, npairs, nb, heads, seqlen,
                static_cast<int>(stride_s), element_tokens_per_frame, element_grid_w,
-               element_w0, base2_scale(scale), 0, 0, 0, {}};
+               element_w0, MaskRule{0, 0, 0}, base2_scale(scale), 0, 0, 0, {}};
+  return launch_fwd(args, items, head_dim, stream);
+}
+
+extern "C" int32_t radial_attn_fwd_rule(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int32_t frames, int32_t tokens_per_frame,
+                                        int32_t grid_w, int32_t w0, int32_t element,
+                                        const int32_t* pairs, int32_t npairs, float scale,
+                                        int32_t batch, int32_t heads, int32_t head_dim,
+                                        int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                                        void* stream) {
+  // The rule itself: frames of tokens_per_frame tokens (grids of grid_w columns, or one
+  // row for grid_w = 0), W0 >= 1.
+  if (frames <= 0 || tokens_per_frame <= 0 || w0 <= 0 || grid_w < 0)
+    return RADIAL_ERR_INVALID_ARG;
+  if (grid_w > 0 && tokens_per_frame % grid_w != 0) return RADIAL_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(frames) * tokens_per_frame;
+  if (n > static_cast<int64_t>(kMaxBlocks) * kBlock) return RADIAL_ERR_TOO_LARGE;
+  const int32_t seqlen = static_cast<int32_t>(n);
+  const int32_t err = check_common(q, k, v, o, heads, scale,
+                                   element ? tokens_per_frame : 0, w0, grid_w, head_dim);
+  if (err != RADIAL_OK) return err;
+  if (batch <= 0) return RADIAL_ERR_INVALID_ARG;
+  const int32_t nb = (seqlen + kBlock - 1) / kBlock;
+  if (stride_s < head_dim || stride_h < 0 || stride_b < 0) return RADIAL_ERR_INVALID_ARG;
+  if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
+  if (pairs == nullptr) npairs = (nb + 1) / 2;
+  else if (npairs < (nb + 1) / 2 || npairs > nb) return RADIAL_ERR_INVALID_ARG;
+  const int64_t items = static_cast<int64_t>(batch) * heads * npairs;
+  if (items > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
+  FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+               static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nullptr, nullptr,
+               pairs, stride_b, stride_h, npairs, nb, heads, seqlen,
+               static_cast<int>(stride_s), element ? tokens_per_frame : 0, grid_w, w0,
+               MaskRule{tokens_per_frame, grid_w > 0 ? grid_w : tokens_per_frame, w0},
+               base2_scale(scale), 0, 0, 0, {}};
   return launch_fwd(args, items, head_dim, stream);
 }
 
@@ -841,9 +940,9 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
                                           int32_t element_w0, int32_t element_grid_w,
                                           int32_t heads, int32_t head_dim,
                                           int64_t stride_h, int64_t stride_s, void* stream) {
-  const int32_t err = check_common(q, k, v, o, row_ptr, col_idx, heads, scale,
-                                   element_tokens_per_frame, element_w0, element_grid_w,
-                                   head_dim);
+  if (!row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
+  const int32_t err = check_common(q, k, v, o, heads, scale, element_tokens_per_frame,
+                                   element_w0, element_grid_w, head_dim);
   if (err != RADIAL_OK) return err;
   if (!seq_tokens || batch <= 0 || (pairs != nullptr && npairs == nullptr))
     return RADIAL_ERR_INVALID_ARG;
@@ -854,8 +953,8 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
   FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
                pairs, 0, stride_h, 0, 0, heads, 0, static_cast<int>(stride_s),
-               element_tokens_per_frame, element_grid_w, element_w0, base2_scale(scale), 0, 0,
-               batch, {}};
+               element_tokens_per_frame, element_grid_w, element_w0, MaskRule{0, 0, 0},
+               base2_scale(scale), 0, 0, batch, {}};
   int64_t tok = 0, rows = 0, prs = 0, items = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t n = seq_tokens[b];

@@ -207,6 +207,42 @@ int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int64_t stride_h, int64_t stride_s, void* stream);
 
 /*
+ * radial_attn_fwd_rule — radial_attn_fwd with the block mask derived on the fly in the
+ * kernel instead of read from a CSR. The call is asynchronous on `stream`.
+ *
+ * Each workgroup marks its two query-block rows' active key blocks itself, from the
+ * same rule and with the same sweep as radial_build_mask (grid_w = 0) or
+ * radial_build_mask_grid (grid_w > 0): the mask is static and determined by (frames,
+ * tokens_per_frame, grid_w, w0) ("Radial Attention: A Breakthrough in Efficient Long
+ * Video Generation", How Radial Attention Works), so it need not be stored. Rows are
+ * visited in the same ascending key-block order as with the built CSR, so the output
+ * and lse equal radial_attn_fwd's on that CSR bit for bit.
+ *
+ * frames, tokens_per_frame, w0: the video and base window; seqlen = frames *
+ *             tokens_per_frame (at most 16352 * 128 tokens).
+ * grid_w:     0 for the 1-D spatial distance, or the grid width (a divisor of
+ *             tokens_per_frame) for the 2-D grid distance.
+ * element:    nonzero applies the same rule to single entries inside the active blocks
+ *             (radial_attn_fwd's element masking with element_tokens_per_frame =
+ *             tokens_per_frame, element_w0 = w0, element_grid_w = grid_w).
+ * q, k, v, o, lse, pairs, npairs, scale, batch, heads, head_dim, strides, stream: as
+ *             radial_attn_fwd (a pair table, if given, comes from radial_build_pairs on
+ *             the built mask; null pairs rows 2p and 2p + 1).
+ *
+ * Errors: INVALID_ARG (frames, tokens_per_frame or w0 <= 0, a grid width that is
+ * negative or does not divide tokens_per_frame, element masking with a frame outside
+ * 128 .. 2^22, and radial_attn_fwd's other argument errors), UNSUPPORTED_HEAD_DIM,
+ * MISALIGNED, TOO_LARGE (a sequence above 16352 * 128 tokens, work items past int32),
+ * HIP.
+ */
+int32_t radial_attn_fwd_rule(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int32_t frames, int32_t tokens_per_frame, int32_t grid_w,
+                             int32_t w0, int32_t element, const int32_t* pairs,
+                             int32_t npairs, float scale, int32_t batch, int32_t heads,
+                             int32_t head_dim, int64_t stride_b, int64_t stride_h,
+                             int64_t stride_s, void* stream);
+
+/*
  * radial_attn_fwd_varlen — radial_attn_fwd over a batch of videos of different lengths
  * (each sample its own frame count, so its own mask), packed into one sequence. The
  * call is asynchronous on `stream`.

@@ -27,7 +27,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted(
         ["radial_mask_dims", "radial_build_mask", "radial_mask_dims_grid",
-         "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd",
+         "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd", "radial_attn_fwd_rule",
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
          "radial_error_string"])
 
@@ -260,3 +260,32 @@ def varlen(**kw):
 def test_attn_fwd_varlen_validation(kw, code):
     # Every case here fails a host check: none may reach a launch (the pointers are fake).
     assert varlen(**kw) == code
+
+
+def rule(**kw):
+    """Call radial_attn_fwd_rule with valid-looking defaults, overridden by kw."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, frames=4, s=250, gw=0,
+             w0=100, element=0, pairs=None, npairs=0, scale=0.125, batch=1, heads=2,
+             head_dim=128, stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_s=128,
+             stream=None)
+    a.update(kw)
+    return radial.lib().radial_attn_fwd_rule(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], a["frames"], a["s"], a["gw"], a["w0"],
+        a["element"], a["pairs"], a["npairs"], a["scale"], a["batch"], a["heads"],
+        a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(frames=0), INVALID),
+    (dict(s=0), INVALID), (dict(w0=0), INVALID), (dict(gw=-1), INVALID),
+    (dict(gw=7), INVALID),                                   # 7 does not divide 250
+    (dict(batch=0), INVALID), (dict(heads=0), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(stride_s=64), INVALID), (dict(head_dim=96), HEADDIM),
+    (dict(q=0x10008), MISALIGNED), (dict(stride_h=1000 * 128 + 4), MISALIGNED),
+    (dict(element=1, s=100, frames=10), INVALID),            # element: frame below 128
+    (dict(pairs=0x70000, npairs=3), INVALID), (dict(pairs=0x70000, npairs=9), INVALID),
+    (dict(frames=16353, s=128), TOO_LARGE),                  # past 16352 blocks
+    (dict(frames=1 << 16, s=1 << 16), TOO_LARGE),
+])
+def test_attn_fwd_rule_validation(kw, code):
+    assert rule(**kw) == code
