@@ -227,8 +227,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
     if constexpr (E != 0)
       element_mask_any<E>(q0 + 32 * wi, kb * kBlock, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane, sacc);
 
-    // P^T = 2^(c s - lse2), dS^T = P^T (dP^T - D), packed as the B operands of dQ^T.
-    bf16x8 dsk[8];
+    // Per step u of 16 keys: P^T = 2^(c s - lse2) and dS^T = P^T (dP^T - D), packed as
+    // the B operand of dQ^T += K^T dS^T (d on M, queries on N, keys contracted in
+    // accumulator order), whose MFMAs are issued right away: they run while the VALU
+    // works on step u + 1.
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int g = u >> 1, s2 = u & 1;
@@ -238,15 +240,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + jj], a.c, -lse2));
         d8[jj] = p * (pacc[g][8 * s2 + jj] - dlt);
       }
-      dsk[u] = __builtin_convertvector(d8, bf16x8);
-    }
-    // dQ^T += K^T dS^T (d on M, queries on N, keys contracted in accumulator order).
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
+      const bf16x8 dsk = __builtin_convertvector(d8, bf16x8);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kt, tb0, tx0, tb1, tx1, u, db),
-                                                         dsk[u], dq[db], 0, 0, 0);
+                                                         dsk, dq[db], 0, 0, 0);
+    }
   }
   if (qrow < n) store_rows<D>(a.dq + base + static_cast<int64_t>(qrow) * a.stride_s, dq, a.scale, hl);
 }
@@ -353,7 +352,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
       element_mask_any<E>(k0 + 32 * wi, qb * kBlock, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane, sacc);
 
     // P = 2^(c s - lse2) and dS = P (dP - D), per entry (query 32g + 8(e/4) + 4hl + e%4),
-    // packed as the B operands of dV^T and dK^T.
+    // packed as the B operands of dV^T and dK^T. (Issuing each step's MFMAs right after
+    // its P and dS, as the dQ kernel does, measured 7% slower here: this kernel holds
+    // every register, and the compiler then schedules worse.)
     bf16x8 pk[8], dsk[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
