@@ -226,12 +226,13 @@ __device__ __forceinline__ void div_frame(int a, int S, float inv_s, int& f, int
   if (s < 0) { --f; s += S; }
 }
 
-// Bits lo .. hi (clamped to 0 .. 31) of a 32-bit word.
+// Bits lo .. hi (clamped to 0 .. 31) of a 32-bit word; none when hi < lo. With
+// 0 <= a <= b <= 32, 2^b - 2^a has exactly bits [a, b) set, and its low word needs no
+// case for b = 32: two 64-bit shifts and one add.
 __device__ __forceinline__ uint32_t run_bits(int lo, int hi) {
-  const int a = min(max(lo, 0), 32), b = min(max(hi + 1, 0), 32);  // [a, b)
-  const uint32_t below_b = b >= 32 ? ~0u : (1u << b) - 1u;
-  const uint32_t below_a = a >= 32 ? ~0u : (1u << a) - 1u;
-  return below_b & ~below_a;
+  const int a = min(max(lo, 0), 32);
+  const int b = max(min(hi + 1, 32), a);
+  return static_cast<uint32_t>((1ull << b) - (1ull << a));
 }
 
 // Element masking of a 128 x 128 tile of scores in MFMA accumulator layout (the rule of
@@ -322,9 +323,9 @@ __device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S
     const int r = min(ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(d) + 1u)), kMaxReach);
     const int t = r - (yq > yk ? yq - yk : yk - yq);
     // Tile positions of columns [xq - t, xq + t] of this row, clipped to the segment, in
-    // this lane's bit numbering; empty when t < 0.
+    // this lane's bit numbering. For t < 0 the run is empty as it stands (hi < lo).
     const int lo = max(c + xq - t - x0, c) - sh;
-    const int hi = t < 0 ? lo - 1 : min(c + xq + t - x0, c + len - 1) - sh;
+    const int hi = min(c + xq + t - x0, c + len - 1) - sh;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       if (c <= 32 * g + 35 && c + len > 32 * g)  // the words the segment can reach
