@@ -4,6 +4,12 @@
     mask = build_mask(frames, tokens_per_frame, w0).to("cuda")
     o = attn_fwd(q, k, v, mask)            # q, k, v: bf16 [B, H, n, D] on the GPU
 
+Variants: attn_fwd(..., element=True) applies the rule to single entries inside the
+active blocks; build_mask(..., grid_w=W) takes the 2-D grid distance on frames of W
+columns; rule_mask(...) lets the kernel derive the blocks itself (no CSR);
+attention(...) adds the backward pass for autograd; build_varlen_mask + attn_fwd_varlen
+run a packed batch of videos of different lengths.
+
 The mask builder and the kernels live in libradial.so (C ABI: include/radial_attn.h),
 built in-tree by `python -m block_sparse_attention_radial_amd.build`.
 """
