@@ -16,28 +16,33 @@ sys.path.insert(0, ROOT)
 from oracle import radial_oracle as ro  # noqa: E402
 
 CASES = [
-    # name, frames, tokens_per_frame, w0
-    ("tiny", 4, 256, 256),
-    ("small", 8, 1024, 512),
-    ("wan2.1-14b-shaped", 21, 1560, 1560),
-    ("hunyuanvideo-shaped", 33, 3600, 3600),
-    ("4x-long-wan-shaped", 84, 1560, 1560),
-    ("ragged-sparse", 6, 1000, 100),
-    ("ragged-half", 8, 1000, 334),
-    ("short-frames", 12, 100, 37),
+    # name, frames, tokens_per_frame, w0, grid width (None: the 1-D distance)
+    ("tiny", 4, 256, 256, None),
+    ("small", 8, 1024, 512, None),
+    ("wan2.1-14b-shaped", 21, 1560, 1560, None),
+    ("hunyuanvideo-shaped", 33, 3600, 3600, None),
+    ("4x-long-wan-shaped", 84, 1560, 1560, None),
+    ("ragged-sparse", 6, 1000, 100, None),
+    ("ragged-half", 8, 1000, 334, None),
+    ("short-frames", 12, 100, 37, None),
+    # the 2-D grid distance: Wan's 30 x 52 and HunyuanVideo's 45 x 80 token grids
+    ("wan2.1-14b-shaped-grid", 21, 1560, 81, 52),
+    ("hunyuanvideo-shaped-grid", 33, 3600, 124, 80),
+    ("grid-rows-of-8", 9, 200, 7, 8),
 ]
 
 
 def main():
     out = []
-    for name, F, S, w0 in CASES:
-        counts = ro.block_counts(F, S, w0)
+    for name, F, S, w0, gw in CASES:
+        counts = ro.block_counts(F, S, w0, grid_w=gw)
         row_ptr, col_idx = ro.csr(counts > 0)
         h = hashlib.sha256()
         h.update(row_ptr.astype("<i4").tobytes())
         h.update(col_idx.astype("<i4").tobytes())
         per_row = np.diff(row_ptr)
-        out.append(dict(name=name, frames=F, tokens_per_frame=S, w0=w0, n=F * S,
+        extra = {} if gw is None else {"grid_w": gw}
+        out.append(dict(name=name, frames=F, tokens_per_frame=S, w0=w0, **extra, n=F * S,
                         nb=len(row_ptr) - 1, nnz=int(row_ptr[-1]),
                         row_nnz_min=int(per_row.min()), row_nnz_max=int(per_row.max()),
                         allowed_elements=int(counts.sum()), sha256=h.hexdigest()))

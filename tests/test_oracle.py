@@ -246,7 +246,8 @@ def test_golden_mask_summaries():
     for case in gold["cases"]:
         if case["n"] > 40_000:
             continue  # the large ones are covered by the slow test below
-        bm = ro.block_mask(case["frames"], case["tokens_per_frame"], case["w0"])
+        bm = ro.block_mask(case["frames"], case["tokens_per_frame"], case["w0"],
+                           grid_w=case.get("grid_w"))
         row_ptr, col_idx = ro.csr(bm)
         assert int(row_ptr[-1]) == case["nnz"]
         assert ro_digest(row_ptr, col_idx) == case["sha256"]
@@ -259,7 +260,8 @@ def test_golden_mask_summaries_large():
     for case in gold["cases"]:
         if case["n"] <= 40_000:
             continue
-        bm = ro.block_mask(case["frames"], case["tokens_per_frame"], case["w0"])
+        bm = ro.block_mask(case["frames"], case["tokens_per_frame"], case["w0"],
+                           grid_w=case.get("grid_w"))
         row_ptr, col_idx = ro.csr(bm)
         assert int(row_ptr[-1]) == case["nnz"]
         assert ro_digest(row_ptr, col_idx) == case["sha256"]
