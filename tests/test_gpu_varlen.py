@@ -79,3 +79,35 @@ def test_varlen_parity_against_oracle():
         err = np.abs(f64(out) - ref)
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
         t0 += m.n
+
+
+def test_varlen_sixty_four_samples():
+    """The largest batch the plan holds, with samples from one block up."""
+    rng = np.random.default_rng(5)
+    frames = [int(f) for f in rng.integers(1, 7, size=64)]
+    S, w0, H, D = 120, 30, 2, 64
+    masks = [radial.build_mask(f, S, w0) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = packed_inputs(total, H, D, seed=64)
+    lse = torch.empty(H, total, dtype=torch.float32, device="cuda")
+    out = radial.attn_fwd_varlen(q, k, v, vm, lse=lse)
+    torch.cuda.synchronize()
+    t0 = 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        qs, ks, vs = (x[sl].permute(1, 0, 2).unsqueeze(0) for x in (q, k, v))
+        ls = torch.empty(1, H, m.n, dtype=torch.float32, device="cuda")
+        os_ = radial.attn_fwd(qs, ks, vs, m.to("cuda"), lse=ls)
+        torch.cuda.synchronize()
+        assert torch.equal(out[sl].permute(1, 0, 2).unsqueeze(0), os_)
+        assert torch.equal(lse[:, sl], ls[0])
+        t0 += m.n
+
+
+def test_varlen_rejects_a_sixty_fifth_sample():
+    masks = [radial.build_mask(1, 128, 10) for _ in range(65)]
+    vm = radial.concat_masks(masks).to("cuda")
+    q, k, v = packed_inputs(65 * 128, 1, 64, seed=65)
+    with pytest.raises(radial.RadialError):
+        radial.attn_fwd_varlen(q, k, v, vm)
