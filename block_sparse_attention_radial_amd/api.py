@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import torch
 
@@ -238,7 +238,7 @@ class RuleMask:
     w0: int
     grid_w: int = 0
     pairs: torch.Tensor | None = None
-    _built: Mask | None = None
+    _built: Mask | None = field(default=None, repr=False, compare=False)
 
     @property
     def n(self) -> int:

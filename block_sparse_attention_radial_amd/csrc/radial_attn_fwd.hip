@@ -313,7 +313,8 @@ __device__ __forceinline__ void mark_run(uint8_t* f, int row0, int lo, int hi, i
 // reached in at most two runs of columns, from the query block's partial first grid
 // row, its whole middle rows and its partial last row. One (query frame piece, key
 // frame, key row) per thread and step; byte marks are idempotent, so threads that mark
-// the same block do not conflict. n = F * s tokens.
+// the same block do not conflict. n = F * s tokens. Kept out of line: it runs once per
+// item, and inlined its integer divisions would crowd the item loop's registers.
 __device__ __noinline__ void mark_rule_row(uint8_t* f, int row, int n, int s, int gw, int w0,
                                            int tid) {
   const int frames = n / s, rows = s / gw;

@@ -217,8 +217,10 @@ inline bool element_args_valid(int32_t s, int32_t w0, int32_t grid_w) {
   return grid_w == 0 || (grid_w > 0 && s % grid_w == 0);
 }
 
-// (a / S, a % S) for 0 <= a < 2^24 and 128 <= S, given inv_s within a few ulp of 1 / S:
-// the float estimate of the quotient is off by at most one, then one correction each way.
+// (a / S, a % S) for 0 <= a < 2^24 with a quotient below 2^21 (frame lengths S >= 128,
+// or any grid width when a < 2^21), given inv_s within a few ulp of 1 / S: the float
+// estimate of the quotient is then off by at most one, and one correction each way
+// gives the exact result.
 __device__ __forceinline__ void div_frame(int a, int S, float inv_s, int& f, int& s) {
   f = static_cast<int>(static_cast<float>(a) * inv_s);
   s = a - f * S;
