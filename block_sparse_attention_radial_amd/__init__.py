@@ -8,17 +8,19 @@ Variants: attn_fwd(..., element=True) applies the rule to single entries inside 
 active blocks; build_mask(..., grid_w=W) takes the 2-D grid distance on frames of W
 columns; rule_mask(...) lets the kernel derive the blocks itself (no CSR);
 attention(...) adds the backward pass for autograd; build_varlen_mask + attn_fwd_varlen
-run a packed batch of videos of different lengths.
+(attention_varlen with autograd) run a packed batch of videos of different lengths.
 
 The mask builder and the kernels live in libradial.so (C ABI: include/radial_attn.h),
 built in-tree by `python -m block_sparse_attention_radial_amd.build`.
 """
-from .api import (BLOCK, Mask, RadialAttentionFunction, RadialError, RuleMask, VarlenMask,
-                  attention, attn_bwd, attn_fwd, attn_fwd_varlen, build_mask, build_pairs,
+from .api import (BLOCK, Mask, RadialAttentionFunction, RadialAttentionVarlenFunction,
+                  RadialError, RuleMask, VarlenMask, attention, attention_varlen, attn_bwd,
+                  attn_bwd_varlen, attn_fwd, attn_fwd_varlen, build_mask, build_pairs,
                   build_varlen_mask, concat_masks, dense_mask, error_string, lib, mask_dims,
                   rule_mask)
 
-__all__ = ["BLOCK", "Mask", "RadialAttentionFunction", "RadialError", "RuleMask", "VarlenMask",
-           "attention", "attn_bwd", "attn_fwd", "attn_fwd_varlen", "build_mask", "build_pairs",
+__all__ = ["BLOCK", "Mask", "RadialAttentionFunction", "RadialAttentionVarlenFunction",
+           "RadialError", "RuleMask", "VarlenMask", "attention", "attention_varlen", "attn_bwd",
+           "attn_bwd_varlen", "attn_fwd", "attn_fwd_varlen", "build_mask", "build_pairs",
            "build_varlen_mask", "concat_masks", "dense_mask", "error_string", "lib",
            "mask_dims", "rule_mask"]

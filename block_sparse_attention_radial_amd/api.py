@@ -48,6 +48,9 @@ _SIGNATURES = {
     "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
         ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_attn_bwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 11 + [ctypes.c_int32] + [
+        ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 5 + [ctypes.c_int64] * 2
+        + [ctypes.c_void_p]),
     "radial_error_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
@@ -407,7 +410,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask | R
 class VarlenMask:
     """The block masks of a varlen batch, concatenated as radial_attn_fwd_varlen takes
     them: sample b's row_ptr (rebased to index the concatenated col_idx) follows those of
-    the samples before it, and likewise its pair table."""
+    the samples before it, and likewise its pair table and (for the backward pass) its
+    transposed mask col_ptr / row_idx."""
 
     seq_tokens: list
     row_ptr: torch.Tensor
@@ -417,16 +421,19 @@ class VarlenMask:
     pairs: torch.Tensor | None = None
     npairs: list | None = None
     grid_w: int = 0
+    col_ptr: torch.Tensor | None = None
+    row_idx: torch.Tensor | None = None
 
     @property
     def batch(self) -> int:
         return len(self.seq_tokens)
 
     def to(self, device) -> "VarlenMask":
+        mv = lambda t: None if t is None else t.to(device)  # noqa: E731
         return VarlenMask(list(self.seq_tokens), self.row_ptr.to(device), self.col_idx.to(device),
-                          self.tokens_per_frame, self.w0,
-                          None if self.pairs is None else self.pairs.to(device),
-                          None if self.npairs is None else list(self.npairs), self.grid_w)
+                          self.tokens_per_frame, self.w0, mv(self.pairs),
+                          None if self.npairs is None else list(self.npairs), self.grid_w,
+                          mv(self.col_ptr), mv(self.row_idx))
 
 
 def concat_masks(masks: list) -> VarlenMask:
@@ -437,15 +444,20 @@ def concat_masks(masks: list) -> VarlenMask:
     S, w0, gw = masks[0].tokens_per_frame, masks[0].w0, masks[0].grid_w
     if any(m.tokens_per_frame != S or m.w0 != w0 or m.grid_w != gw for m in masks):
         raise ValueError("the samples must share the frame length, W0 and grid width")
-    rps, off = [], 0
+    rps, cps, off, off_t = [], [], 0, 0
     for m in masks:
+        m.transposed()
         rps.append(m.row_ptr.to("cpu", torch.int32) + off)
+        cps.append(m.col_ptr.to("cpu", torch.int32) + off_t)
         off += m.nnz
+        off_t += m.row_idx.numel()
     with_pairs = all(m.pairs is not None for m in masks)
     return VarlenMask([m.n for m in masks], torch.cat(rps),
                       torch.cat([m.col_idx.to("cpu", torch.int32) for m in masks]), S, w0,
                       torch.cat([m.pairs.to("cpu") for m in masks]) if with_pairs else None,
-                      [m.pairs.shape[0] for m in masks] if with_pairs else None, gw)
+                      [m.pairs.shape[0] for m in masks] if with_pairs else None, gw,
+                      torch.cat(cps),
+                      torch.cat([m.row_idx.to("cpu", torch.int32) for m in masks]))
 
 
 def build_varlen_mask(frames: list, tokens_per_frame: int, w0: int, pairs: bool = True,
@@ -495,3 +507,71 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Var
         mask.col_idx.data_ptr(), None if mask.pairs is None else mask.pairs.data_ptr(), npr,
         float(scale), elem_s, elem_w0, elem_gw, H, D, q.stride(1), q.stride(0), stream))
     return out
+
+
+def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    do: torch.Tensor, lse: torch.Tensor, mask: VarlenMask,
+                    scale: float | None = None, element: bool = False):
+    """Gradients (dq, dk, dv) of attn_fwd_varlen on a packed batch [total_tokens, H, D],
+    from its output `o` and lse [H, total_tokens]. Asynchronous on torch's current
+    stream."""
+    if q.dim() != 3 or any(t.shape != q.shape for t in (k, v, o, do)):
+        raise ValueError("q, k, v, o, do must share the shape [total_tokens, H, D]")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, do)):
+        raise TypeError("q, k, v, o, do must be bfloat16")
+    if not q.is_cuda or any(t.device != q.device for t in (k, v, o, do, lse)):
+        raise ValueError("every tensor must be on the same GPU")
+    if any(t.stride() != q.stride() for t in (k, v, o, do)) or q.stride(-1) != 1:
+        raise ValueError("q, k, v, o, do must share strides with a contiguous last axis")
+    total, H, D = q.shape
+    if sum(mask.seq_tokens) != total:
+        raise ValueError("the samples' lengths must add up to q's token count")
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [H, total_tokens] output")
+    if mask.col_ptr is None or mask.row_idx is None:
+        raise ValueError("the mask has no transposed rows (build it with concat_masks)")
+    if any(t.device != q.device for t in (mask.row_ptr, mask.col_idx, mask.col_ptr,
+                                          mask.row_idx)):
+        raise ValueError("the mask must be on the same device as q (VarlenMask.to(device))")
+    if scale is None:
+        scale = D ** -0.5
+    elem_s, elem_w0, elem_gw = _element_args(mask, element)
+    dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+                  for _ in range(3))
+    delta = torch.empty(H, total, dtype=torch.float32, device=q.device)
+    seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check("radial_attn_bwd_varlen", lib().radial_attn_bwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), seq, mask.batch,
+        mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.col_ptr.data_ptr(),
+        mask.row_idx.data_ptr(), float(scale), elem_s, elem_w0, elem_gw, H, D, q.stride(1),
+        q.stride(0), stream))
+    return dq, dk, dv
+
+
+class RadialAttentionVarlenFunction(torch.autograd.Function):
+    """attn_fwd_varlen with its backward (attn_bwd_varlen) for autograd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask, scale, element):
+        total, H, _ = q.shape
+        lse = torch.empty(H, total, dtype=torch.float32, device=q.device)
+        o = attn_fwd_varlen(q, k, v, mask, scale=scale, lse=lse, element=element)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.mask, ctx.scale, ctx.element = mask, scale, element
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        do = do if do.stride() == q.stride() else do.as_strided(q.shape, q.stride()).copy_(do)
+        dq, dk, dv = attn_bwd_varlen(q, k, v, o, do, lse, ctx.mask, scale=ctx.scale,
+                                     element=ctx.element)
+        return dq, dk, dv, None, None, None
+
+
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: VarlenMask,
+                     scale: float | None = None, element: bool = False) -> torch.Tensor:
+    """Radial attention on a packed varlen batch with autograd support."""
+    return RadialAttentionVarlenFunction.apply(q, k, v, mask, scale, element)

@@ -38,6 +38,15 @@ namespace {
 
 constexpr int kBwdThreads = 256;  // four wave64, one per SIMD
 
+// One sample of a varlen batch: its first token in the packed sequence, its length and
+// block count, the offset of its rows in the concatenated row_ptr and col_ptr (nb + 1
+// entries per sample), and its first workgroup id (workgroups go sample by sample, head
+// by head, block by block).
+struct BwdSample {
+  int tok0, n, nb, rp0, wg0, pad0, pad1, pad2;
+};
+constexpr int kMaxBwdVarlen = 64;
+
 struct BwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -58,7 +67,60 @@ struct BwdArgs {
   int elem_s, elem_gw, elem_w0;  // element masking: frame length, grid width, W0
   float c;      // scale * log2(e)
   float scale;
+  // varlen: 0 for a uniform batch, else the number of samples in `plan`; q, k, v, o, dO,
+  // dq, dk, dv are then one packed sequence of n tokens, and lse, delta are [heads, n].
+  int varlen;
+  BwdSample plan[kMaxBwdVarlen];
 };
+typedef __attribute__((address_space(4))) const BwdArgs* BwdArgsPtr;
+
+// Where a dq or dkdv workgroup works: the (batch, head) element offset, its rows of lse
+// and delta, its mask rows (row_ptr / col_ptr point at its sample's), its sequence length
+// and block count, and its block. Varlen plans are read from the kernel-argument segment
+// (scalar loads; a copy of the plan would go to scratch memory under a dynamic index).
+struct BwdGeometry {
+  int64_t base;
+  const float* lse;
+  const float* delta;
+  const int32_t* row_ptr;
+  const int32_t* col_ptr;
+  int n, nb, blk;
+};
+
+__device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
+  BwdGeometry g;
+  if (a.varlen == 0) {
+    const int bh = wg / a.nb;
+    const int b = bh / a.heads, h = bh - b * a.heads;
+    g.base = b * a.stride_b + h * a.stride_h;
+    g.lse = a.lse + static_cast<int64_t>(bh) * a.n;
+    g.delta = a.delta + static_cast<int64_t>(bh) * a.n;
+    g.row_ptr = a.row_ptr;
+    g.col_ptr = a.col_ptr;
+    g.n = a.n;
+    g.nb = a.nb;
+    g.blk = wg - bh * a.nb;
+    return g;
+  }
+  const BwdArgsPtr ap = (BwdArgsPtr)(__builtin_amdgcn_kernarg_segment_ptr());
+  int lo = 0, hi = a.varlen - 1;  // the last sample whose first workgroup is at most wg
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ap->plan[mid].wg0 <= wg) lo = mid;
+    else hi = mid - 1;
+  }
+  const int tok0 = ap->plan[lo].tok0, nb = ap->plan[lo].nb, rp0 = ap->plan[lo].rp0;
+  const int h = (wg - ap->plan[lo].wg0) / nb;
+  g.base = static_cast<int64_t>(tok0) * a.stride_s + h * a.stride_h;
+  g.lse = a.lse + static_cast<int64_t>(h) * a.n + tok0;
+  g.delta = a.delta + static_cast<int64_t>(h) * a.n + tok0;
+  g.row_ptr = a.row_ptr + rp0;
+  g.col_ptr = a.col_ptr + rp0;
+  g.n = ap->plan[lo].n;
+  g.nb = nb;
+  g.blk = wg - ap->plan[lo].wg0 - h * nb;
+  return g;
+}
 
 // ---- 1. D_i = <do_i, o_i> ----
 // D / 8 lanes per row, 8 bf16 each; 256 / (D / 8) rows per workgroup.
@@ -71,8 +133,9 @@ __global__ __launch_bounds__(kBwdThreads) void radial_bwd_delta_kernel(const Bwd
   const int ch = tid % kLanes;
   float acc = 0.f;
   if (r < rows_total) {
+    // Row r of delta's layout: [batch, heads, n], or [heads, n] of a packed varlen batch.
     const int bh = r / a.n, i = r - bh * a.n;
-    const int b = bh / a.heads, h = bh - b * a.heads;
+    const int b = a.varlen ? 0 : bh / a.heads, h = a.varlen ? bh : bh - b * a.heads;
     const int64_t off = b * a.stride_b + h * a.stride_h + static_cast<int64_t>(i) * a.stride_s +
                         8 * ch;
     const bf16x8 ov = *reinterpret_cast<const bf16x8*>(a.o + off);
@@ -148,10 +211,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
   char* const kb0 = smem;
   char* const vb0 = smem + 2 * T::kBytes;
 
-  const int nb = a.nb, n = a.n;
-  const int bh = blockIdx.x / nb, qb = blockIdx.x - bh * nb;
-  const int b = bh / a.heads, h = bh - b * a.heads;
-  const int64_t base = b * a.stride_b + h * a.stride_h;
+  const BwdGeometry geo = bwd_geometry(a, blockIdx.x);
+  const int nb = geo.nb, n = geo.n, qb = geo.blk;
+  const int64_t base = geo.base;
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row_bytes = a.stride_s * 2;
@@ -163,8 +225,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
   // This lane's query: its log-sum-exp in base 2 and D_i.
   float lse2 = 0.f, dlt = 0.f;
   if (qrow < n) {
-    lse2 = a.lse[static_cast<int64_t>(bh) * n + qrow] * kLog2e;
-    dlt = a.delta[static_cast<int64_t>(bh) * n + qrow];
+    lse2 = geo.lse[qrow] * kLog2e;
+    dlt = geo.delta[qrow];
   }
   int copy_off[T::kOffsetPeriod];
   copy_offsets<D>(wi, lane, row_bytes, copy_off);
@@ -172,8 +234,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
   row_read_offsets<D>(lane, rbase, rx);
   tr_read_offsets<D>(lane, tb0, tx0, tb1, tx1);
 
-  const int r0 = a.row_ptr[qb];
-  const int L = a.row_ptr[qb + 1] - r0;
+  const int r0 = geo.row_ptr[qb];
+  const int L = geo.row_ptr[qb + 1] - r0;
   auto column = [&](int t) { return __builtin_amdgcn_readfirstlane(a.col_idx[r0 + t]); };
   auto copy_tile = [&](int t) {
     const int kb = column(t);
@@ -263,10 +325,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
   char* const lb0 = smem + 4 * T::kBytes;          // lse, buffers 0 and 1
   char* const db0 = smem + 4 * T::kBytes + 2048;   // D, buffers 0 and 1
 
-  const int nb = a.nb, n = a.n;
-  const int bh = blockIdx.x / nb, kb = blockIdx.x - bh * nb;
-  const int b = bh / a.heads, h = bh - b * a.heads;
-  const int64_t base = b * a.stride_b + h * a.stride_h;
+  const BwdGeometry geo = bwd_geometry(a, blockIdx.x);
+  const int nb = geo.nb, n = geo.n, kb = geo.blk;
+  const int64_t base = geo.base;
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
   const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row_bytes = a.stride_s * 2;
@@ -274,8 +335,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
   const int krow = k0 + 32 * wi + lq;
   const char* const qh = reinterpret_cast<const char*>(a.q + base);
   const char* const gh = reinterpret_cast<const char*>(a.g + base);
-  const float* const lse_bh = a.lse + static_cast<int64_t>(bh) * n;
-  const float* const dl_bh = a.delta + static_cast<int64_t>(bh) * n;
+  const float* const lse_bh = geo.lse;
+  const float* const dl_bh = geo.delta;
 
   int copy_off[T::kOffsetPeriod];
   copy_offsets<D>(wi, lane, row_bytes, copy_off);
@@ -283,8 +344,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
   row_read_offsets<D>(lane, rbase, rx);
   tr_read_offsets<D>(lane, tb0, tx0, tb1, tx1);
 
-  const int c0 = a.col_ptr[kb];
-  const int L = a.col_ptr[kb + 1] - c0;
+  const int c0 = geo.col_ptr[kb];
+  const int L = geo.col_ptr[kb + 1] - c0;
   auto qblock = [&](int t) { return __builtin_amdgcn_readfirstlane(a.row_idx[c0 + t]); };
   auto copy_tile = [&](int t) {
     const int qb = qblock(t);
@@ -405,6 +466,24 @@ void launch_bwd(const BwdArgs& args, int rows_total, int items, hipStream_t st) 
   hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, E>), dim3(items), dim3(kBwdThreads), 0, st, args);
 }
 
+// The three kernels of one call, at the template instance of head_dim and the element
+// mode (none, 1-D distance, grid distance).
+int32_t launch_all(const BwdArgs& args, int rows_total, int items, int head_dim,
+                   int32_t element_tokens_per_frame, int32_t element_grid_w, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int mode = element_tokens_per_frame == 0 ? 0 : (element_grid_w == 0 ? 1 : 2);
+  if (head_dim == 128) {
+    if (mode == 2) launch_bwd<128, 2>(args, rows_total, items, st);
+    else if (mode == 1) launch_bwd<128, 1>(args, rows_total, items, st);
+    else launch_bwd<128, 0>(args, rows_total, items, st);
+  } else {
+    if (mode == 2) launch_bwd<64, 2>(args, rows_total, items, st);
+    else if (mode == 1) launch_bwd<64, 1>(args, rows_total, items, st);
+    else launch_bwd<64, 0>(args, rows_total, items, st);
+  }
+  return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -463,17 +542,79 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
   args.elem_w0 = element_w0;
   args.c = scale * kLog2e;
   args.scale = scale;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int mode = element_tokens_per_frame == 0 ? 0 : (element_grid_w == 0 ? 1 : 2);
-  const int it = static_cast<int>(items), rt = static_cast<int>(rows_total);
-  if (head_dim == 128) {
-    if (mode == 2) launch_bwd<128, 2>(args, rt, it, st);
-    else if (mode == 1) launch_bwd<128, 1>(args, rt, it, st);
-    else launch_bwd<128, 0>(args, rt, it, st);
-  } else {
-    if (mode == 2) launch_bwd<64, 2>(args, rt, it, st);
-    else if (mode == 1) launch_bwd<64, 1>(args, rt, it, st);
-    else launch_bwd<64, 0>(args, rt, it, st);
+  args.varlen = 0;
+  return launch_all(args, static_cast<int>(rows_total), static_cast<int>(items), head_dim,
+                    element_tokens_per_frame, element_grid_w, stream);
+}
+
+extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v,
+                                          const void* o, const void* dout, const float* lse,
+                                          void* dq, void* dk, void* dv, float* delta,
+                                          const int32_t* seq_tokens, int32_t batch,
+                                          const int32_t* row_ptr, const int32_t* col_idx,
+                                          const int32_t* col_ptr, const int32_t* row_idx,
+                                          float scale, int32_t element_tokens_per_frame,
+                                          int32_t element_w0, int32_t element_grid_w,
+                                          int32_t heads, int32_t head_dim, int64_t stride_h,
+                                          int64_t stride_s, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta || !row_ptr ||
+      !col_idx || !col_ptr || !row_idx || !seq_tokens)
+    return RADIAL_ERR_INVALID_ARG;
+  if (batch <= 0 || heads <= 0) return RADIAL_ERR_INVALID_ARG;
+  if (batch > kMaxBwdVarlen) return RADIAL_ERR_TOO_LARGE;
+  if (!std::isfinite(scale) || scale < 0.f) return RADIAL_ERR_INVALID_ARG;
+  if (!element_args_valid(element_tokens_per_frame, element_w0, element_grid_w))
+    return RADIAL_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return RADIAL_ERR_UNSUPPORTED_HEAD_DIM;
+  if (stride_s < head_dim || stride_h < 0) return RADIAL_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return RADIAL_ERR_MISALIGNED;
+  if (!aligned(lse, 4) || !aligned(delta, 4)) return RADIAL_ERR_MISALIGNED;
+  if ((stride_s | stride_h) & 7) return RADIAL_ERR_MISALIGNED;
+  if (stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
+
+  BwdArgs args;
+  args.q = static_cast<const __bf16*>(q);
+  args.k = static_cast<const __bf16*>(k);
+  args.v = static_cast<const __bf16*>(v);
+  args.o = static_cast<const __bf16*>(o);
+  args.g = static_cast<const __bf16*>(dout);
+  args.lse = lse;
+  args.dq = static_cast<__bf16*>(dq);
+  args.dk = static_cast<__bf16*>(dk);
+  args.dv = static_cast<__bf16*>(dv);
+  args.delta = delta;
+  args.row_ptr = row_ptr;
+  args.col_idx = col_idx;
+  args.col_ptr = col_ptr;
+  args.row_idx = row_idx;
+  args.stride_b = 0;
+  args.stride_h = stride_h;
+  args.heads = heads;
+  args.stride_s = static_cast<int>(stride_s);
+  args.elem_s = element_tokens_per_frame;
+  args.elem_gw = element_grid_w;
+  args.elem_w0 = element_w0;
+  args.c = scale * kLog2e;
+  args.scale = scale;
+  args.varlen = batch;
+  int64_t tok = 0, rows = 0, wgs = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = seq_tokens[b];
+    if (n <= 0) return RADIAL_ERR_INVALID_ARG;
+    const int32_t nb = (n + kBlock - 1) / kBlock;
+    if (tok > INT32_MAX || rows > INT32_MAX || wgs > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+    args.plan[b] = BwdSample{static_cast<int>(tok), n, nb, static_cast<int>(rows),
+                             static_cast<int>(wgs), 0, 0, 0};
+    tok += n;
+    rows += nb + 1;
+    wgs += static_cast<int64_t>(heads) * nb;
   }
-  return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
+  if (tok > INT32_MAX || wgs > INT32_MAX || static_cast<int64_t>(heads) * tok > INT32_MAX)
+    return RADIAL_ERR_TOO_LARGE;
+  args.n = static_cast<int>(tok);  // the packed sequence; lse and delta are [heads, n]
+  args.nb = 0;                     // per sample, from the plan
+  return launch_all(args, static_cast<int>(heads * tok), static_cast<int>(wgs), head_dim,
+                    element_tokens_per_frame, element_grid_w, stream);
 }

@@ -331,6 +331,38 @@ int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
                         int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream);
 
+/*
+ * radial_attn_bwd_varlen — radial_attn_bwd over a packed varlen batch (the backward of
+ * radial_attn_fwd_varlen). The call is asynchronous on `stream`.
+ *
+ * q, k, v, o, dout, dq, dk, dv: device bf16 [total_tokens, heads, head_dim] with element
+ *             strides stride_s between tokens and stride_h between heads, shared by all
+ *             eight, head_dim contiguous; sample b holds the next seq_tokens[b] tokens.
+ * lse:        the forward's fp32 [heads, total_tokens] output (contiguous).
+ * delta:      caller-owned fp32 workspace of heads * total_tokens.
+ * seq_tokens: host array of batch lengths (each >= 1); 1 <= batch <= 64.
+ * row_ptr, col_idx, col_ptr, row_idx: the samples' block masks and their transposes
+ *             (device), each concatenated as radial_attn_fwd_varlen takes row_ptr and
+ *             col_idx: sample b's nb_b + 1 pointer entries follow those of the samples
+ *             before it and index the concatenated index array; indices count blocks
+ *             within the sample.
+ * scale, element arguments: as passed to the forward.
+ * Each sample's gradients equal radial_attn_bwd's on that sample alone (the same kernels
+ * on the same tiles).
+ *
+ * Errors: INVALID_ARG (null pointer, batch <= 0, a length <= 0, heads <= 0, bad scale or
+ * element arguments, stride_s < head_dim), UNSUPPORTED_HEAD_DIM, MISALIGNED, TOO_LARGE
+ * (batch above 64, totals past int32), HIP.
+ */
+int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, void* dq, void* dk,
+                               void* dv, float* delta, const int32_t* seq_tokens,
+                               int32_t batch, const int32_t* row_ptr, const int32_t* col_idx,
+                               const int32_t* col_ptr, const int32_t* row_idx, float scale,
+                               int32_t element_tokens_per_frame, int32_t element_w0,
+                               int32_t element_grid_w, int32_t heads, int32_t head_dim,
+                               int64_t stride_h, int64_t stride_s, void* stream);
+
 /* radial_error_string — a static, human-readable text for a return code. */
 const char* radial_error_string(int32_t code);
 

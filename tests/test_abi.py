@@ -29,6 +29,7 @@ def test_header_declares_the_boundary():
         ["radial_mask_dims", "radial_build_mask", "radial_mask_dims_grid",
          "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd", "radial_attn_fwd_rule",
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
+         "radial_attn_bwd_varlen",
          "radial_error_string"])
 
 
@@ -289,3 +290,36 @@ def rule(**kw):
 ])
 def test_attn_fwd_rule_validation(kw, code):
     assert rule(**kw) == code
+
+
+def bwd_varlen(**kw):
+    """Call radial_attn_bwd_varlen with valid-looking defaults, overridden by kw."""
+    import ctypes
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, do=0x50000, lse=0x60000,
+             dq=0x70000, dk=0x80000, dv=0x90000, delta=0xa0000, seq=[1000, 300], batch=2,
+             row_ptr=0xb0000, col_idx=0xc0000, col_ptr=0xd0000, row_idx=0xe0000,
+             scale=0.125, elem_s=0, elem_w0=0, elem_gw=0, heads=2, head_dim=128,
+             stride_h=128, stride_s=256, stream=None)
+    a.update(kw)
+    seq = None if a["seq"] is None else (ctypes.c_int32 * len(a["seq"]))(*a["seq"])
+    return radial.lib().radial_attn_bwd_varlen(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+        a["delta"], seq, a["batch"], a["row_ptr"], a["col_idx"], a["col_ptr"], a["row_idx"],
+        a["scale"], a["elem_s"], a["elem_w0"], a["elem_gw"], a["heads"], a["head_dim"],
+        a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    *[(dict(**{name: None}), INVALID) for name in (
+        "q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "delta", "seq", "row_ptr",
+        "col_idx", "col_ptr", "row_idx")],
+    (dict(batch=0), INVALID), (dict(seq=[1000, 0]), INVALID), (dict(heads=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(stride_s=64), INVALID),
+    (dict(elem_s=64, elem_w0=5), INVALID), (dict(elem_s=300, elem_w0=5, elem_gw=7), INVALID),
+    (dict(head_dim=80), HEADDIM), (dict(dk=0x80004), MISALIGNED),
+    (dict(delta=0xa0002), MISALIGNED), (dict(stride_h=132), MISALIGNED),
+    (dict(seq=[100] * 65, batch=65), TOO_LARGE),
+])
+def test_attn_bwd_varlen_validation(kw, code):
+    # Every case here fails a host check: none may reach a launch (the pointers are fake).
+    assert bwd_varlen(**kw) == code

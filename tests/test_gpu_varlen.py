@@ -111,3 +111,60 @@ def test_varlen_rejects_a_sixty_fifth_sample():
     q, k, v = packed_inputs(65 * 128, 1, 64, seed=65)
     with pytest.raises(radial.RadialError):
         radial.attn_fwd_varlen(q, k, v, vm)
+
+
+BWD_CASES = [
+    # frames, S, W0, grid_w, H, D, element
+    ([7, 3, 11], 300, 40, None, 2, 128, False),
+    ([5, 2, 9], 300, 40, None, 2, 64, True),
+    ([4, 6], 200, 9, 8, 1, 128, True),
+]
+
+
+@pytest.mark.parametrize("frames,S,w0,gw,H,D,element", BWD_CASES)
+def test_varlen_backward_equals_per_sample(frames, S, w0, gw, H, D, element):
+    masks = [radial.build_mask(f, S, w0, grid_w=gw) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = packed_inputs(total, H, D, seed=31 + D)
+    g = torch.Generator(device="cuda").manual_seed(32)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    lse = torch.empty(H, total, dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd_varlen(q, k, v, vm, lse=lse, element=element)
+    grads = radial.attn_bwd_varlen(q, k, v, o, do, lse, vm, element=element)
+    torch.cuda.synchronize()
+    t0 = 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        view = lambda x: x[sl].permute(1, 0, 2).unsqueeze(0)  # noqa: E731
+        md = m.to("cuda")
+        ls = torch.empty(1, H, m.n, dtype=torch.float32, device="cuda")
+        os_ = radial.attn_fwd(view(q), view(k), view(v), md, lse=ls, element=element)
+        ref = radial.attn_bwd(view(q), view(k), view(v), os_, view(do), ls, md,
+                              element=element)
+        torch.cuda.synchronize()
+        for got, r in zip(grads, ref):
+            assert torch.equal(view(got), r)
+        t0 += m.n
+
+
+def test_varlen_backward_against_oracle():
+    frames, S, w0, H, D = [4, 2], 500, 60, 2, 128
+    masks = [radial.build_mask(f, S, w0) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = (x.requires_grad_() for x in packed_inputs(total, H, D, seed=33))
+    g = torch.Generator(device="cuda").manual_seed(34)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    radial.attention_varlen(q, k, v, vm).backward(do)
+    torch.cuda.synchronize()
+    t0 = 0
+    for m in masks:
+        sl = slice(t0, t0 + m.n)
+        f64 = lambda x: x.detach()[sl].permute(1, 0, 2).to("cpu", torch.float64).numpy()  # noqa: E731
+        ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), m.row_ptr.numpy(),
+                                    m.col_idx.numpy(), D ** -0.5)
+        for got, r in zip((q.grad, k.grad, v.grad), ref):
+            err = np.abs(f64(got) - r)
+            assert err.max() <= 2e-2 * np.abs(r).max() and err.mean() <= 5e-3 * np.abs(r).mean()
+        t0 += m.n
