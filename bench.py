@@ -17,7 +17,8 @@ times the backward pass (dq, dk, dv from the forward's o and lse, and a seeded d
 counting 2.5 times the forward's work (the usual five products against two), and its
 dense baseline and CPU oracle likewise. --varlen F1,F2,... times one packed launch over
 videos of those frame counts (the workload's frame length, W0, heads and head_dim),
-beside the same samples run as separate launches one after another. --rule times the
+beside the same samples run as separate launches one after another (with --backward,
+the backward pass likewise). --rule times the
 forward with the block mask derived in the kernel from the rule instead of read from the
 CSR (the same key blocks, so the same work is counted).
 
@@ -163,20 +164,39 @@ def bench_varlen(args, wl, dev):
     log(f"varlen {wl.name} frames {frames}: {total} tokens, {nnz} active blocks, "
         f"mask build {mask_ms:.2f} ms")
 
-    run = lambda: radial.attn_fwd_varlen(q, k, v, vdev, out=o, element=args.element)  # noqa: E731
+    work = 2.5 if args.backward else 1.0
+    flops = int(flops * work)
+    el = args.element
+    if args.backward:
+        gen = torch.Generator(device=dev).manual_seed(1)
+        do = torch.randn(q.shape, generator=gen, device=dev).to(torch.bfloat16)
+        lse = torch.empty(wl.heads, total, dtype=torch.float32, device=dev)
+        radial.attn_fwd_varlen(q, k, v, vdev, out=o, lse=lse, element=el)
+        run = lambda: radial.attn_bwd_varlen(q, k, v, o, do, lse, vdev, element=el)  # noqa: E731
+    else:
+        run = lambda: radial.attn_fwd_varlen(q, k, v, vdev, out=o, element=el)  # noqa: E731
     ms, wall = time_launches(run, args.steps, args.warmup)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"packed: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
+    log(f"packed{' backward' if args.backward else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s "
+        f"({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
 
     views, t0 = [], 0
-    for m in masks:
+    for i, m in enumerate(masks):
         sl = slice(t0, t0 + m.n)
-        views.append(tuple(x[sl].permute(1, 0, 2).unsqueeze(0) for x in (q, k, v, o)))
+        xs = (q, k, v, o) + ((do,) if args.backward else ())
+        views.append(tuple(x[sl].permute(1, 0, 2).unsqueeze(0) for x in xs))
+        if args.backward:  # this sample's own lse, as its own forward writes it
+            views[-1] += (lse[:, sl].unsqueeze(0).contiguous(),)
         t0 += m.n
 
     def separate():
-        for (qs, ks, vs, os_), md in zip(views, mdevs):
-            radial.attn_fwd(qs, ks, vs, md, out=os_, element=args.element)
+        for vw, md in zip(views, mdevs):
+            if args.backward:
+                qs, ks, vs, os_, dos, ls = vw
+                radial.attn_bwd(qs, ks, vs, os_, dos, ls, md, element=el)
+            else:
+                qs, ks, vs, os_ = vw
+                radial.attn_fwd(qs, ks, vs, md, out=os_, element=el)
     sms, _ = time_launches(separate, args.steps, args.warmup)
     log(f"separate launches: {sms:.3f} ms/step ({flops / (sms * 1e-3) / 1e12:.1f} TFLOP/s)")
 
@@ -185,8 +205,9 @@ def bench_varlen(args, wl, dev):
         # The oracle on the first sample alone (its own [1, H, n, D] views).
         swl = Workload(f"{wl.name}-sample0", 1, wl.heads, wl.head_dim, frames[0],
                        wl.tokens_per_frame, wl.w0, wl.sigma, grid_w=wl.grid_w)
-        qs, ks, vs, _ = views[0]
-        cpu = cpu_baseline(swl, qs, ks, vs, masks[0], args.cpu_seconds, args.element)
+        qs, ks, vs = views[0][:3]
+        dos = views[0][4] if args.backward else None
+        cpu = cpu_baseline(swl, qs, ks, vs, masks[0], args.cpu_seconds, args.element, dos)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
     line = result_line(args, tflops, ms, wall, {
@@ -194,7 +215,8 @@ def bench_varlen(args, wl, dev):
         "head_dim": wl.head_dim, "frames": frames, "tokens_per_frame": wl.tokens_per_frame,
         "seq_len": total, "w0": wl.w0, "grid_w": wl.grid_w, "block": 128, "active_blocks": nnz,
         "total_blocks": sum(m.nb ** 2 for m in masks),
-        "semantics": "element" if args.element else "block", "pass": "forward"},
+        "semantics": "element" if args.element else "block",
+        "pass": "backward" if args.backward else "forward"},
         traffic=None, cpu=cpu)
     line["separate_launches_ms"] = round(sms, 4)
     line["speedup_vs_separate"] = round(sms / ms, 3)
