@@ -148,3 +148,49 @@ def test_row_absent_from_table_is_not_written():
     keep = torch.ones(out.shape[2], dtype=torch.bool)
     keep[rows7] = False
     assert torch.equal(out[:, :, keep], ref[:, :, keep])
+
+
+def test_graph_capture_of_varlen_rule_and_backward():
+    """The varlen forward, the on-the-fly mask and the backward pass, captured in one graph,
+    replay bit-identically, with eager calls of the same entry points in between."""
+    from block_sparse_attention_radial_amd.inputs import draw_packed_qkv
+    masks = [radial.build_mask(f, 300, 40) for f in (5, 2, 7)]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    pq, pk, pv = draw_packed_qkv(total, 2, 128, seed=41, device="cuda")
+    q, k, v, mask = problem(6)
+    rm = radial.rule_mask(mask.frames, mask.tokens_per_frame, mask.w0, pairs=True).to("cuda")
+    g = torch.Generator(device="cuda").manual_seed(42)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def work(outs):
+        radial.attn_fwd_varlen(pq, pk, pv, vm, out=outs[0])
+        radial.attn_fwd(q, k, v, rm, out=outs[1], lse=lse)
+        grads = radial.attn_bwd(q, k, v, outs[1], do, lse, mask)
+        for dst, src in zip(outs[2:], grads):
+            dst.copy_(src)
+
+    refs = [torch.empty_like(pq), torch.empty_like(q)] + [torch.empty_like(q) for _ in range(3)]
+    work(refs)
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(r) for r in refs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work(outs)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work(outs)
+    eager = [torch.empty_like(r) for r in refs]
+    for r in range(4):
+        for o in outs:
+            o.zero_()
+        graph.replay()
+        work(eager)
+        torch.cuda.synchronize()
+        for a, b, c in zip(outs, refs, eager):
+            assert torch.equal(a, b), r
+            assert torch.equal(c, b), r
