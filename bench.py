@@ -302,6 +302,10 @@ def main():
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if args.varlen:
+        if args.rule:
+            print("--rule and --varlen do not combine: the on-the-fly mask is for a uniform "
+                  "batch", file=sys.stderr)
+            sys.exit(2)
         bench_varlen(args, wl, dev)
         return
 
