@@ -1,6 +1,6 @@
 """bench.py's command-line contract, checked without a GPU.
 
-More than one GPU is refused with a message (this build measures one GPU); a run on a
+More than one GPU is refused with a message (the benchmark measures one GPU); a run on a
 host without a GPU exits with an error instead of printing a result line; the traffic
 record is keyed to the kernel sources.
 """
