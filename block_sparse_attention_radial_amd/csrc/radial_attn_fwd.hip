@@ -287,6 +287,9 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
   w.l_run += lt;
 }
 
+// Most marking steps per row that radial_attn_fwd_rule accepts.
+constexpr int64_t kMaxRuleSteps = 1 << 16;
+
 // Union-list entry bits.
 constexpr uint32_t kInA = 1u << 14, kInB = 1u << 15, kKbMask = kInA - 1;
 
@@ -912,6 +915,11 @@ extern "C" int32_t radial_attn_fwd_rule(const void* q, const void* k, const void
   if (grid_w > 0 && tokens_per_frame % grid_w != 0) return RADIAL_ERR_INVALID_ARG;
   const int64_t n = static_cast<int64_t>(frames) * tokens_per_frame;
   if (n > static_cast<int64_t>(kMaxBlocks) * kBlock) return RADIAL_ERR_TOO_LARGE;
+  // A workgroup marks a row in (query frame pieces) x frames x grid rows steps; bound it
+  // (realistic videos need a few thousand) so that no shape makes the marking crawl.
+  const int64_t pieces = std::min<int64_t>(frames, (kBlock - 1) / tokens_per_frame + 2);
+  const int64_t rows = grid_w > 0 ? tokens_per_frame / grid_w : 1;
+  if (pieces * frames * rows > kMaxRuleSteps) return RADIAL_ERR_TOO_LARGE;
   const int32_t seqlen = static_cast<int32_t>(n);
   const int32_t err = check_common(q, k, v, o, heads, scale,
                                    element ? tokens_per_frame : 0, w0, grid_w, head_dim);

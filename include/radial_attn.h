@@ -236,8 +236,9 @@ int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
  * Errors: INVALID_ARG (frames, tokens_per_frame or w0 <= 0, a grid width that is
  * negative or does not divide tokens_per_frame, element masking with a frame outside
  * 128 .. 2^22, and radial_attn_fwd's other argument errors), UNSUPPORTED_HEAD_DIM,
- * MISALIGNED, TOO_LARGE (a sequence above 16352 * 128 tokens, work items past int32),
- * HIP.
+ * MISALIGNED, TOO_LARGE (a sequence above 16352 * 128 tokens, work items past int32, or
+ * more than 2^16 marking steps per row: (frame pieces of a 128-token block) x frames x
+ * grid rows, a few thousand for real videos), HIP.
  */
 int32_t radial_attn_fwd_rule(const void* q, const void* k, const void* v, void* o, float* lse,
                              int32_t frames, int32_t tokens_per_frame, int32_t grid_w,

@@ -286,6 +286,8 @@ def rule(**kw):
     (dict(element=1, s=100, frames=10), INVALID),            # element: frame below 128
     (dict(pairs=0x70000, npairs=3), INVALID), (dict(pairs=0x70000, npairs=9), INVALID),
     (dict(frames=16353, s=128), TOO_LARGE),                  # past 16352 blocks
+    (dict(frames=300000, s=1), TOO_LARGE),                   # 2 x 300000 marking steps a row
+    (dict(frames=100, s=2000, gw=2), TOO_LARGE),             # 2 x 100 x 1000 steps a row
     (dict(frames=1 << 16, s=1 << 16), TOO_LARGE),
 ])
 def test_attn_fwd_rule_validation(kw, code):
