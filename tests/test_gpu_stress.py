@@ -121,3 +121,36 @@ def test_batched_strided_layout_wan_frames():
     rows = np.concatenate([np.arange(b * 128, min(n, b * 128 + 128)) for b in blocks])
     err = np.abs(f64(o)[..., rows, :] - ref[..., rows, :])
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("element,rule", [(False, False), (True, False), (False, True)],
+                         ids=["block", "element", "on-the-fly"])
+def test_maximum_sequence_length(element, rule):
+    """16352 blocks, the kernel's limit (2,093,056 tokens), as one frame with W0 = 100: a
+    sliding window |i - j| < 100 that depends only on i - j. A query block's keys then lie
+    in its own block and its neighbours, so its output equals that of block 1 (or block 0
+    or 2 at the ends) of the same rule on the 384 tokens around it, which the oracle
+    computes."""
+    nb = 16352
+    n, w0, D = nb * 128, 100, 64
+    g = torch.Generator(device="cuda").manual_seed(77)
+    q, k, v = (torch.randn(1, 1, n, D, generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    mask = (radial.rule_mask(1, n, w0) if rule else radial.build_mask(1, n, w0)).to("cuda")
+    lse = torch.empty(1, 1, n, dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(q, k, v, mask, lse=lse, element=element)
+    torch.cuda.synchronize()
+    lrp, lci = ro.csr(ro.block_mask(1, 384, w0))
+    for qb in (0, 1, 8000, nb - 2, nb - 1):
+        b0 = min(max(qb - 1, 0), nb - 3)  # first global block of the local window
+        sl = slice(b0 * 128, b0 * 128 + 384)
+        local = qb - b0
+        ref, ref_lse = ro.attention(
+            *(x[0, 0, sl].to("cpu", torch.float64).numpy() for x in (q, k, v)), lrp, lci,
+            D ** -0.5, query_blocks=[local], element=(384, w0) if element else None)
+        rows = slice(local * 128, local * 128 + 128)
+        got = o[0, 0, qb * 128:qb * 128 + 128].to("cpu", torch.float64).numpy()
+        err = np.abs(got - ref[rows])
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (qb, err.max(), err.mean())
+        got_lse = lse[0, 0, qb * 128:qb * 128 + 128].to("cpu", torch.float64).numpy()
+        assert np.abs(got_lse - ref_lse[rows]).max() < 1e-3, qb
