@@ -14,13 +14,14 @@ The mask builder and the kernels live in libradial.so (C ABI: include/radial_att
 built in-tree by `python -m block_sparse_attention_radial_amd.build`.
 """
 from .api import (BLOCK, Mask, RadialAttentionFunction, RadialAttentionVarlenFunction,
-                  RadialError, RuleMask, VarlenMask, attention, attention_varlen, attn_bwd,
+                  RadialError, RuleMask, VarlenMask, VarlenRuleMask, attention, attention_varlen,
+                  attn_bwd,
                   attn_bwd_varlen, attn_fwd, attn_fwd_varlen, build_mask, build_pairs,
                   build_varlen_mask, concat_masks, dense_mask, error_string, lib, mask_dims,
                   rule_mask)
 
 __all__ = ["BLOCK", "Mask", "RadialAttentionFunction", "RadialAttentionVarlenFunction",
-           "RadialError", "RuleMask", "VarlenMask", "attention", "attention_varlen", "attn_bwd",
+           "RadialError", "RuleMask", "VarlenMask", "VarlenRuleMask", "attention", "attention_varlen", "attn_bwd",
            "attn_bwd_varlen", "attn_fwd", "attn_fwd_varlen", "build_mask", "build_pairs",
            "build_varlen_mask", "concat_masks", "dense_mask", "error_string", "lib",
            "mask_dims", "rule_mask"]

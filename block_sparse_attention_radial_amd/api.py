@@ -41,6 +41,9 @@ _SIGNATURES = {
     "radial_attn_fwd_rule": (ctypes.c_int32, [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 5 + [
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 3
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_attn_fwd_varlen_rule": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32] * 5
+        + [ctypes.c_void_p] * 2 + [ctypes.c_float] + [ctypes.c_int32] * 2
+        + [ctypes.c_int64] * 2 + [ctypes.c_void_p]),
     "radial_attn_fwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32] + [
         ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 5 + [ctypes.c_int64] * 2
         + [ctypes.c_void_p]),
@@ -468,7 +471,44 @@ def build_varlen_mask(frames: list, tokens_per_frame: int, w0: int, pairs: bool 
                          for f in frames])
 
 
-def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: VarlenMask,
+@dataclass
+class VarlenRuleMask:
+    """The masks of a varlen batch given by their rule alone (no CSR): sample b is a
+    video of frames[b] frames; the kernel derives each row's key blocks on the fly
+    (radial_attn_fwd_varlen_rule). `pairs` / `npairs` (optional) as in VarlenMask."""
+
+    frames: list
+    tokens_per_frame: int
+    w0: int
+    grid_w: int = 0
+    pairs: torch.Tensor | None = None
+    npairs: list | None = None
+    _built: "VarlenMask | None" = field(default=None, repr=False, compare=False)
+
+    @property
+    def seq_tokens(self) -> list:
+        return [f * self.tokens_per_frame for f in self.frames]
+
+    def built(self, device="cpu") -> "VarlenMask":
+        """The concatenated CSRs this rule gives (built on the host once, cached), on
+        `device`: what the backward pass walks."""
+        if self._built is None:
+            self._built = build_varlen_mask(self.frames, self.tokens_per_frame, self.w0,
+                                            pairs=False, grid_w=self.grid_w or None)
+        return self._built.to(device)
+
+    @property
+    def batch(self) -> int:
+        return len(self.frames)
+
+    def to(self, device) -> "VarlenRuleMask":
+        return VarlenRuleMask(list(self.frames), self.tokens_per_frame, self.w0, self.grid_w,
+                              None if self.pairs is None else self.pairs.to(device),
+                              None if self.npairs is None else list(self.npairs), self._built)
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    mask: "VarlenMask | VarlenRuleMask",
                     scale: float | None = None, out: torch.Tensor | None = None,
                     lse: torch.Tensor | None = None, element: bool = False) -> torch.Tensor:
     """Radial attention forward on a packed batch: q, k, v of shape [total_tokens, H, D]
@@ -485,7 +525,8 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Var
     total, H, D = q.shape
     if sum(mask.seq_tokens) != total:
         raise ValueError("the samples' lengths must add up to q's token count")
-    if mask.row_ptr.device != q.device or mask.col_idx.device != q.device or (
+    rule = isinstance(mask, VarlenRuleMask)
+    if (not rule and (mask.row_ptr.device != q.device or mask.col_idx.device != q.device)) or (
             mask.pairs is not None and mask.pairs.device != q.device):
         raise ValueError("the mask must be on the same device as q (VarlenMask.to(device))")
     if out is None:
@@ -498,9 +539,18 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Var
     if scale is None:
         scale = D ** -0.5
     elem_s, elem_w0, elem_gw = _element_args(mask, element)
-    seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
     npr = None if mask.npairs is None else (ctypes.c_int32 * mask.batch)(*mask.npairs)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if rule:
+        frames = (ctypes.c_int32 * mask.batch)(*mask.frames)
+        _check("radial_attn_fwd_varlen_rule", lib().radial_attn_fwd_varlen_rule(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), frames, mask.batch,
+            mask.tokens_per_frame, mask.grid_w, mask.w0, int(bool(element)),
+            None if mask.pairs is None else mask.pairs.data_ptr(), npr, float(scale), H, D,
+            q.stride(1), q.stride(0), stream))
+        return out
+    seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
     _check("radial_attn_fwd_varlen", lib().radial_attn_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         None if lse is None else lse.data_ptr(), seq, mask.batch, mask.row_ptr.data_ptr(),
@@ -524,6 +574,8 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     if any(t.stride() != q.stride() for t in (k, v, o, do)) or q.stride(-1) != 1:
         raise ValueError("q, k, v, o, do must share strides with a contiguous last axis")
     total, H, D = q.shape
+    if isinstance(mask, VarlenRuleMask):
+        mask = mask.built(q.device)
     if sum(mask.seq_tokens) != total:
         raise ValueError("the samples' lengths must add up to q's token count")
     if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():

@@ -868,6 +868,35 @@ int32_t check_common(const void* q, const void* k, const void* v, const void* o,
   return RADIAL_OK;
 }
 
+// The per-sample plan and launch of a varlen batch: tokens[b] is sample b's length. With
+// a mask rule (args.rule.s > 0) there is no CSR: each sample's row offset is 0, so
+// nothing is added to the null row_ptr.
+int32_t launch_varlen(FwdArgs& args, const int32_t* tokens, int32_t batch,
+                      const int32_t* pairs, const int32_t* npairs, int32_t heads,
+                      int32_t head_dim, void* stream) {
+  const bool rule = args.rule.s > 0;
+  int64_t tok = 0, rows = 0, prs = 0, items = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t n = tokens[b];
+    if (n <= 0) return RADIAL_ERR_INVALID_ARG;
+    const int32_t nb = (n + kBlock - 1) / kBlock;
+    if (nb > kMaxBlocks) return RADIAL_ERR_TOO_LARGE;
+    const int32_t np = pairs == nullptr ? (nb + 1) / 2 : npairs[b];
+    if (np < (nb + 1) / 2 || np > nb) return RADIAL_ERR_INVALID_ARG;
+    if (tok > INT32_MAX || rows > INT32_MAX || prs > INT32_MAX || items > INT32_MAX)
+      return RADIAL_ERR_TOO_LARGE;
+    args.plan[b] = VarlenSample{static_cast<int>(tok), n, nb, rule ? 0 : static_cast<int>(rows),
+                                static_cast<int>(prs), np, static_cast<int>(items), 0};
+    tok += n;
+    rows += nb + 1;
+    prs += np;
+    items += static_cast<int64_t>(heads) * np;
+  }
+  if (tok > INT32_MAX || items > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  args.n = static_cast<int>(tok);  // the packed sequence; lse is [heads, n]
+  return launch_fwd(args, items, head_dim, stream);
+}
+
 }  // namespace
 
 extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
@@ -964,24 +993,40 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
                pairs, 0, stride_h, 0, 0, heads, 0, static_cast<int>(stride_s),
                element_tokens_per_frame, element_grid_w, element_w0, MaskRule{0, 0, 0},
                base2_scale(scale), 0, 0, batch, {}};
-  int64_t tok = 0, rows = 0, prs = 0, items = 0;
+  return launch_varlen(args, seq_tokens, batch, pairs, npairs, heads, head_dim, stream);
+}
+
+extern "C" int32_t radial_attn_fwd_varlen_rule(
+    const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* frames,
+    int32_t batch, int32_t tokens_per_frame, int32_t grid_w, int32_t w0, int32_t element,
+    const int32_t* pairs, const int32_t* npairs, float scale, int32_t heads, int32_t head_dim,
+    int64_t stride_h, int64_t stride_s, void* stream) {
+  if (tokens_per_frame <= 0 || w0 <= 0 || grid_w < 0) return RADIAL_ERR_INVALID_ARG;
+  if (grid_w > 0 && tokens_per_frame % grid_w != 0) return RADIAL_ERR_INVALID_ARG;
+  const int32_t err = check_common(q, k, v, o, heads, scale,
+                                   element ? tokens_per_frame : 0, w0, grid_w, head_dim);
+  if (err != RADIAL_OK) return err;
+  if (!frames || batch <= 0 || (pairs != nullptr && npairs == nullptr))
+    return RADIAL_ERR_INVALID_ARG;
+  if (batch > kMaxVarlen) return RADIAL_ERR_TOO_LARGE;
+  if (stride_s < head_dim || stride_h < 0) return RADIAL_ERR_INVALID_ARG;
+  if ((stride_s | stride_h) & 7) return RADIAL_ERR_MISALIGNED;
+  if (stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
+  int32_t tokens[kMaxVarlen];
+  const int64_t rows = grid_w > 0 ? tokens_per_frame / grid_w : 1;
   for (int32_t b = 0; b < batch; ++b) {
-    const int32_t n = seq_tokens[b];
-    if (n <= 0) return RADIAL_ERR_INVALID_ARG;
-    const int32_t nb = (n + kBlock - 1) / kBlock;
-    if (nb > kMaxBlocks) return RADIAL_ERR_TOO_LARGE;
-    const int32_t np = pairs == nullptr ? (nb + 1) / 2 : npairs[b];
-    if (np < (nb + 1) / 2 || np > nb) return RADIAL_ERR_INVALID_ARG;
-    if (tok > INT32_MAX || rows > INT32_MAX || prs > INT32_MAX || items > INT32_MAX)
-      return RADIAL_ERR_TOO_LARGE;
-    args.plan[b] = VarlenSample{static_cast<int>(tok), n, nb, static_cast<int>(rows),
-                                static_cast<int>(prs), np, static_cast<int>(items), 0};
-    tok += n;
-    rows += nb + 1;
-    prs += np;
-    items += static_cast<int64_t>(heads) * np;
+    if (frames[b] <= 0) return RADIAL_ERR_INVALID_ARG;
+    const int64_t n = static_cast<int64_t>(frames[b]) * tokens_per_frame;
+    if (n > static_cast<int64_t>(kMaxBlocks) * kBlock) return RADIAL_ERR_TOO_LARGE;
+    const int64_t pieces = std::min<int64_t>(frames[b], (kBlock - 1) / tokens_per_frame + 2);
+    if (pieces * frames[b] * rows > kMaxRuleSteps) return RADIAL_ERR_TOO_LARGE;
+    tokens[b] = static_cast<int32_t>(n);
   }
-  if (tok > INT32_MAX || items > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
-  args.n = static_cast<int>(tok);  // the packed sequence; lse is [heads, n]
-  return launch_fwd(args, items, head_dim, stream);
+  FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+               static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, nullptr, nullptr,
+               pairs, 0, stride_h, 0, 0, heads, 0, static_cast<int>(stride_s),
+               element ? tokens_per_frame : 0, grid_w, w0,
+               MaskRule{tokens_per_frame, grid_w > 0 ? grid_w : tokens_per_frame, w0},
+               base2_scale(scale), 0, 0, batch, {}};
+  return launch_varlen(args, tokens, batch, pairs, npairs, heads, head_dim, stream);
 }

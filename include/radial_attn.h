@@ -283,6 +283,29 @@ int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void
                                int64_t stride_s, void* stream);
 
 /*
+ * radial_attn_fwd_varlen_rule — radial_attn_fwd_varlen with each sample's block mask
+ * derived on the fly in the kernel (as radial_attn_fwd_rule does) instead of read from a
+ * CSR. The call is asynchronous on `stream`.
+ *
+ * frames:     host array of batch frame counts (each >= 1); sample b holds
+ *             frames[b] * tokens_per_frame tokens; 1 <= batch <= 64.
+ * tokens_per_frame, grid_w, w0, element: the rule, as for radial_attn_fwd_rule.
+ * pairs, npairs: optional pair tables as for radial_attn_fwd_varlen.
+ * Other arguments as radial_attn_fwd_varlen. Output and lse equal radial_attn_fwd_varlen's
+ * on the samples' built masks bit for bit.
+ *
+ * Errors: as radial_attn_fwd_varlen and radial_attn_fwd_rule (a frame count <= 0 is
+ * INVALID_ARG; a sample past 16352 blocks or 2^16 marking steps per row is TOO_LARGE).
+ */
+int32_t radial_attn_fwd_varlen_rule(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int32_t* frames, int32_t batch,
+                                    int32_t tokens_per_frame, int32_t grid_w, int32_t w0,
+                                    int32_t element, const int32_t* pairs,
+                                    const int32_t* npairs, float scale, int32_t heads,
+                                    int32_t head_dim, int64_t stride_h, int64_t stride_s,
+                                    void* stream);
+
+/*
  * radial_transpose_mask — the transposed block mask, for the backward pass: for key
  * block c, the query blocks whose rows list it, in ascending order. Host code.
  *

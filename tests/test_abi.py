@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         ["radial_mask_dims", "radial_build_mask", "radial_mask_dims_grid",
          "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd", "radial_attn_fwd_rule",
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
-         "radial_attn_bwd_varlen",
+         "radial_attn_bwd_varlen", "radial_attn_fwd_varlen_rule",
          "radial_error_string"])
 
 
@@ -325,3 +325,32 @@ def bwd_varlen(**kw):
 def test_attn_bwd_varlen_validation(kw, code):
     # Every case here fails a host check: none may reach a launch (the pointers are fake).
     assert bwd_varlen(**kw) == code
+
+
+def varlen_rule(**kw):
+    """Call radial_attn_fwd_varlen_rule with valid-looking defaults, overridden by kw."""
+    import ctypes
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, frames=[4, 2], batch=2,
+             s=250, gw=0, w0=100, element=0, pairs=None, npairs=None, scale=0.125, heads=2,
+             head_dim=128, stride_h=128, stride_s=256, stream=None)
+    a.update(kw)
+    fr = None if a["frames"] is None else (ctypes.c_int32 * len(a["frames"]))(*a["frames"])
+    npr = None if a["npairs"] is None else (ctypes.c_int32 * len(a["npairs"]))(*a["npairs"])
+    return radial.lib().radial_attn_fwd_varlen_rule(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], fr, a["batch"], a["s"], a["gw"], a["w0"],
+        a["element"], a["pairs"], npr, a["scale"], a["heads"], a["head_dim"], a["stride_h"],
+        a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(frames=None), INVALID), (dict(batch=0), INVALID),
+    (dict(frames=[4, 0]), INVALID), (dict(s=0), INVALID), (dict(w0=0), INVALID),
+    (dict(gw=7), INVALID), (dict(gw=-1), INVALID), (dict(heads=0), INVALID),
+    (dict(element=1, s=100), INVALID), (dict(pairs=0x70000), INVALID),
+    (dict(pairs=0x70000, npairs=[9, 2]), INVALID), (dict(head_dim=80), HEADDIM),
+    (dict(stride_h=132), MISALIGNED), (dict(frames=[1] * 65, batch=65), TOO_LARGE),
+    (dict(frames=[16353, 1], s=128), TOO_LARGE), (dict(frames=[300000, 1], s=1), TOO_LARGE),
+])
+def test_attn_fwd_varlen_rule_validation(kw, code):
+    # Every case here fails a host check: none may reach a launch (the pointers are fake).
+    assert varlen_rule(**kw) == code

@@ -168,3 +168,46 @@ def test_varlen_backward_against_oracle():
             err = np.abs(f64(got) - r)
             assert err.max() <= 2e-2 * np.abs(r).max() and err.mean() <= 5e-3 * np.abs(r).mean()
         t0 += m.n
+
+
+RULE_CASES = [
+    # frames, S, W0, grid_w, H, D, element, pairs
+    ([21, 8, 3], 1560, 1560, None, 2, 128, False, True),
+    ([5, 12, 1, 7], 1000, 300, None, 3, 64, True, False),
+    ([6, 2, 9], 300, 40, 20, 2, 128, True, True),
+    ([3, 40], 100, 37, None, 1, 64, False, False),  # frames shorter than a block
+]
+
+
+@pytest.mark.parametrize("frames,S,w0,gw,H,D,element,pairs", RULE_CASES)
+def test_varlen_rule_equals_varlen_csr(frames, S, w0, gw, H, D, element, pairs):
+    masks = [radial.build_mask(f, S, w0, pairs=pairs, grid_w=gw) for f in frames]
+    vm = radial.concat_masks(masks)
+    rm = radial.VarlenRuleMask(frames, S, w0, gw or 0, vm.pairs, vm.npairs)
+    total = sum(m.n for m in masks)
+    q, k, v = packed_inputs(total, H, D, seed=50 + D)
+    lse1 = torch.empty(H, total, dtype=torch.float32, device="cuda")
+    lse2 = torch.empty_like(lse1)
+    o1 = radial.attn_fwd_varlen(q, k, v, vm.to("cuda"), lse=lse1, element=element)
+    o2 = radial.attn_fwd_varlen(q, k, v, rm.to("cuda"), lse=lse2, element=element)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(lse1, lse2)
+
+
+def test_varlen_rule_autograd_matches_csr():
+    frames, S, w0, H, D = [4, 2, 5], 300, 40, 2, 128
+    vm = radial.build_varlen_mask(frames, S, w0).to("cuda")
+    rm = radial.VarlenRuleMask(frames, S, w0)
+    total = sum(f * S for f in frames)
+    base = packed_inputs(total, H, D, seed=60)
+    g = torch.Generator(device="cuda").manual_seed(61)
+    do = torch.randn(base[0].shape, generator=g, device="cuda").to(torch.bfloat16)
+    grads = []
+    for mask in (vm, rm):
+        q, k, v = (x.clone().requires_grad_() for x in base)
+        radial.attention_varlen(q, k, v, mask).backward(do)
+        grads.append((q.grad, k.grad, v.grad))
+    torch.cuda.synchronize()
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)
