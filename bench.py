@@ -18,9 +18,9 @@ counting 2.5 times the forward's work (the usual five products against two), and
 dense baseline and CPU oracle likewise. --varlen F1,F2,... times one packed launch over
 videos of those frame counts (the workload's frame length, W0, heads and head_dim),
 beside the same samples run as separate launches one after another (with --backward,
-the backward pass likewise). --rule times the
-forward with the block mask derived in the kernel from the rule instead of read from the
-CSR (the same key blocks, so the same work is counted).
+the backward pass likewise). --rule times the forward with the block mask derived in the
+kernel from the rule instead of read from the CSR (the same key blocks, so the same work
+is counted), also for --varlen.
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -155,6 +155,12 @@ def bench_varlen(args, wl, dev):
     vmask = radial.concat_masks(masks)
     mask_ms = (time.perf_counter() - t0) * 1e3
     vdev = vmask.to(dev)
+    if args.rule:  # the same samples, each mask derived in the kernel
+        if args.backward:
+            print("--rule times the forward only", file=sys.stderr)
+            sys.exit(2)
+        vdev = radial.VarlenRuleMask(frames, wl.tokens_per_frame, wl.w0, wl.grid_w or 0,
+                                     vmask.pairs, vmask.npairs).to(dev)
     mdevs = [m.to(dev) for m in masks]
     total = sum(m.n for m in masks)
     q, k, v = draw_packed_qkv(total, wl.heads, wl.head_dim, wl.sigma, seed=0, device=dev)
@@ -216,7 +222,8 @@ def bench_varlen(args, wl, dev):
         "seq_len": total, "w0": wl.w0, "grid_w": wl.grid_w, "block": 128, "active_blocks": nnz,
         "total_blocks": sum(m.nb ** 2 for m in masks),
         "semantics": "element" if args.element else "block",
-        "pass": "backward" if args.backward else "forward"},
+        "pass": "backward" if args.backward else "forward",
+        "mask": "rule (in-kernel)" if args.rule else "csr"},
         traffic=None, cpu=cpu)
     line["separate_launches_ms"] = round(sms, 4)
     line["speedup_vs_separate"] = round(sms / ms, 3)
@@ -302,10 +309,6 @@ def main():
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if args.varlen:
-        if args.rule:
-            print("--rule and --varlen do not combine: the on-the-fly mask is for a uniform "
-                  "batch", file=sys.stderr)
-            sys.exit(2)
         bench_varlen(args, wl, dev)
         return
 
