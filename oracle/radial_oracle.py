@@ -329,10 +329,3 @@ def full_csr(n: int, block: int = BLOCK):
     """The CSR of the all-active block mask (every query block sees every key block)."""
     return csr(np.ones((num_blocks(n, block),) * 2, dtype=bool))
 
-
-def active_tile_flops(row_ptr, head_dim: int, batch_heads: int, block: int = BLOCK) -> int:
-    """Work counted on whole active tiles: 4 * D * block**2 per tile per (batch, head).
-
-    QK^T and PV each take 2 * block**2 * D multiply-adds per tile.
-    """
-    return 4 * head_dim * block * block * int(row_ptr[-1]) * batch_heads

@@ -13,6 +13,7 @@ import torch
 import block_sparse_attention_radial_amd as radial
 from block_sparse_attention_radial_amd.inputs import WORKLOADS, Workload, draw_qkv
 from oracle import radial_oracle as ro
+from oracle_masks import oracle_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +32,7 @@ def f64(x):
 
 
 def oracle_element(q, k, v, mask, scale, query_blocks=None):
-    rp, ci = mask.row_ptr.cpu().numpy(), mask.col_idx.cpu().numpy()
+    rp, ci = oracle_csr(mask.frames, mask.tokens_per_frame, mask.w0)
     return ro.attention(f64(q), f64(k), f64(v), rp, ci, scale, query_blocks=query_blocks,
                         element=(mask.tokens_per_frame, mask.w0))
 

@@ -14,6 +14,7 @@ import torch
 import block_sparse_attention_radial_amd as radial
 from block_sparse_attention_radial_amd.inputs import WORKLOADS, Workload, draw_packed_qkv, draw_qkv
 from oracle import radial_oracle as ro
+from oracle_masks import oracle_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -69,8 +70,7 @@ def test_grid_parity_small(name, B, H, D, F, gh, gw, w0, element):
     lse = torch.empty(B, H, wl.n, dtype=torch.float32, device="cuda")
     o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), lse=lse, element=element)
     torch.cuda.synchronize()
-    ref, ref_lse = ro.attention(f64(q), f64(k), f64(v), mask.row_ptr.numpy(),
-                                mask.col_idx.numpy(), wl.scale,
+    ref, ref_lse = ro.attention(f64(q), f64(k), f64(v), *oracle_csr(F, S, w0, gw), wl.scale,
                                 element=(S, w0, gw) if element else None)
     check(o, ref)
     assert np.abs(f64(lse) - ref_lse).max() < 1e-3
@@ -126,7 +126,8 @@ def test_grid_full_size_sampled_wan(element):
     o = radial.attn_fwd(q, k, v, mask.to("cuda"), element=element)
     torch.cuda.synchronize()
     qbs = [0, 1, 97, 128, 200, wl.nb - 1]
-    ref, _ = ro.attention(f64(q), f64(k), f64(v), mask.row_ptr.numpy(), mask.col_idx.numpy(),
+    ref, _ = ro.attention(f64(q), f64(k), f64(v),
+                          *oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0, wl.grid_w),
                           wl.scale, query_blocks=qbs,
                           element=(wl.tokens_per_frame, wl.w0, wl.grid_w) if element else None)
     rows = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in qbs])
@@ -155,8 +156,8 @@ def test_grid_element_backward(name, D, F, gh, gw, w0):
     o = radial.attn_fwd(qc, kc, vc, md, lse=lse, element=True)
     grads = radial.attn_bwd(qc, kc, vc, o, dc, lse, md, element=True)
     torch.cuda.synchronize()
-    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), mask.row_ptr.numpy(),
-                                mask.col_idx.numpy(), wl.scale, element=(S, w0, gw))
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), *oracle_csr(F, S, w0, gw),
+                                wl.scale, element=(S, w0, gw))
     for got, r in zip(grads, ref):
         check_rel(got, r)
 
@@ -186,6 +187,6 @@ def test_1d_element_with_a_huge_window_is_block_dense():
     mask = radial.build_mask(5, 300, 2**31 - 1)
     o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), element=True)
     torch.cuda.synchronize()
-    ref, _ = ro.attention(f64(q), f64(k), f64(v), mask.row_ptr.numpy(), mask.col_idx.numpy(),
+    ref, _ = ro.attention(f64(q), f64(k), f64(v), *oracle_csr(5, 300, 2**31 - 1),
                           wl.scale, element=(300, 2**31 - 1))
     check(o, ref)

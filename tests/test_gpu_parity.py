@@ -2,9 +2,10 @@
 
 Bar: every checked output element within max-abs 2e-2 and mean-abs 2e-3 of the oracle.
 The oracle sees the exact fp64 upcast of the bf16 tensors given to the GPU. Small shapes
-are compared on every element. The full-size workloads are compared on sampled
-query blocks: the first one, the ragged last one, and seeded picks between, for several
-heads. The CPU oracle computes those blocks one by one.
+are compared on every element. At full size the oracle walks its own CSR of the rule:
+Wan is compared on every element of all 40 heads; HunyuanVideo and the 4x longer video
+on every query block of one head and on sampled blocks of two more. out and lse start as
+NaN, and every row of every head must come out finite.
 """
 import numpy as np
 import pytest
@@ -13,6 +14,7 @@ import torch
 import block_sparse_attention_radial_amd as radial
 from block_sparse_attention_radial_amd.inputs import WORKLOADS, Workload, draw_qkv
 from oracle import radial_oracle as ro
+from oracle_masks import oracle_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +33,12 @@ def f64(x):
 
 
 def oracle_out(q, k, v, mask, scale, query_blocks=None):
-    rp, ci = mask.row_ptr.cpu().numpy(), mask.col_idx.cpu().numpy()
+    """The oracle over the same rule as `mask` (its own CSR, or its own all-active CSR for
+    the dense mask)."""
+    if mask.w0 == 2**31 - 1 and mask.frames == 1:
+        rp, ci = ro.full_csr(mask.n)
+    else:
+        rp, ci = oracle_csr(mask.frames, mask.tokens_per_frame, mask.w0)
     return ro.attention(f64(q), f64(k), f64(v), rp, ci, scale, query_blocks=query_blocks)
 
 
@@ -86,7 +93,7 @@ def test_scale_zero_is_mean_of_v_over_key_set():
     o = radial.attn_fwd(q.cuda(), k.cuda(), v.cuda(), mask.to("cuda"), scale=0.0)
     torch.cuda.synchronize()
     vv = f64(v)
-    rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
+    rp, ci = oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0)
     ref = np.empty_like(vv)
     for qb in range(mask.nb):
         keys = ro.row_keys(rp, ci, qb, wl.n)
@@ -144,19 +151,112 @@ def sampled_blocks(nb, seed):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("key", ["wan", "hunyuan", "long4x"])
-def test_parity_full_size_sampled(key):
-    wl = WORKLOADS[key]
-    q, k, v = draw_qkv(wl, seed=0, device="cuda")
-    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
-    o = radial.attn_fwd(q, k, v, mask.to("cuda"))
-    torch.cuda.synchronize()
+FULL = ["wan", "hunyuan", "long4x"]
+# Wan's 40 heads are compared on every element, in groups of 8 heads per test (about
+# half a minute of oracle time each on 16 host threads).
+WAN_HEAD_GROUPS = [range(h, h + 8) for h in range(0, 40, 8)]
+
+_full_cache = {}
+
+
+def full_size_run(key):
+    """The forward pass of a full-size workload, once per module: q, k, v drawn on the
+    GPU, out and lse pre-filled with NaN (so a row the kernel skips stays NaN), and the
+    oracle's own CSR of the rule. Only the latest workload is kept, to bound memory."""
+    if key not in _full_cache:
+        _full_cache.clear()
+        torch.cuda.empty_cache()
+        wl = WORKLOADS[key]
+        q, k, v = draw_qkv(wl, seed=0, device="cuda")
+        mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+        rp, ci = oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        radial.attn_fwd(q, k, v, mask.to("cuda"), out=o, lse=lse)
+        torch.cuda.synchronize()
+        _full_cache[key] = (wl, q, k, v, o, lse, mask, rp, ci)
+    return _full_cache[key]
+
+
+def compare_head(run, h, query_blocks=None):
+    """Output and lse of head h (rows of `query_blocks`, or every row) against the
+    oracle, which walks its own CSR."""
+    wl, q, k, v, o, lse, _, rp, ci = run
+    sl = (slice(None), slice(h, h + 1))
+    ref, ref_lse = ro.attention(f64(q[sl]), f64(k[sl]), f64(v[sl]), rp, ci, wl.scale,
+                                query_blocks=query_blocks)
+    rows = None
+    if query_blocks is not None:
+        rows = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128))
+                               for b in query_blocks])
+    check(o[sl], ref, rows=rows)
+    got_lse = f64(lse[sl])
+    if rows is not None:
+        got_lse, ref_lse = got_lse[..., rows], ref_lse[..., rows]
+    assert np.abs(got_lse - ref_lse).max() < 1e-3
+
+
+@pytest.mark.parametrize("key", FULL)
+def test_full_size_mask_is_the_oracle_csr(key):
+    _, _, _, _, _, _, mask, rp, ci = full_size_run(key)
+    assert np.array_equal(mask.row_ptr.numpy(), rp)
+    assert np.array_equal(mask.col_idx.numpy(), ci)
+
+
+@pytest.mark.parametrize("key", FULL)
+def test_full_size_every_row_written(key):
+    """out and lse start as NaN: after one call every row of every (batch, head) must be
+    finite, so no work item was skipped by the persistent scheduler."""
+    _, _, _, _, o, lse, _, _, _ = full_size_run(key)
+    assert bool(torch.isfinite(o).all())
+    assert bool(torch.isfinite(lse).all())
+
+
+@pytest.mark.parametrize("heads", WAN_HEAD_GROUPS,
+                         ids=[f"heads{r.start}-{r.stop - 1}" for r in WAN_HEAD_GROUPS])
+def test_wan_every_element(heads):
+    run = full_size_run("wan")
+    for h in heads:
+        print(f"wan head {h}", flush=True)
+        compare_head(run, h)
+
+
+@pytest.mark.parametrize("key", ["hunyuan", "long4x"])
+def test_full_size_one_head_every_block(key):
+    """Every query block of the middle head against the oracle."""
+    run = full_size_run(key)
+    compare_head(run, run[0].heads // 2)
+
+
+@pytest.mark.parametrize("key", ["hunyuan", "long4x"])
+def test_full_size_sampled_blocks(key):
+    """Sampled query blocks (the first two, the middle one, the last two with the ragged
+    tail, and three seeded picks) of the first and the last head."""
+    run = full_size_run(key)
+    wl = run[0]
     blocks = sampled_blocks(wl.nb, seed=wl.n)
-    for h in sorted({0, wl.heads // 2, wl.heads - 1}):
-        sl = (slice(None), slice(h, h + 1))
-        ref, _ = oracle_out(q[sl], k[sl], v[sl], mask, wl.scale, query_blocks=blocks)
-        rows = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in blocks])
-        check(o[sl], ref, rows=rows)
+    for h in (0, wl.heads - 1):
+        compare_head(run, h, query_blocks=blocks)
+
+
+def test_many_work_items_full_output():
+    """Small's shape with 64 heads: 2048 work items, eight per workgroup of the
+    persistent grid on average, so the item loop, the per-XCD lists and the taking of
+    items from other lists all run; every element against the oracle."""
+    wl = Workload("small-64-heads", 1, 64, 64, 8, 1024, 512, 0.5)
+    q, k, v = draw_qkv(wl, seed=9, device="cuda")
+    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+    rp, ci = oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0)
+    for pairs in (True, False):
+        m = mask if pairs else radial.Mask(mask.row_ptr, mask.col_idx, wl.frames,
+                                           wl.tokens_per_frame, wl.w0)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+        radial.attn_fwd(q, k, v, m.to("cuda"), out=o, lse=lse)
+        torch.cuda.synchronize()
+        ref, ref_lse = ro.attention(f64(q), f64(k), f64(v), rp, ci, wl.scale)
+        check(o, ref)
+        assert np.abs(f64(lse) - ref_lse).max() < 1e-3
 
 
 def test_dense_full_size_sampled():

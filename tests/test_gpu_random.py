@@ -13,6 +13,7 @@ import torch
 import block_sparse_attention_radial_amd as radial
 from block_sparse_attention_radial_amd.inputs import Workload, draw_qkv
 from oracle import radial_oracle as ro
+from oracle_masks import oracle_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +68,7 @@ def test_random_case_against_oracle(seed):
     o = radial.attn_fwd(qc, kc, vc, md, lse=lse, element=c["element"])
     torch.cuda.synchronize()
     rule = ((c["S"], c["w0"]) + ((c["gw"],) if c["gw"] else ())) if c["element"] else None
-    rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
+    rp, ci = oracle_csr(c["F"], c["S"], c["w0"], c["gw"])
     ref, ref_lse = ro.attention(f64(q), f64(k), f64(v), rp, ci, wl.scale, element=rule)
     err = np.abs(f64(o) - ref)
     assert np.isfinite(f64(o)).all()

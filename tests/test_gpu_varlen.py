@@ -11,6 +11,7 @@ import torch
 
 import block_sparse_attention_radial_amd as radial
 from oracle import radial_oracle as ro
+from oracle_masks import oracle_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +75,7 @@ def test_varlen_parity_against_oracle():
     for m in masks:
         sl = slice(t0, t0 + m.n)
         f64 = lambda x: x[sl].permute(1, 0, 2).to("cpu", torch.float64).numpy()  # noqa: E731
-        ref, _ = ro.attention(f64(q), f64(k), f64(v), m.row_ptr.numpy(), m.col_idx.numpy(),
+        ref, _ = ro.attention(f64(q), f64(k), f64(v), *oracle_csr(m.frames, S, w0),
                               D ** -0.5)
         err = np.abs(f64(out) - ref)
         assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
@@ -162,8 +163,8 @@ def test_varlen_backward_against_oracle():
     for m in masks:
         sl = slice(t0, t0 + m.n)
         f64 = lambda x: x.detach()[sl].permute(1, 0, 2).to("cpu", torch.float64).numpy()  # noqa: E731
-        ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), m.row_ptr.numpy(),
-                                    m.col_idx.numpy(), D ** -0.5)
+        ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do),
+                                    *oracle_csr(m.frames, S, w0), D ** -0.5)
         for got, r in zip((q.grad, k.grad, v.grad), ref):
             err = np.abs(f64(got) - r)
             assert err.max() <= 2e-2 * np.abs(r).max() and err.mean() <= 5e-3 * np.abs(r).mean()
