@@ -382,6 +382,15 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     return dq, dk, dv
 
 
+def _like_q(do: torch.Tensor, q: torch.Tensor) -> torch.Tensor:
+    """The output gradient in q's strides (the backward kernels take one set of strides
+    for every tensor). A gradient in other strides (a contiguous one for a [B, n, H, D]
+    view, or the zero strides of an expanded sum's gradient) is copied into a new tensor."""
+    if do.stride() == q.stride() and do.dtype == q.dtype:
+        return do
+    return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device).copy_(do)
+
+
 class RadialAttentionFunction(torch.autograd.Function):
     """attn_fwd with its backward (attn_bwd) for autograd."""
 
@@ -397,8 +406,7 @@ class RadialAttentionFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        do = do if do.stride() == q.stride() else do.as_strided(q.shape, q.stride()).copy_(do)
-        dq, dk, dv = attn_bwd(q, k, v, o, do, lse, ctx.mask, scale=ctx.scale,
+        dq, dk, dv = attn_bwd(q, k, v, o, _like_q(do, q), lse, ctx.mask, scale=ctx.scale,
                               element=ctx.element)
         return dq, dk, dv, None, None, None
 
@@ -617,9 +625,8 @@ class RadialAttentionVarlenFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        do = do if do.stride() == q.stride() else do.as_strided(q.shape, q.stride()).copy_(do)
-        dq, dk, dv = attn_bwd_varlen(q, k, v, o, do, lse, ctx.mask, scale=ctx.scale,
-                                     element=ctx.element)
+        dq, dk, dv = attn_bwd_varlen(q, k, v, o, _like_q(do, q), lse, ctx.mask,
+                                     scale=ctx.scale, element=ctx.element)
         return dq, dk, dv, None, None, None
 
 

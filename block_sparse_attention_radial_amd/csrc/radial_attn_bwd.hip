@@ -65,7 +65,7 @@ struct BwdArgs {
   int64_t stride_b, stride_h;
   int nb, heads, n, stride_s;
   int elem_s, elem_gw, elem_w0;  // element masking: frame length, grid width, W0
-  float c;      // scale * log2(e)
+  float c;      // scale * log2(e), at least FLT_MIN (base2_scale)
   float scale;
   // varlen: 0 for a uniform batch, else the number of samples in `plan`; q, k, v, o, dO,
   // dq, dk, dv are then one packed sequence of n tokens, and lse, delta are [heads, n].
@@ -540,7 +540,7 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
   args.elem_s = element_tokens_per_frame;
   args.elem_gw = element_grid_w;
   args.elem_w0 = element_w0;
-  args.c = scale * kLog2e;
+  args.c = base2_scale(scale);
   args.scale = scale;
   args.varlen = 0;
   return launch_all(args, static_cast<int>(rows_total), static_cast<int>(items), head_dim,
@@ -596,7 +596,7 @@ extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const vo
   args.elem_s = element_tokens_per_frame;
   args.elem_gw = element_grid_w;
   args.elem_w0 = element_w0;
-  args.c = scale * kLog2e;
+  args.c = base2_scale(scale);
   args.scale = scale;
   args.varlen = batch;
   int64_t tok = 0, rows = 0, wgs = 0;

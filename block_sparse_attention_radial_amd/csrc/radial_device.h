@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
+#include <cmath>
 #include <cstdint>
 
 namespace {
@@ -216,6 +218,12 @@ inline bool element_args_valid(int32_t s, int32_t w0, int32_t grid_w) {
   if (s < kBlock || s > kMaxFrame || w0 < 1) return false;
   return grid_w == 0 || (grid_w > 0 && s % grid_w == 0);
 }
+
+// Base-2 score scale (host): c = scale * log2(e), kept >= FLT_MIN so that a masked score
+// of -inf stays -inf after scaling (never -inf * 0 = NaN). For scale = 0 every finite
+// score times FLT_MIN rounds away against the reference maximum, so each real key gets
+// the same p: the scale-0 softmax, a mean over the key set.
+inline float base2_scale(float scale) { return fmaxf(scale * kLog2e, FLT_MIN); }
 
 // (a / S, a % S) for 0 <= a < 2^24 with a quotient below 2^21 (frame lengths S >= 128,
 // or any grid width when a < 2^21), given inv_s within a few ulp of 1 / S: the float

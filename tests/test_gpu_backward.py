@@ -19,6 +19,7 @@ import torch
 import block_sparse_attention_radial_amd as radial
 from block_sparse_attention_radial_amd.inputs import WORKLOADS, Workload, draw_qkv
 from oracle import radial_oracle as ro
+from oracle_masks import oracle_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -77,8 +78,8 @@ SMALL = [
 def test_backward_parity_small(name, B, H, D, F, S, w0, element):
     wl = Workload(name, B, H, D, F, S, w0, 1.0)
     (q, k, v, do), mask, grads = run(wl, element)
-    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), mask.row_ptr.numpy(),
-                                mask.col_idx.numpy(), D ** -0.5,
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), *oracle_csr(F, S, w0),
+                                D ** -0.5,
                                 element=(S, w0) if element else None)
     for got, r in zip(grads, ref):
         check(got, r)
@@ -118,6 +119,64 @@ def test_autograd_matches_attn_bwd():
         assert torch.equal(a, b)
 
 
+def test_autograd_of_a_sum():
+    """o.sum().backward(): the output gradient arrives as an expanded tensor with zero
+    strides; it is copied into q's strides before the backward kernels read it."""
+    wl = Workload("sum", 1, 2, 128, 4, 1000, 200, 1.0)
+    q, k, v = draw_qkv(wl, seed=6)
+    mask = radial.build_mask(4, 1000, 200)
+    qc, kc, vc = (x.cuda().requires_grad_() for x in (q, k, v))
+    radial.attention(qc, kc, vc, mask.to("cuda")).sum().backward()
+    torch.cuda.synchronize()
+    do = torch.ones(q.shape, dtype=torch.bfloat16)
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), *oracle_csr(4, 1000, 200),
+                                wl.scale)
+    for got, r in zip((qc.grad, kc.grad, vc.grad), ref):
+        check(got, r)
+
+
+def test_autograd_with_bnhd_views():
+    """q, k, v stored [B, n, H, D] and viewed as [B, H, n, D]; the output gradient comes
+    contiguous in [B, H, n, D] (other strides than q's) and is copied into q's strides."""
+    wl = Workload("bnhd", 2, 3, 128, 4, 500, 150, 1.0)
+    q, k, v = draw_qkv(wl, seed=8)
+    g = torch.Generator().manual_seed(9)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    mask = radial.build_mask(4, 500, 150)
+    views = [x.transpose(1, 2).contiguous().cuda().transpose(1, 2).requires_grad_()
+             for x in (q, k, v)]
+    assert views[0].stride() != do.stride()
+    o = radial.attention(*views, mask.to("cuda"))
+    o.backward(do.cuda())
+    torch.cuda.synchronize()
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), *oracle_csr(4, 500, 150),
+                                wl.scale)
+    for got, r in zip((x.grad for x in views), ref):
+        check(got, r)
+
+
+def test_backward_scale_zero_ragged():
+    """scale = 0 on a ragged shape: P is uniform over each row's real keys, so dq and dk
+    are exactly zero and dv is the mean of dO over the rows that reach each key; padded
+    keys must not turn into NaN."""
+    wl = Workload("s0", 1, 2, 128, 5, 1000, 100, 1.0)
+    q, k, v = draw_qkv(wl, seed=10)
+    g = torch.Generator().manual_seed(11)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    mask = radial.build_mask(5, 1000, 100)
+    md = mask.to("cuda")
+    qc, kc, vc, dc = (x.cuda() for x in (q, k, v, do))
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(qc, kc, vc, md, scale=0.0, lse=lse)
+    dq, dk, dv = radial.attn_bwd(qc, kc, vc, o, dc, lse, md, scale=0.0)
+    torch.cuda.synchronize()
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), *oracle_csr(5, 1000, 100),
+                                0.0)
+    assert not np.abs(ref[0]).any() and not np.abs(ref[1]).any()
+    assert bool((dq == 0).all()) and bool((dk == 0).all())
+    check(dv, ref[2])
+
+
 def test_backward_full_size_sampled_wan():
     """Wan shape (two heads): dq on sampled query blocks, dk and dv on sampled key
     blocks (the oracle processes every query block that reaches them)."""
@@ -133,8 +192,9 @@ def test_backward_full_size_sampled_wan():
     dq, dk, dv = radial.attn_bwd(q, k, v, o, do, lse, md)
     torch.cuda.synchronize()
     qbs, kbs = [0, 131, wl.nb - 1], [3, wl.nb - 1]
-    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), mask.row_ptr.numpy(),
-                                mask.col_idx.numpy(), wl.scale, query_blocks=qbs,
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do),
+                                *oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0),
+                                wl.scale, query_blocks=qbs,
                                 key_blocks=kbs)
     rows_q = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in qbs])
     rows_k = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in kbs])
