@@ -20,7 +20,9 @@ videos of those frame counts (the workload's frame length, W0, heads and head_di
 beside the same samples run as separate launches one after another (with --backward,
 the backward pass likewise). --rule times the forward with the block mask derived in the
 kernel from the rule instead of read from the CSR (the same key blocks, so the same work
-is counted), also for --varlen.
+is counted), also for --varlen. The default run (Wan, block semantics, forward) also
+times the HunyuanVideo and the 4x-long workloads, sparse and dense, and adds them to the
+line under "other_workloads" (--no-extra skips them).
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -72,21 +74,29 @@ def traffic_bytes(workload_name: str):
 
 
 def time_launches(fn, steps: int, warmup: int):
+    """Run `fn` warmup times, synchronise, then time exactly `steps` calls, each between its
+    own pair of HIP events on torch's current stream (the stream the kernels run on),
+    and synchronise again. Returns the mean, median and minimum per-call milliseconds
+    and the host wall time of the timed region."""
+    import statistics
+
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    for start, stop in events:
+        start.record(stream)
         fn()
-    stop.record(stream)
+        stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall
+    ms = [start.elapsed_time(stop) for start, stop in events]
+    return {"mean": sum(ms) / len(ms), "median": statistics.median(ms), "min": min(ms),
+            "wall": wall}
 
 
 def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False, do=None):
@@ -99,10 +109,9 @@ def cpu_baseline(wl, q, k, v, mask, seconds: float, element: bool = False, do=No
     from oracle import radial_oracle as ro
 
     t0 = time.perf_counter()
-    ro.block_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w)
+    rp, ci = ro.csr(ro.block_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w))
     mask_s = time.perf_counter() - t0
-
-    rp, ci = mask.row_ptr.numpy(), mask.col_idx.numpy()
+    del mask  # the oracle walks its own CSR
     rule = (wl.tokens_per_frame, wl.w0) + ((wl.grid_w,) if wl.grid_w else ())
     order = np.random.default_rng(0).permutation(wl.nb)
     blocks, tiles, heads, elapsed = 0, 0, 0, 0.0
@@ -181,7 +190,8 @@ def bench_varlen(args, wl, dev):
         run = lambda: radial.attn_bwd_varlen(q, k, v, o, do, lse, vdev, element=el)  # noqa: E731
     else:
         run = lambda: radial.attn_fwd_varlen(q, k, v, vdev, out=o, element=el)  # noqa: E731
-    ms, wall = time_launches(run, args.steps, args.warmup)
+    tm = time_launches(run, args.steps, args.warmup)
+    ms, wall = tm["mean"], tm["wall"]
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"packed{' backward' if args.backward else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s "
         f"({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
@@ -203,7 +213,7 @@ def bench_varlen(args, wl, dev):
             else:
                 qs, ks, vs, os_ = vw
                 radial.attn_fwd(qs, ks, vs, md, out=os_, element=el)
-    sms, _ = time_launches(separate, args.steps, args.warmup)
+    sms = time_launches(separate, args.steps, args.warmup)["mean"]
     log(f"separate launches: {sms:.3f} ms/step ({flops / (sms * 1e-3) / 1e12:.1f} TFLOP/s)")
 
     cpu = None
@@ -216,7 +226,7 @@ def bench_varlen(args, wl, dev):
         cpu = cpu_baseline(swl, qs, ks, vs, masks[0], args.cpu_seconds, args.element, dos)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
-    line = result_line(args, tflops, ms, wall, {
+    line = result_line(args, tflops, tm, {
         "workload": f"varlen-{wl.name}", "batch": len(frames), "heads": wl.heads,
         "head_dim": wl.head_dim, "frames": frames, "tokens_per_frame": wl.tokens_per_frame,
         "seq_len": total, "w0": wl.w0, "grid_w": wl.grid_w, "block": 128, "active_blocks": nnz,
@@ -231,8 +241,10 @@ def bench_varlen(args, wl, dev):
     print(json.dumps(line), flush=True)
 
 
-def result_line(args, tflops, ms, wall, config, traffic, cpu):
-    """The JSON result line, without the dense baseline fields."""
+def result_line(args, tflops, tm, config, traffic, cpu):
+    """The JSON result line, without the dense baseline fields. tm: time_launches' result;
+    ms_per_step is the mean per-launch time, and value the work over it."""
+    ms = tm["mean"]
     return {
         "metric": "active-block attention TFLOP/s (% bf16 MFMA peak) + speedup vs dense, 1 GPU",
         "value": round(tflops, 3),
@@ -248,7 +260,9 @@ def result_line(args, tflops, ms, wall, config, traffic, cpu):
         "data": "synthetic: seeded N(0,1) q/k/v in bf16 at the workload's shape",
         "config": config,
         "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "wall_s_timed": round(wall, 4),
+        "ms_median": round(tm["median"], 4),
+        "ms_min": round(tm["min"], 4),
+        "wall_s_timed": round(tm["wall"], 4),
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 3),
@@ -269,6 +283,9 @@ def main():
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with the default Wan workload, skip the HunyuanVideo and 4x-long "
+                         "timings that the line otherwise carries")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--element", action="store_true",
                     help="element masking inside the active blocks (block semantics otherwise)")
@@ -344,10 +361,13 @@ def main():
         run = step(mdev)
     else:
         run = lambda: radial.attn_fwd(q, k, v, mdev, out=o, element=args.element)  # noqa: E731
-    ms, wall = time_launches(run, args.steps, args.warmup)
+    tm = time_launches(run, args.steps, args.warmup)
+    ms = tm["mean"]
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{'backward' if args.backward else 'sparse'}"
-        f"{' (element masking)' if args.element else ''}: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
+        f"{' (element masking)' if args.element else ''}: {ms:.3f} ms/step "
+        f"(median {tm['median']:.3f}, min {tm['min']:.3f}), {tflops:.1f} TFLOP/s "
+        f"({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
 
     dense = None
     if not args.no_dense:
@@ -355,7 +375,7 @@ def main():
         dsteps = max(3, args.steps // 2)
         drun = step(dmask) if args.backward else (
             lambda: radial.attn_fwd(q, k, v, dmask, out=o))
-        dms, _ = time_launches(drun, dsteps, min(args.warmup, 2))
+        dms = time_launches(drun, dsteps, min(args.warmup, 2))["mean"]
         dflops = 4 * wl.head_dim * 128 * 128 * dmask.nnz * bh * work
         dense = {"ms": dms, "tflops": dflops / (dms * 1e-3) / 1e12, "steps": dsteps,
                  "speedup": dms / ms, "ideal_speedup": dmask.nnz / mask.nnz}
@@ -369,7 +389,7 @@ def main():
 
     traffic = None if args.backward or args.rule else traffic_bytes(
         wl.name + ("-element" if args.element else ""))
-    line = result_line(args, tflops, ms, wall, {
+    line = result_line(args, tflops, tm, {
         "workload": wl.name, "batch": wl.batch, "heads": wl.heads,
         "head_dim": wl.head_dim, "frames": wl.frames,
         "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
@@ -382,7 +402,52 @@ def main():
     line["speedup_vs_dense"] = None if dense is None else round(dense["speedup"], 3)
     line["dense"] = None if dense is None else {k_: round(v_, 4) for k_, v_ in dense.items()}
     line["mask_build_ms"] = round(mask_ms, 3)
+
+    plain = not (args.backward or args.element or args.rule or args.no_extra)
+    if plain and args.workload == "wan":
+        # The pages' other two workloads, on the same kernel: the same line carries their
+        # sparse and dense times (no CPU leg), with the ceiling that block skipping allows.
+        del q, k, v, o, run, mdev
+        torch.cuda.empty_cache()
+        line["other_workloads"] = {key: other_workload(WORKLOADS[key], dev, args)
+                                   for key in ("hunyuan", "long4x")}
     print(json.dumps(line), flush=True)
+
+
+def other_workload(wl, dev, args):
+    """Sparse and dense forward times of a full-size workload (5 and 3 timed launches)."""
+    import torch
+
+    import block_sparse_attention_radial_amd as radial
+    from block_sparse_attention_radial_amd.inputs import draw_qkv
+
+    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
+    mdev = mask.to(dev)
+    q, k, v = draw_qkv(wl, seed=0, device=dev)
+    o = torch.empty_like(q)
+    flops = 4 * wl.head_dim * 128 * 128 * mask.nnz * wl.batch * wl.heads
+    tm = time_launches(lambda: radial.attn_fwd(q, k, v, mdev, out=o), 5, 2)
+    dmask = radial.dense_mask(wl.n, device=dev)
+    dms = time_launches(lambda: radial.attn_fwd(q, k, v, dmask, out=o), 3, 1)["mean"]
+    tflops = flops / (tm["mean"] * 1e-3) / 1e12
+    rec = {
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "frames": wl.frames,
+                   "tokens_per_frame": wl.tokens_per_frame, "seq_len": wl.n, "w0": wl.w0,
+                   "active_blocks": mask.nnz, "total_blocks": mask.nb ** 2},
+        "steps": 5, "ms_per_step": round(tm["mean"], 4), "ms_median": round(tm["median"], 4),
+        "ms_min": round(tm["min"], 4), "tflops": round(tflops, 3),
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "dense_ms": round(dms, 4), "dense_steps": 3,
+        "speedup_vs_dense": round(dms / tm["mean"], 3),
+        "block_count_ceiling": round(mask.nb ** 2 / mask.nnz, 3),
+    }
+    log(f"{wl.name}: sparse {tm['mean']:.3f} ms ({tflops:.1f} TFLOP/s, "
+        f"{tflops / PEAK_BF16_TFLOPS:.1%}), dense {dms:.3f} ms, speedup "
+        f"{rec['speedup_vs_dense']:.2f}x (block-count ceiling {rec['block_count_ceiling']:.2f}x)")
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return rec
 
 
 if __name__ == "__main__":
