@@ -58,6 +58,7 @@
 #include <climits>
 #include <cstdint>
 #include <atomic>
+#include <mutex>
 
 #include "../../include/radial_attn.h"
 #include "radial_device.h"
@@ -805,27 +806,8 @@ int cu_count() {
   return cus;
 }
 
-// Counter slots: eager calls rotate through the first half; a call made under stream
-// capture takes one from the second half, so that the slot baked into a graph is not
-// the one of any eager call made in the next 128 calls.
-std::atomic<uint32_t> g_next_slot{0};
-std::atomic<uint32_t> g_next_capture_slot{0};
-
-// The launch shared by the uniform and the varlen entry points: a persistent grid of one
-// workgroup per CU (a multiple of 8, at most one per item) and a counter slot.
-int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, void* stream) {
-  const int cus = cu_count();
-  if (cus < 0) return RADIAL_ERR_HIP;
-  const int64_t per_xcd = std::min<int64_t>(std::max(cus / 8, 1), (items + 7) / 8);
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-  if (st != nullptr && hipStreamIsCapturing(st, &capture) != hipSuccess) return RADIAL_ERR_HIP;
-  constexpr uint32_t kHalf = kCounterSlots / 2;
-  const bool captured = capture == hipStreamCaptureStatusActive;
-  const uint32_t turn = (captured ? g_next_capture_slot : g_next_slot)
-                            .fetch_add(1, std::memory_order_relaxed);
-  args.slot = static_cast<int>((captured ? kHalf : 0u) + turn % kHalf);
-  args.items = static_cast<int>(items);
+// One launch of the forward kernel for these arguments (slot and item count set).
+int32_t launch_kernel(const FwdArgs& args, int64_t per_xcd, int head_dim, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>(8 * per_xcd)), block(kThreads);
   const int mode = args.elem_s == 0 ? 0 : (args.elem_gw == 0 ? 1 : 2);
   if (head_dim == 128) {
@@ -846,11 +828,66 @@ int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, void* stream) {
   return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
 }
 
-// Base-2 score scale. It is kept >= FLT_MIN so a padding score of -inf stays -inf after
-// scaling (never -inf * 0 = NaN). For scale = 0 every finite score times FLT_MIN rounds
-// away against m, giving p = 2^-m for each real key: the mean of V over the key set,
-// which is the scale-0 softmax.
-float base2_scale(float scale) { return fmaxf(scale * kLog2e, FLT_MIN); }
+// Counter slots. Eager calls rotate through the first half of the ring, per device. Each
+// slot keeps an event recorded after the launch that last used it; a new launch on that
+// slot first makes its stream wait for that event if it has not completed, so two
+// kernels never use one slot at the same time, however many calls are in flight and on
+// however many streams. A call made under stream capture takes a slot from the second
+// half instead (a captured graph cannot wait for an event recorded outside it), so the
+// slot baked into a graph is not the one of any eager call.
+constexpr int kMaxDevices = 64;
+constexpr uint32_t kEagerSlots = kCounterSlots / 2;
+struct EagerSlots {
+  std::mutex mu;
+  uint32_t next = 0;
+  hipEvent_t done[kEagerSlots] = {};
+};
+EagerSlots g_eager[kMaxDevices];
+std::atomic<uint32_t> g_next_capture_slot{0};
+
+// The launch shared by the uniform and the varlen entry points: a persistent grid of one
+// workgroup per CU (a multiple of 8, at most one per item) and a counter slot.
+int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, void* stream) {
+  const int cus = cu_count();
+  if (cus < 0) return RADIAL_ERR_HIP;
+  const int64_t per_xcd = std::min<int64_t>(std::max(cus / 8, 1), (items + 7) / 8);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (st != nullptr && hipStreamIsCapturing(st, &capture) != hipSuccess) return RADIAL_ERR_HIP;
+  args.items = static_cast<int>(items);
+  if (capture == hipStreamCaptureStatusActive) {
+    const uint32_t turn = g_next_capture_slot.fetch_add(1, std::memory_order_relaxed);
+    args.slot = static_cast<int>(kEagerSlots + turn % kEagerSlots);
+    return launch_kernel(args, per_xcd, head_dim, st);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RADIAL_ERR_HIP;
+  EagerSlots& tab = g_eager[dev];
+  // Held from the choice of the slot to the event that marks its new use, so that two
+  // host threads never take one slot at once.
+  std::lock_guard<std::mutex> lock(tab.mu);
+  const uint32_t slot = tab.next;
+  hipEvent_t& done = tab.done[slot];
+  if (done == nullptr) {
+    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess) {
+      done = nullptr;
+      return RADIAL_ERR_HIP;
+    }
+  } else {
+    const hipError_t q = hipEventQuery(done);
+    if (q == hipErrorNotReady) {
+      if (hipStreamWaitEvent(st, done, 0) != hipSuccess) return RADIAL_ERR_HIP;
+    } else if (q != hipSuccess) {
+      return RADIAL_ERR_HIP;
+    }
+  }
+  args.slot = static_cast<int>(slot);
+  const int32_t err = launch_kernel(args, per_xcd, head_dim, st);
+  if (err != RADIAL_OK) return err;
+  if (hipEventRecord(done, st) != hipSuccess) return RADIAL_ERR_HIP;
+  tab.next = (slot + 1) % kEagerSlots;
+  return RADIAL_OK;
+}
 
 // Checks shared by both entry points.
 int32_t check_common(const void* q, const void* k, const void* v, const void* o,

@@ -25,8 +25,9 @@
  * Conventions for every call:
  *  - The return value is 0 (RADIAL_OK) on success or a negative RADIAL_ERR_* code.
  *    No call aborts or prints.
- *  - All buffers are owned by the caller. The library allocates no memory. Its only
- *    state is described under radial_attn_fwd (work counters in static device memory).
+ *  - All buffers are owned by the caller. The library allocates no device memory. Its
+ *    only state is described under radial_attn_fwd (work counters in static device
+ *    memory and the events that guard their reuse).
  *  - Every check that can fail is done on the host before any HIP call.
  */
 #ifndef RADIAL_ATTN_H
@@ -184,14 +185,21 @@ int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const int32_t* co
  * Scheduling state. The kernel runs one workgroup per compute unit; the workgroups take
  * (batch, head, query-block pair) items from atomic counters. The counters live in a
  * ring of 256 slots in the library's static device memory (one copy per device, zero
- * when the library loads). Each call uses one slot and its kernel leaves that slot at
- * zero when it ends. Eager calls rotate through slots 0..127. A call made while
- * `stream` is being captured into a graph takes its slot from 128..255, so a graph
- * keeps a slot of its own (the 128 most recent captures never share one). Two kernels
- * that use the same slot at the same time produce wrong results: at most 128 eager
- * calls may be in flight on one device at once, and one graph's replays must not
- * overlap (HIP orders the launches of one graph). Results do not depend on which
- * workgroup computes which item.
+ * when the library loads); each launch uses one slot and its kernel leaves that slot at
+ * zero when it ends. Results do not depend on which workgroup computes which item.
+ *  - Eager calls rotate through slots 0..127 of the current device. Each slot keeps an
+ *    event recorded after its last launch; when a call finds that launch unfinished,
+ *    it makes `stream` wait for it first (hipStreamWaitEvent), so two kernels never use
+ *    one slot at the same time, whatever the number of calls in flight and of streams.
+ *    The choice of a slot and its event are guarded by a lock: calls from several host
+ *    threads are safe. The events are created on first use and live until the process
+ *    ends.
+ *  - A call made while `stream` is being captured into a graph takes its slot from
+ *    128..255 in turn and records no event (a graph cannot wait for an event recorded
+ *    outside it). A graph's slot is never an eager call's. Unchecked: two replays of
+ *    graphs whose captures took the same slot (captures 128 apart), running at the
+ *    same time on different streams, would split each other's items; the replays of one
+ *    graph are ordered by HIP.
  *
  * Errors: INVALID_ARG (null pointer, size <= 0, bad scale, stride_s < head_dim, a pair
  * table with npairs outside [ceil(nb / 2), nb], element masking with a frame length

@@ -2,9 +2,10 @@
 
 The kernel runs one workgroup per compute unit, and the workgroups take work items from
 atomic counters in a ring of slots in static device memory; every launch must leave its
-slot at zero. These tests check that results stay bit-identical when the ring wraps
-many times, when two streams run the kernel at once, and when the call is captured into
-a graph and replayed between eager calls.
+slot at zero, and a slot is reused only after its last launch has ended. These tests
+check that results stay bit-identical when the ring wraps many times, when two streams
+run the kernel at once, when 300 calls are queued on four streams without waiting, and
+when the call is captured into a graph and replayed between eager calls.
 """
 import pytest
 import torch
@@ -63,6 +64,28 @@ def test_two_streams_at_once():
     for i in range(8):
         assert torch.equal(outs_a[i], ref_a), ("a", i)
         assert torch.equal(outs_b[i], ref_b), ("b", i)
+
+
+def test_three_hundred_launches_on_four_streams():
+    """300 calls queued on four streams with no synchronisation in between: more calls
+    in flight than the ring has eager slots, on streams that do not order each other.
+    Three different problems (each more work items than the grid has workgroups) take
+    turns, so a slot shared by two running kernels would show as wrong output."""
+    probs = [problem(20), problem(21, heads=16, frames=6, tokens=1560, w0=1560, d=128),
+             problem(22, heads=12, frames=5, tokens=1000, w0=300, d=64)]
+    refs = [radial.attn_fwd(*p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    outs = []
+    for i in range(300):
+        p = i % 3
+        out = torch.empty_like(refs[p])
+        with torch.cuda.stream(streams[i % 4]):
+            radial.attn_fwd(*probs[p], out=out)
+        outs.append((p, out))
+    torch.cuda.synchronize()
+    for i, (p, out) in enumerate(outs):
+        assert torch.equal(out, refs[p]), i
 
 
 def test_graph_capture_and_replay():
