@@ -457,9 +457,10 @@ __device__ __forceinline__ void run_item(
   // Work mapping. Item ids are taken by the XCDs round-robin (XCD = id % 8), in id order
   // on each XCD (see radial_fwd_kernel). The ids of one head are contiguous, so the whole
   // chip works on one or two heads at a time and their K/V stays in the shared Infinity
-  // Cache. Inside a head, the ids that land on XCD x take one contiguous run of pairs, in
-  // order, so neighbouring query blocks (which read mostly the same K/V tiles) share that
-  // XCD's L2.
+  // Cache. Inside a head, the ids that land on XCD x take one contiguous run of the pair
+  // table, in order; the host orders the table so that a run holds pairs of nearly
+  // equal length close in the sequence, which walk their lists in step and share that
+  // XCD's L2 (radial_build_pairs).
   const int xcd = pid & 7;
   int seg = 0;  // pairs of this head taken by XCDs 0 .. xcd-1
   for (int y = 0; y < xcd; ++y)

@@ -1,7 +1,8 @@
 """The pair table (radial_build_pairs): which query-block rows the kernel computes together.
 
 A pairing changes no result, only which rows share a workgroup, so these tests check
-that a table is a valid schedule (every row exactly once, pairs ascending), that it is
+that a table is a valid schedule (every row exactly once, a < b in a pair, the pairs
+ordered by union-length band and then by first row), that it is
 deterministic, and that on the radial masks it never makes the shared walk longer than
 the adjacent pairing (2p, 2p + 1). GPU tests check that the output does not depend on
 the table.
@@ -29,11 +30,17 @@ def row_sets(mask):
     return [set(ci[rp[i]:rp[i + 1]].tolist()) for i in range(mask.nb)]
 
 
-def check_partition(table, nb):
+def union_length(rows, a, b):
+    return len(rows[a] | (rows[b] if b >= 0 else set()))
+
+
+def check_partition(table, nb, rows=None):
     t = np.asarray(table).reshape(-1, 2)
     assert (nb + 1) // 2 <= len(t) <= nb
     firsts = t[:, 0]
-    assert np.all(np.diff(firsts) > 0), "pairs sorted by first row"
+    if rows is not None:  # bands of 16 blocks of union length, longest first; then by row
+        key = [(-(union_length(rows, a, b) // 16), a) for a, b in t]
+        assert key == sorted(key), "pairs ordered by union-length band, then first row"
     seconds = t[:, 1]
     assert np.all((seconds == -1) | (seconds > firsts)), "a < b or a single row"
     listed = np.concatenate([firsts, seconds[seconds >= 0]])
@@ -45,8 +52,8 @@ def test_workload_tables_are_valid_and_never_longer_than_adjacent(key):
     wl = WORKLOADS[key]
     m = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0)
     table = m.pairs.numpy()
-    check_partition(table, m.nb)
     rows = row_sets(m)
+    check_partition(table, m.nb, rows)
     adjacent = [(2 * p, 2 * p + 1 if 2 * p + 1 < m.nb else -1) for p in range((m.nb + 1) // 2)]
     assert union_walk(rows, table) <= union_walk(rows, adjacent)
     # Radial masks leave no row alone except the odd one out.
@@ -82,7 +89,7 @@ def test_small_and_odd_sizes(nb):
     ci = np.concatenate(rows + [np.zeros(0, np.int32)])
     for tpf in (0, 256, 1000):
         table = radial.build_pairs(torch.from_numpy(rp), torch.from_numpy(ci), tpf).numpy()
-        check_partition(table, nb)
+        check_partition(table, nb, [set(r.tolist()) for r in rows])
         assert len(table) == (nb + 1) // 2
 
 
