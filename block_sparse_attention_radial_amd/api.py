@@ -51,6 +51,9 @@ _SIGNATURES = {
     "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
         ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_attn_bwd_noalloc": (ctypes.c_int32, [ctypes.c_void_p] * 13 + [
+        ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
+        + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_attn_bwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 11 + [ctypes.c_int32] + [
         ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 5 + [ctypes.c_int64] * 2
         + [ctypes.c_void_p]),
@@ -389,6 +392,49 @@ def _like_q(do: torch.Tensor, q: torch.Tensor) -> torch.Tensor:
     if do.stride() == q.stride() and do.dtype == q.dtype:
         return do
     return torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device).copy_(do)
+
+
+def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     do: torch.Tensor, lse: torch.Tensor, mask: Mask,
+                     scale: float | None = None, element: bool = False, out=None):
+    """attn_bwd through radial_attn_bwd_noalloc: the library allocates nothing (its D_i
+    workspace is static device memory, shared by every call on the device). `out`
+    (optional) is a tuple (dq, dk, dv) of tensors in q's shape and strides; without it
+    they are allocated here. `mask` must already hold its transpose on q's device
+    (Mask.transposed().to(device)), so that this call makes no host work either."""
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, do)):
+        raise ValueError("q, k, v, o, do must share the shape [B, H, n, D]")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, do)):
+        raise TypeError("q, k, v, o, do must be bfloat16")
+    if not q.is_cuda or any(t.device != q.device for t in (k, v, o, do, lse)):
+        raise ValueError("every tensor must be on the same GPU")
+    if any(t.stride() != q.stride() for t in (k, v, o, do)) or q.stride(-1) != 1:
+        raise ValueError("q, k, v, o, do must share strides with a contiguous last axis")
+    B, H, n, D = q.shape
+    if lse.shape != (B, H, n) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [B, H, n] output")
+    if mask.col_ptr is None or mask.row_idx is None or any(
+            t.device != q.device for t in (mask.row_ptr, mask.col_idx, mask.col_ptr,
+                                           mask.row_idx)):
+        raise ValueError("the mask and its transpose must be on q's device")
+    if scale is None:
+        scale = D ** -0.5
+    elem_s, elem_w0, elem_gw = _element_args(mask, element)
+    if out is None:
+        out = tuple(torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+                    for _ in range(3))
+    elif any(t.shape != q.shape or t.stride() != q.stride() or t.dtype != q.dtype
+             or t.device != q.device for t in out):
+        raise ValueError("out must be three tensors in q's shape, strides, dtype and device")
+    dq, dk, dv = out
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check("radial_attn_bwd_noalloc", lib().radial_attn_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), mask.row_ptr.data_ptr(),
+        mask.col_idx.data_ptr(), mask.col_ptr.data_ptr(), mask.row_idx.data_ptr(), mask.nb,
+        float(scale), elem_s, elem_w0, elem_gw, B, H, n, D, q.stride(0), q.stride(1),
+        q.stride(2), stream))
+    return dq, dk, dv
 
 
 class RadialAttentionFunction(torch.autograd.Function):

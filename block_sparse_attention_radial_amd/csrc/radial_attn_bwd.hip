@@ -30,6 +30,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/radial_attn.h"
 #include "radial_device.h"
@@ -486,16 +487,19 @@ int32_t launch_all(const BwdArgs& args, int rows_total, int items, int head_dim,
 
 }  // namespace
 
-extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                                   const void* dout, const float* lse, void* dq, void* dk,
-                                   void* dv, float* delta, const int32_t* row_ptr,
-                                   const int32_t* col_idx, const int32_t* col_ptr,
-                                   const int32_t* row_idx, int32_t nb, float scale,
-                                   int32_t element_tokens_per_frame, int32_t element_w0,
-                                   int32_t element_grid_w, int32_t batch, int32_t heads,
-                                   int32_t seqlen,
-                                   int32_t head_dim, int64_t stride_b, int64_t stride_h,
-                                   int64_t stride_s, void* stream) {
+namespace {
+
+// The uniform backward: checks, then the three kernels. delta is the D_i workspace
+// (caller-owned, or the static scratch of radial_attn_bwd_noalloc); max_rows bounds
+// batch * heads * seqlen (the workspace's size), or is 0 for no bound.
+int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    float* delta, int64_t max_rows, const int32_t* row_ptr,
+                    const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
+                    int32_t nb, float scale, int32_t element_tokens_per_frame,
+                    int32_t element_w0, int32_t element_grid_w, int32_t batch, int32_t heads,
+                    int32_t seqlen, int32_t head_dim, int64_t stride_b, int64_t stride_h,
+                    int64_t stride_s, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta || !row_ptr ||
       !col_idx || !col_ptr || !row_idx)
     return RADIAL_ERR_INVALID_ARG;
@@ -515,6 +519,7 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
   const int64_t rows_total = static_cast<int64_t>(batch) * heads * seqlen;
   if (items > INT32_MAX || rows_total > INT32_MAX || stride_s > (INT32_MAX / 2) / kBlock)
     return RADIAL_ERR_TOO_LARGE;
+  if (max_rows > 0 && rows_total > max_rows) return RADIAL_ERR_TOO_LARGE;
 
   BwdArgs args;
   args.q = static_cast<const __bf16*>(q);
@@ -545,6 +550,77 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
   args.varlen = 0;
   return launch_all(args, static_cast<int>(rows_total), static_cast<int>(items), head_dim,
                     element_tokens_per_frame, element_grid_w, stream);
+}
+
+// radial_attn_bwd_noalloc's workspace: the backward's D_i, one fp32 per row, for at most
+// kScratchRows rows (32 MiB per device, held until the process ends). Host code never
+// uses the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr int64_t kScratchRows = int64_t(1) << 23;
+constexpr int kScratchDevices = 64;
+float* g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[kScratchRows];
+
+namespace {
+
+// The current device's address of `scratch`, looked up on the device's first call.
+int32_t scratch_address(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+    return RADIAL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return RADIAL_ERR_HIP;
+    g_scratch[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return RADIAL_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, void* dq, void* dk,
+                                   void* dv, float* delta, const int32_t* row_ptr,
+                                   const int32_t* col_idx, const int32_t* col_ptr,
+                                   const int32_t* row_idx, int32_t nb, float scale,
+                                   int32_t element_tokens_per_frame, int32_t element_w0,
+                                   int32_t element_grid_w, int32_t batch, int32_t heads,
+                                   int32_t seqlen,
+                                   int32_t head_dim, int64_t stride_b, int64_t stride_h,
+                                   int64_t stride_s, void* stream) {
+  return bwd_uniform(q, k, v, o, dout, lse, dq, dk, dv, delta, 0, row_ptr, col_idx, col_ptr,
+                     row_idx, nb, scale, element_tokens_per_frame, element_w0, element_grid_w,
+                     batch, heads, seqlen, head_dim, stride_b, stride_h, stride_s, stream);
+}
+
+extern "C" int32_t radial_attn_bwd_noalloc(
+    const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv, const int32_t* row_ptr,
+    const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx, int32_t nb,
+    float scale, int32_t element_tokens_per_frame, int32_t element_w0, int32_t element_grid_w,
+    int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim, int64_t stride_b,
+    int64_t stride_h, int64_t stride_s, void* stream) {
+  // Sizes first, so that an input past the workspace is refused before any HIP call.
+  if (batch > 0 && heads > 0 && seqlen > 0 &&
+      static_cast<int64_t>(batch) * heads * seqlen > kScratchRows)
+    return RADIAL_ERR_TOO_LARGE;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !row_ptr || !col_idx ||
+      !col_ptr || !row_idx)
+    return RADIAL_ERR_INVALID_ARG;
+  float* delta = nullptr;
+  const int32_t err = scratch_address(&delta);
+  if (err != RADIAL_OK) return err;
+  return bwd_uniform(q, k, v, o, dout, lse, dq, dk, dv, delta, kScratchRows, row_ptr, col_idx,
+                     col_ptr, row_idx, nb, scale, element_tokens_per_frame, element_w0,
+                     element_grid_w, batch, heads, seqlen, head_dim, stride_b, stride_h,
+                     stride_s, stream);
 }
 
 extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v,

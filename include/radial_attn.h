@@ -370,6 +370,33 @@ int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream);
 
 /*
+ * radial_attn_bwd_noalloc — radial_attn_bwd without the delta workspace argument, for
+ * callers that cannot allocate device memory: code under graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The call allocates nothing: its D_i workspace
+ * is a static device array of the library, 2^23 fp32 values (32 MiB) on each device
+ * the library runs on, held until the process ends.
+ *
+ * Arguments, results and numerics are radial_attn_bwd's (the same kernels), without
+ * `delta`. The workspace keeps the last call's values; nothing needs to start at zero.
+ * Every call on one device shares that device's workspace, so two calls that overlap
+ * on one device (on different streams, or graph replays running at once) race and give
+ * wrong gradients; calls on one stream are ordered and safe.
+ *
+ * Errors: as radial_attn_bwd, plus TOO_LARGE when batch * heads * seqlen exceeds 2^23
+ * (the workspace), checked before any HIP call; HIP also when the workspace's device
+ * address cannot be looked up.
+ */
+int32_t radial_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk,
+                                void* dv, const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* col_ptr, const int32_t* row_idx, int32_t nb,
+                                float scale, int32_t element_tokens_per_frame,
+                                int32_t element_w0, int32_t element_grid_w, int32_t batch,
+                                int32_t heads, int32_t seqlen, int32_t head_dim,
+                                int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                                void* stream);
+
+/*
  * radial_attn_bwd_varlen — radial_attn_bwd over a packed varlen batch (the backward of
  * radial_attn_fwd_varlen). The call is asynchronous on `stream`.
  *

@@ -175,6 +175,16 @@ void attention_checks() {
   expect(radial_attn_bwd_varlen(p, p, p, p, p, lse, p, p, p, lse, tokens, 2, ip, ip, ip, ip, 0.1f,
                                 0, 0, 0, 1, 128, 128, 128, nullptr) == RADIAL_ERR_HIP,
          "bwd varlen no GPU");
+  // radial_attn_bwd_noalloc: a shape past its static workspace, then a valid one.
+  expect(radial_attn_bwd_noalloc(p, p, p, p, p, lse, p, p, p, ip, ip, ip, ip, 2048, 0.1f, 0, 0,
+                                 0, 1, 33, 1 << 18, 128, 0, 0, 128, nullptr) ==
+             RADIAL_ERR_TOO_LARGE, "bwd noalloc size");
+  expect(radial_attn_bwd_noalloc(p, p, p, p, p, lse, p, p, p, nullptr, ip, ip, ip, 8, 0.1f, 0, 0,
+                                 0, 1, 1, 1000, 128, 0, 0, 128, nullptr) ==
+             RADIAL_ERR_INVALID_ARG, "bwd noalloc null");
+  expect(radial_attn_bwd_noalloc(p, p, p, p, p, lse, p, p, p, ip, ip, ip, ip, 8, 0.1f, 0, 0, 0, 1,
+                                 1, 1000, 128, 0, 0, 128, nullptr) == RADIAL_ERR_HIP,
+         "bwd noalloc no GPU");
   for (int32_t code = -8; code <= 1; ++code) expect(radial_error_string(code) != nullptr, "text");
 }
 

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         ["radial_mask_dims", "radial_build_mask", "radial_mask_dims_grid",
          "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd", "radial_attn_fwd_rule",
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
-         "radial_attn_bwd_varlen", "radial_attn_fwd_varlen_rule",
+         "radial_attn_bwd_varlen", "radial_attn_fwd_varlen_rule", "radial_attn_bwd_noalloc",
          "radial_error_string"])
 
 
