@@ -267,47 +267,63 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
     lds_barrier();     // every wave's part landed; tile t-1 is no longer read
     if (t + 1 < L) copy_tile(t + 1);
     const int kb = column(t);
-    if (static_cast<unsigned>(kb) >= static_cast<unsigned>(nb)) continue;
+    // A column outside [0, nb) was copied as zeros; every one of its keys is masked as
+    // padding (n_eff = its first token), so it adds nothing. No branch skips it: a second
+    // path through the loop would make the compiler copy dQ between register files.
+    const bool valid = static_cast<unsigned>(kb) < static_cast<unsigned>(nb);
+    const int n_eff = valid ? n : kb * kBlock;
     const char* const kt = kb0 + (t & 1) * T::kBytes;
     const char* const vt = vb0 + (t & 1) * T::kBytes;
 
-    // S^T = K Q^T and dP^T = V dO^T (keys on M, this wave's queries on N).
-    f32x16 sacc[4], pacc[4];
+    // The tile in two halves of 64 keys, so that only half of S^T and dP^T is live.
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      bf16x8 kf[4], vf[4];
-      read_rows<D>(kt + rbase, rx, s, kf);
-      read_rows<D>(vt + rbase, rx, s, vf);
+    for (int h = 0; h < 2; ++h) {
+      // S^T = K Q^T and dP^T = V dO^T for keys 64h .. 64h + 63 (keys on M, this wave's
+      // queries on N).
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            kf[g], __builtin_bit_cast(bf16x8, qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
-        pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            vf[g], __builtin_bit_cast(bf16x8, gf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 kf[2], vf[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int off = rbase + (2 * h + g) * 32 * T::kRowBytes + ((s << 5) ^ rx);
+          kf[g] = *reinterpret_cast<const bf16x8*>(kt + off);
+          vf[g] = *reinterpret_cast<const bf16x8*>(vt + off);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              kf[g], __builtin_bit_cast(bf16x8, qf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+          pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              vf[g], __builtin_bit_cast(bf16x8, gf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
+        }
       }
-    }
-    if (n - kb * kBlock < kBlock) pad_mask_tile(kb * kBlock, n, lane, sacc);
-    if constexpr (E != 0)
-      element_mask_any<E>(q0 + 32 * wi, kb * kBlock, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane, sacc);
+      const int key0 = kb * kBlock + 64 * h;
+      if (n_eff - key0 < 64) pad_mask_tile<2>(key0, n_eff, lane, sacc);
+      if constexpr (E != 0)
+        if (valid)
+          element_mask_any<E, 2>(q0 + 32 * wi, key0, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane,
+                                 sacc);
 
-    // Per step u of 16 keys: P^T = 2^(c s - lse2) and dS^T = P^T (dP^T - D), packed as
-    // the B operand of dQ^T += K^T dS^T (d on M, queries on N, keys contracted in
-    // accumulator order), whose MFMAs are issued right away: they run while the VALU
-    // works on step u + 1.
+      // Per step u of 16 keys: P^T = 2^(c s - lse2) and dS^T = P^T (dP^T - D), packed as
+      // the B operand of dQ^T += K^T dS^T (d on M, queries on N, keys contracted in
+      // accumulator order), whose MFMAs are issued right away: they run while the VALU
+      // works on step u + 1.
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int g = u >> 1, s2 = u & 1;
-      f32x8 d8;
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const int g = u2 >> 1, s2 = u2 & 1;
+        f32x8 d8;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + jj], a.c, -lse2));
-        d8[jj] = p * (pacc[g][8 * s2 + jj] - dlt);
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + jj], a.c, -lse2));
+          d8[jj] = p * (pacc[g][8 * s2 + jj] - dlt);
+        }
+        const bf16x8 dsk = __builtin_convertvector(d8, bf16x8);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              read_tr<D>(kt, tb0, tx0, tb1, tx1, 4 * h + u2, db), dsk, dq[db], 0, 0, 0);
       }
-      const bf16x8 dsk = __builtin_convertvector(d8, bf16x8);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kt, tb0, tx0, tb1, tx1, u, db),
-                                                         dsk, dq[db], 0, 0, 0);
     }
   }
   if (qrow < n) store_rows<D>(a.dq + base + static_cast<int64_t>(qrow) * a.stride_s, dq, a.scale, hl);
@@ -387,67 +403,82 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const B
     lds_barrier();
     if (t + 1 < L) copy_tile(t + 1);
     const int qb = qblock(t);
-    if (static_cast<unsigned>(qb) >= static_cast<unsigned>(nb)) continue;
+    // A row block outside [0, nb) was copied as zeros; all of its queries are masked as
+    // padding (see the dQ kernel: no second path through the loop).
+    const bool valid = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
+    const int n_eff = valid ? n : qb * kBlock;
     const char* const qt = qb0 + (t & 1) * T::kBytes;
     const char* const gt = gb0 + (t & 1) * T::kBytes;
     const float* const lt = reinterpret_cast<const float*>(lb0 + (t & 1) * 1024);
     const float* const dt = reinterpret_cast<const float*>(db0 + (t & 1) * 1024);
 
-    // S = Q K^T and dP = dO V^T (queries on M, this wave's keys on N).
-    f32x16 sacc[4], pacc[4];
+    // The tile in two halves of 64 queries, so that only half of S and dP is live.
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      bf16x8 qf[4], gf[4];
-      read_rows<D>(qt + rbase, rx, s, qf);
-      read_rows<D>(gt + rbase, rx, s, gf);
+    for (int h = 0; h < 2; ++h) {
+      // S = Q K^T and dP = dO V^T for queries 64h .. 64h + 63 (queries on M, this
+      // wave's keys on N).
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            qf[g], __builtin_bit_cast(bf16x8, kf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
-        pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            gf[g], __builtin_bit_cast(bf16x8, vf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
-      }
-    }
-    // Entries are queries here: padding rows and the element rule mask them.
-    if (n - qb * kBlock < kBlock) pad_mask_tile(qb * kBlock, n, lane, sacc);
-    if constexpr (E != 0)
-      element_mask_any<E>(k0 + 32 * wi, qb * kBlock, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane, sacc);
-
-    // P = 2^(c s - lse2) and dS = P (dP - D), per entry (query 32g + 8(e/4) + 4hl + e%4),
-    // packed as the B operands of dV^T and dK^T. (Issuing each step's MFMAs right after
-    // its P and dS, as the dQ kernel does, measured 7% slower here: this kernel holds
-    // every register, and the compiler then schedules worse.)
-    bf16x8 pk[8], dsk[8];
+      for (int s = 0; s < NS; ++s) {
+        bf16x8 qf[2], gf[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int g = u >> 1, s2 = u & 1;
-      f32x8 p8, d8;
+        for (int g = 0; g < 2; ++g) {
+          const int off = rbase + (2 * h + g) * 32 * T::kRowBytes + ((s << 5) ^ rx);
+          qf[g] = *reinterpret_cast<const bf16x8*>(qt + off);
+          gf[g] = *reinterpret_cast<const bf16x8*>(gt + off);
+        }
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qi = 32 * g + 8 * (2 * s2 + half) + 4 * hl;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + qi);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + qi);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 8 * s2 + 4 * half + r;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[g][e], a.c, -l4[r] * kLog2e));
-          p8[4 * half + r] = p;
-          d8[4 * half + r] = p * (pacc[g][e] - d4[r]);
+        for (int g = 0; g < 2; ++g) {
+          sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              qf[g], __builtin_bit_cast(bf16x8, kf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+          pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              gf[g], __builtin_bit_cast(bf16x8, vf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
         }
       }
-      pk[u] = __builtin_convertvector(p8, bf16x8);
-      dsk[u] = __builtin_convertvector(d8, bf16x8);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (d on M, keys on N, queries contracted).
+      // Entries are queries here: padding rows and the element rule mask them.
+      const int row0 = qb * kBlock + 64 * h;
+      if (n_eff - row0 < 64) pad_mask_tile<2>(row0, n_eff, lane, sacc);
+      if constexpr (E != 0)
+        if (valid)
+          element_mask_any<E, 2>(k0 + 32 * wi, row0, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane,
+                                 sacc);
+
+      // P = 2^(c s - lse2) and dS = P (dP - D), per entry (query 64h + 32g + 8(e/4) +
+      // 4hl + e%4), packed as the B operands of dV^T and dK^T. (Issuing each step's MFMAs
+      // right after its P and dS, as the dQ kernel does, measured slower here.)
+      bf16x8 pk[4], dsk[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const int g = u2 >> 1, s2 = u2 & 1;
+        f32x8 p8, d8;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(gt, tb0, tx0, tb1, tx1, u, db),
-                                                         pk[u], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(qt, tb0, tx0, tb1, tx1, u, db),
-                                                         dsk[u], dk[db], 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+          const int qi = 64 * h + 32 * g + 8 * (2 * s2 + half) + 4 * hl;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + qi);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + qi);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 8 * s2 + 4 * half + r;
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[g][e], a.c, -l4[r] * kLog2e));
+            p8[4 * half + r] = p;
+            d8[4 * half + r] = p * (pacc[g][e] - d4[r]);
+          }
+        }
+        pk[u2] = __builtin_convertvector(p8, bf16x8);
+        dsk[u2] = __builtin_convertvector(d8, bf16x8);
       }
+      // dV^T += dO^T P and dK^T += Q^T dS (d on M, keys on N, queries contracted).
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int u = 4 * h + u2;
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              read_tr<D>(gt, tb0, tx0, tb1, tx1, u, db), pk[u2], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              read_tr<D>(qt, tb0, tx0, tb1, tx1, u, db), dsk[u2], dk[db], 0, 0, 0);
+        }
+    }
   }
   if (krow < n) {
     const int64_t off = base + static_cast<int64_t>(krow) * a.stride_s;

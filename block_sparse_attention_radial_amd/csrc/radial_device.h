@@ -260,9 +260,13 @@ __device__ __forceinline__ uint32_t run_bits(int lo, int hi) {
 // [lo_b, hi_b]. Per group of 32 entries the runs become a 32-bit mask; each entry then
 // takes its bit as 0 or all ones (v_bfe_i32) and selects its score or -inf with it
 // (v_bfi_b32): two VALU instructions and no lane masks. A tile that every lane of the
-// wave keeps whole is left alone.
+// wave keeps whole is left alone. NG is the number of 32-entry groups the lane holds: 4
+// for a whole tile (entries c < 128), 2 for the first or second half of one (c < 64,
+// with ent0 the half's first token).
+template <int NG = 4>
 __device__ __forceinline__ void element_mask_tile(int own0, int ent0, int S, int ew0m1, int lane,
-                                                  f32x16 (&sacc)[4]) {
+                                                  f32x16 (&sacc)[NG]) {
+  constexpr int kLast = 32 * NG - 4;  // one past the lane's last entry position c
   // S and own0 go through an empty asm so that what is derived from them is recomputed
   // here, per tile, rather than held in registers across the caller's loop.
   asm volatile("" : "+s"(S), "+s"(own0));
@@ -285,11 +289,11 @@ __device__ __forceinline__ void element_mask_tile(int own0, int ent0, int S, int
   const int base = sq - ks;  // c of the entry at the lane's own spatial index, frame kf
   const int lo_a = max(base - ra, 0), hi_a = min(base + ra, cut - 1);
   const int lo_b = max(base + S - rb, cut), hi_b = base + S + rb;
-  const bool full = lo_a <= 0 && hi_a >= min(cut, 124) - 1 &&
-                    (cut >= 124 || (lo_b <= cut && hi_b >= 123));
+  const bool full = lo_a <= 0 && hi_a >= min(cut, kLast) - 1 &&
+                    (cut >= kLast || (lo_b <= cut && hi_b >= kLast - 1));
   if (__builtin_amdgcn_ballot_w64(!full) == 0) return;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < NG; ++g) {
     const uint32_t bits = run_bits(lo_a - 32 * g, hi_a - 32 * g) |
                           run_bits(lo_b - 32 * g, hi_b - 32 * g);
 #pragma unroll
@@ -311,10 +315,13 @@ __device__ __forceinline__ void element_mask_tile(int own0, int ent0, int S, int
 // [x - t, x + t], t = r(f) - |y_own - y|, which is one run of tile positions. The runs
 // go into the lane's four 32-bit words and are applied as there. There are at most
 // ceil(128 / W) + 1 segments; a frame ends at a row end, so frames add none. Divisions
-// use the float reciprocal with one correction (all indices are below 2^21).
+// use the float reciprocal with one correction (all indices are below 2^21). NG as for
+// element_mask_tile.
+template <int NG = 4>
 __device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S, int W,
                                                        int ew0m1, int lane,
-                                                       f32x16 (&sacc)[4]) {
+                                                       f32x16 (&sacc)[NG]) {
+  constexpr int kEntries = 32 * NG;
   asm volatile("" : "+s"(S), "+s"(W), "+s"(own0));
   const float inv_s = __builtin_amdgcn_rcpf(static_cast<float>(S));
   const float inv_w = __builtin_amdgcn_rcpf(static_cast<float>(W));
@@ -326,9 +333,9 @@ __device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S
   div_frame(sk, W, inv_w, yk, x0);
   int row_end = sk - x0 + W;  // in-frame index one past the segment's row
   const int sh = 4 * (lane >> 5);  // this lane's entries sit sh positions later
-  uint32_t bits[4] = {0u, 0u, 0u, 0u};
-  for (int c = 0; c < kBlock;) {
-    const int len = min(W - x0, kBlock - c);
+  uint32_t bits[NG] = {};
+  for (int c = 0; c < kEntries;) {
+    const int len = min(W - x0, kEntries - c);
     const int d = fq > fk ? fq - fk : fk - fq;
     const int r = min(ew0m1 >> (31 - __builtin_clz(static_cast<unsigned>(d) + 1u)), kMaxReach);
     const int t = r - (yq > yk ? yq - yk : yk - yq);
@@ -337,7 +344,7 @@ __device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S
     const int lo = max(c + xq - t - x0, c) - sh;
     const int hi = min(c + xq + t - x0, c + len - 1) - sh;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < NG; ++g)
       if (c <= 32 * g + 35 && c + len > 32 * g)  // the words the segment can reach
         bits[g] |= run_bits(lo - 32 * g, hi - 32 * g);
     c += len;
@@ -351,10 +358,13 @@ __device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S
     }
   }
   const uint32_t mine = 0x0f0f0f0fu;  // the bits of this lane's 16 entries of a word
-  const bool full = (bits[0] & bits[1] & bits[2] & bits[3] & mine) == mine;
+  uint32_t all = mine;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) all &= bits[g];
+  const bool full = all == mine;
   if (__builtin_amdgcn_ballot_w64(!full) == 0) return;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < NG; ++g) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t keep = static_cast<uint32_t>(
@@ -366,25 +376,26 @@ __device__ __forceinline__ void element_mask_grid_tile(int own0, int ent0, int S
 
 // Element masking of a tile: E = 1 takes the 1-D distance, E = 2 the grid distance with
 // grid width gw.
-template <int E>
+template <int E, int NG = 4>
 __device__ __forceinline__ void element_mask_any(int own0, int ent0, int S, int gw, int ew0m1,
-                                                 int lane, f32x16 (&sacc)[4]) {
+                                                 int lane, f32x16 (&sacc)[NG]) {
   if constexpr (E == 2)
-    element_mask_grid_tile(own0, ent0, S, gw, ew0m1, lane, sacc);
+    element_mask_grid_tile<NG>(own0, ent0, S, gw, ew0m1, lane, sacc);
   else
-    element_mask_tile(own0, ent0, S, ew0m1, lane, sacc);
+    element_mask_tile<NG>(own0, ent0, S, ew0m1, lane, sacc);
 }
 
 // Padding of the entries of a tile in accumulator layout: entry (g, e) of a lane is
-// token ent0 + 4 hl + 32g + 8(e/4) + e%4, and tokens at or past n get -inf. Applied
+// token ent0 + 4 hl + 32g + 8(e/4) + e%4 (g < NG), and tokens at or past n get -inf. Applied
 // arithmetically, min(s, +inf or -inf), so that the 64 tests need no lane masks; the
 // per-group base goes through an empty asm so that the compiler does not fold the 64
 // offsets into 64 scalar-register constants (the remaining offsets, 0 .. 27, are inline
 // operands).
-__device__ __forceinline__ void pad_mask_tile(int ent0, int n, int lane, f32x16 (&sacc)[4]) {
+template <int NG = 4>
+__device__ __forceinline__ void pad_mask_tile(int ent0, int n, int lane, f32x16 (&sacc)[NG]) {
   const int lim = n - ent0 - 4 * (lane >> 5);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < NG; ++g) {
     int base = lim - 1 - 32 * g;
     asm volatile("" : "+v"(base));
 #pragma unroll
