@@ -20,8 +20,10 @@
 //     on M, keys on N, Q and dO rows from LDS, K and V in registers), P and dS, then
 //     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from transposing LDS reads.
 // A workgroup is four wave64, one per SIMD; wave i owns rows (dq) or keys (dkdv)
-// 32i .. 32i+31 of its block. Tiles are copied HBM/L2 -> LDS with LDS-DMA into two
-// buffers: tile t+1 is in flight while tile t is used. Accumulation is fp32; P and dS
+// 32i .. 32i+31 of its block. Tiles are copied HBM/L2 -> LDS with LDS-DMA. dkdv runs one
+// workgroup per CU and double-buffers its tiles (tile t+1 is in flight while tile t is
+// used); dq runs two workgroups per CU with single buffers, and each SIMD interleaves
+// the two workgroups' waves. Accumulation is fp32; P and dS
 // enter the MFMAs as bf16. Padding (rows or keys at or past n) and element masking work
 // as in the forward.
 #include <hip/hip_runtime.h>
@@ -204,13 +206,18 @@ __device__ __forceinline__ void store_rows(__bf16* dst_row, const f32x16 (&acc)[
 }
 
 // ---- 2. dQ ----
+// Two workgroups share a CU (64 KiB of LDS and at most 256 registers per wave each), so
+// each SIMD runs two dQ waves from different workgroups and interleaves them: while one
+// waits for its tile copy or works through its VALU steps, the other issues MFMAs. The
+// K and V tiles are therefore single-buffered: tile t + 1 is copied after every wave
+// is done with tile t.
 template <int D, int E>
-__global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const BwdArgs a) {
   using T = Tile<D>;
   constexpr int NDB = D / 32, NS = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::kBytes];
   char* const kb0 = smem;
-  char* const vb0 = smem + 2 * T::kBytes;
+  char* const vb0 = smem + T::kBytes;
 
   const BwdGeometry geo = bwd_geometry(a, blockIdx.x);
   const int nb = geo.nb, n = geo.n, qb = geo.blk;
@@ -241,9 +248,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
   auto copy_tile = [&](int t) {
     const int kb = column(t);
     const bool on = static_cast<unsigned>(kb) < static_cast<unsigned>(nb);
-    const int buf = (t & 1) * T::kBytes;
-    const Stage<D> sk = stage_rows<D>(kb0 + buf, kh, kb * kBlock, n, row_bytes, wi, on);
-    const Stage<D> sv = stage_rows<D>(vb0 + buf, vh, kb * kBlock, n, row_bytes, wi, on);
+    const Stage<D> sk = stage_rows<D>(kb0, kh, kb * kBlock, n, row_bytes, wi, on);
+    const Stage<D> sv = stage_rows<D>(vb0, vh, kb * kBlock, n, row_bytes, wi, on);
 #pragma unroll
     for (int i = 0; i < T::kCopiesPerWave; ++i) {
       stage_issue<D>(sk, copy_off, i);
@@ -264,16 +270,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
 
   for (int t = 0; t < L; ++t) {
     wait_copies<0>();  // this wave's part of tile t
-    lds_barrier();     // every wave's part landed; tile t-1 is no longer read
-    if (t + 1 < L) copy_tile(t + 1);
+    lds_barrier();     // every wave's part landed
     const int kb = column(t);
     // A column outside [0, nb) was copied as zeros; every one of its keys is masked as
     // padding (n_eff = its first token), so it adds nothing. No branch skips it: a second
     // path through the loop would make the compiler copy dQ between register files.
     const bool valid = static_cast<unsigned>(kb) < static_cast<unsigned>(nb);
     const int n_eff = valid ? n : kb * kBlock;
-    const char* const kt = kb0 + (t & 1) * T::kBytes;
-    const char* const vt = vb0 + (t & 1) * T::kBytes;
+    const char* const kt = kb0;
+    const char* const vt = vb0;
 
     // The tile in two halves of 64 keys, so that only half of S^T and dP^T is live.
 #pragma unroll
@@ -325,6 +330,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dq_kernel(const Bwd
               read_tr<D>(kt, tb0, tx0, tb1, tx1, 4 * h + u2, db), dsk, dq[db], 0, 0, 0);
       }
     }
+    lds_barrier();  // every wave is done with tile t
+    if (t + 1 < L) copy_tile(t + 1);
   }
   if (qrow < n) store_rows<D>(a.dq + base + static_cast<int64_t>(qrow) * a.stride_s, dq, a.scale, hl);
 }
