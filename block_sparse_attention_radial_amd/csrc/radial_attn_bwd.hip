@@ -76,6 +76,8 @@ struct BwdArgs {
   BwdSample plan[kMaxBwdVarlen];
 };
 typedef __attribute__((address_space(4))) const BwdArgs* BwdArgsPtr;
+typedef __attribute__((address_space(4))) const int32_t ConstI32;
+typedef __attribute__((address_space(3))) volatile int LdsFlag;
 
 // Where a dq or dkdv workgroup works: the (batch, head) element offset, its rows of lse
 // and delta, its mask rows (row_ptr / col_ptr point at its sample's), its sequence length
@@ -337,160 +339,291 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
 }
 
 // ---- 3. dK, dV ----
+// Eight waves in two roles over the block's 128 keys. Waves 0-3 (the P side) hold K as
+// MFMA B operands, compute S = Q K^T and P, and accumulate dV^T += dO^T P; waves 4-7 (the
+// dS side) hold V, compute dP = dO V^T, and accumulate dK^T += Q^T dS with
+// dS = P (dP - D). Waves i and i + 4 share SIMD i and keys 32i .. 32i + 31, so each SIMD
+// runs two waves whose VALU and MFMA work interleave, and neither needs more than half
+// of the SIMD's registers. P goes from the P side to the dS side through LDS, as the
+// bf16 values that also enter dV's MFMAs.
+//
+// The query tiles of the column are walked in halves of 64 queries, one half per phase,
+// with one workgroup barrier between phases. In phase p the P side finishes dV for half
+// p - 1 (P kept in registers) and computes S and P of half p, which it writes to the
+// exchange buffer; the dS side reads P of half p - 1 from that buffer, finishes dK for
+// it, and computes dP of half p. The dS wave of a SIMD marks in an LDS word when it has
+// read the buffer, and the P wave waits for that mark before writing the next half
+// (the dS wave reads first thing after the barrier, so the wait is normally already
+// over). Q and dO halves, with the lse and D of their 64 queries, sit in a ring of four
+// slots: phase p reads halves p - 1 and p, and copies half p + 2, two phases ahead of
+// its use.
+constexpr int kDkdvThreads = 512;
+
+template <int D>
+struct DkdvLds {
+  static constexpr int kHalfBytes = 64 * D * 2;             // 64 rows of Q or dO
+  static constexpr int kCopies = kHalfBytes / 1024 / 4;     // per P-side wave and operand
+  static constexpr int kLse = 2 * kHalfBytes;               // then 64 lse, then 64 D
+  static constexpr int kSlot = 2 * kHalfBytes + 512;
+  static constexpr int kExchange = 4 * kSlot;               // P: 64 queries x 128 keys, bf16
+  static constexpr int kFlags = kExchange + 16384;          // one word per SIMD
+  static constexpr int kBytes = kFlags + 16;
+  static_assert(kCopies * 4 * 1024 == kHalfBytes, "four waves' copies must cover a half");
+  static_assert(kSlot % 256 == 0, "slots keep the bank swizzle");
+};
+
+// One 256-byte copy instruction: lane l's 4 bytes at byte_offset land at lds + 4 l
+// (buffer_load_dword ... lds), ordered like copy_1k.
+__device__ __forceinline__ void copy_256(const i32x4& desc, uint32_t lds, int byte_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(byte_offset), "s"(desc)
+               : "memory");
+}
+
 template <int D, int E>
-__global__ __launch_bounds__(kBwdThreads, 1) void radial_bwd_dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const BwdArgs a) {
   using T = Tile<D>;
+  using M = DkdvLds<D>;
   constexpr int NDB = D / 32, NS = D / 16;
-  // Q and dO tiles (two of each), then lse and D of the tile's 128 queries (two of each,
-  // 1 KiB apiece: one 1 KiB copy writes 128 values and zeros after them).
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + 4 * 1024];
-  char* const qb0 = smem;
-  char* const gb0 = smem + 2 * T::kBytes;
-  char* const lb0 = smem + 4 * T::kBytes;          // lse, buffers 0 and 1
-  char* const db0 = smem + 4 * T::kBytes + 2048;   // D, buffers 0 and 1
+  __shared__ __attribute__((aligned(1024))) char smem[M::kBytes];
+  char* const xb = smem + M::kExchange;
+  // (An LDS pointer: through a generic one the volatile accesses become flat memory
+  // operations, whose waits include the tile copies in flight.)
+  LdsFlag* const flags = (LdsFlag*)(smem + M::kFlags);
 
   const BwdGeometry geo = bwd_geometry(a, blockIdx.x);
   const int nb = geo.nb, n = geo.n, kb = geo.blk;
   const int64_t base = geo.base;
   const int tid = threadIdx.x, lane = tid & 63, lq = lane & 31, hl = lane >> 5;
-  const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = w & 3;  // key slice (and SIMD)
   const int row_bytes = a.stride_s * 2;
   const int k0 = kb * kBlock;
   const int krow = k0 + 32 * wi + lq;
   const char* const qh = reinterpret_cast<const char*>(a.q + base);
   const char* const gh = reinterpret_cast<const char*>(a.g + base);
-  const float* const lse_bh = geo.lse;
-  const float* const dl_bh = geo.delta;
 
-  int copy_off[T::kOffsetPeriod];
-  copy_offsets<D>(wi, lane, row_bytes, copy_off);
+  // Lane offsets of a P-side wave's share of a half copy: KiB wi * kCopies + i of the
+  // half, lane l's 16 bytes at chunk position p of row r, holding global chunk p ^ swz(r).
+  int copy_off[M::kCopies];
+#pragma unroll
+  for (int i = 0; i < M::kCopies; ++i) {
+    const int ci = (wi * M::kCopies + i) * 64 + lane;
+    const int row = ci / T::kChunks, pos = ci % T::kChunks;
+    copy_off[i] = row * row_bytes + ((pos ^ swz<D>(row)) << 4);
+  }
   int rbase, rx, tb0, tx0, tb1, tx1;
   row_read_offsets<D>(lane, rbase, rx);
   tr_read_offsets<D>(lane, tb0, tx0, tb1, tx1);
 
   const int c0 = geo.col_ptr[kb];
   const int L = geo.col_ptr[kb + 1] - c0;
-  auto qblock = [&](int t) { return __builtin_amdgcn_readfirstlane(a.row_idx[c0 + t]); };
-  auto copy_tile = [&](int t) {
+  const int halves = 2 * L;
+  // The column's row blocks, read through the constant address space so that the
+  // compiler uses scalar loads: a vector load would be waited for with vmcnt(0), which
+  // also waits for the tile copies in flight.
+  ConstI32* const rows_of = (ConstI32*)(a.row_idx + c0);
+  auto qblock = [&](int t) { return rows_of[t]; };
+  auto slot = [&](int j) { return smem + (j & 3) * M::kSlot; };
+  // Copy half j (query tile j / 2, rows 64 (j % 2) ..) into its slot; the P-side waves
+  // issue the copies (the dS side is the longer path through a phase), wave 0 also copies
+  // the half's lse and wave 1 its D, one instruction more per half.
+  auto copy_half = [&](int j) {
+    const int t = j >> 1, h = j & 1;
     const int qb = qblock(t);
     const bool on = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
-    const int buf = (t & 1) * T::kBytes;
-    const Stage<D> sq = stage_rows<D>(qb0 + buf, qh, qb * kBlock, n, row_bytes, wi, on);
-    const Stage<D> sg = stage_rows<D>(gb0 + buf, gh, qb * kBlock, n, row_bytes, wi, on);
+    const int row0 = on ? qb * kBlock + 64 * h : 0;
+    const int left = n - row0;
+    // (readfirstlane: the compiler clamps with a vector instruction, and the descriptors
+    // built from this must be scalar.)
+    const int rows = __builtin_amdgcn_readfirstlane(on ? (left < 64 ? (left > 0 ? left : 0) : 64) : 0);
+    const int bytes = rows > 0 ? (rows - 1) * row_bytes + T::kRowBytes : 0;
+    const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)slot(j)));
+    const uint32_t dst = sb + wi * M::kCopies * 1024;
+    const i32x4 dq_ = raw_descriptor(qh + static_cast<int64_t>(row0) * row_bytes, bytes);
+    const i32x4 dg_ = raw_descriptor(gh + static_cast<int64_t>(row0) * row_bytes, bytes);
 #pragma unroll
-    for (int i = 0; i < T::kCopiesPerWave; ++i) {
-      stage_issue<D>(sq, copy_off, i);
-      stage_issue<D>(sg, copy_off, i);
+    for (int i = 0; i < M::kCopies; ++i) {
+      copy_1k(dq_, dst + i * 1024, copy_off[i]);
+      copy_1k(dg_, dst + M::kHalfBytes + i * 1024, copy_off[i]);
     }
-    if (wi == 0) {  // lse and D of the 128 queries: 512 bytes each
-      const int rows = on ? (n - qb * kBlock < kBlock ? n - qb * kBlock : kBlock) : 0;
-      const int q0 = on ? qb * kBlock : 0;
-      const uint32_t lb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lb0)) +
-                          (t & 1) * 1024;
-      const uint32_t dbv = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)db0)) +
-                           (t & 1) * 1024;
-      copy_1k(raw_descriptor(reinterpret_cast<const char*>(lse_bh + q0), rows * 4), lb, lane * 16);
-      copy_1k(raw_descriptor(reinterpret_cast<const char*>(dl_bh + q0), rows * 4), dbv, lane * 16);
+    if (w < 2) {
+      const float* src = (w == 0 ? geo.lse : geo.delta) + row0;
+      copy_256(raw_descriptor(reinterpret_cast<const char*>(src), rows * 4),
+               sb + M::kLse + w * 256, lane * 4);
     }
   };
-  if (L > 0) copy_tile(0);
-
-  // K and V as MFMA B operands: d = 16s + 8hl .. +7 of this lane's key.
-  u32x4 kf[NS], vf[NS];
-  load_b_operand<D>(a.k + base, k0, n, row_bytes, 32 * wi + lq, hl, kf);
-  load_b_operand<D>(a.v + base, k0, n, row_bytes, 32 * wi + lq, hl, vf);
-  __builtin_amdgcn_s_waitcnt(0);
-
-  f32x16 dk[NDB], dv[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) dk[i] = dv[i] = f32x16{};
-
-  for (int t = 0; t < L; ++t) {
-    wait_copies<0>();
-    lds_barrier();
-    if (t + 1 < L) copy_tile(t + 1);
-    const int qb = qblock(t);
-    // A row block outside [0, nb) was copied as zeros; all of its queries are masked as
-    // padding (see the dQ kernel: no second path through the loop).
-    const bool valid = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
-    const int n_eff = valid ? n : qb * kBlock;
-    const char* const qt = qb0 + (t & 1) * T::kBytes;
-    const char* const gt = gb0 + (t & 1) * T::kBytes;
-    const float* const lt = reinterpret_cast<const float*>(lb0 + (t & 1) * 1024);
-    const float* const dt = reinterpret_cast<const float*>(db0 + (t & 1) * 1024);
-
-    // The tile in two halves of 64 queries, so that only half of S and dP is live.
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // S = Q K^T and dP = dO V^T for queries 64h .. 64h + 63 (queries on M, this
-      // wave's keys on N).
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        bf16x8 qf[2], gf[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int off = rbase + (2 * h + g) * 32 * T::kRowBytes + ((s << 5) ^ rx);
-          qf[g] = *reinterpret_cast<const bf16x8*>(qt + off);
-          gf[g] = *reinterpret_cast<const bf16x8*>(gt + off);
-        }
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              qf[g], __builtin_bit_cast(bf16x8, kf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
-          pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              gf[g], __builtin_bit_cast(bf16x8, vf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
-        }
-      }
-      // Entries are queries here: padding rows and the element rule mask them.
-      const int row0 = qb * kBlock + 64 * h;
-      if (n_eff - row0 < 64) pad_mask_tile<2>(row0, n_eff, lane, sacc);
-      if constexpr (E != 0)
-        if (valid)
-          element_mask_any<E, 2>(k0 + 32 * wi, row0, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane,
-                                 sacc);
-
-      // P = 2^(c s - lse2) and dS = P (dP - D), per entry (query 64h + 32g + 8(e/4) +
-      // 4hl + e%4), packed as the B operands of dV^T and dK^T. (Issuing each step's MFMAs
-      // right after its P and dS, as the dQ kernel does, measured slower here.)
-      bf16x8 pk[4], dsk[4];
-#pragma unroll
-      for (int u2 = 0; u2 < 4; ++u2) {
-        const int g = u2 >> 1, s2 = u2 & 1;
-        f32x8 p8, d8;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int qi = 64 * h + 32 * g + 8 * (2 * s2 + half) + 4 * hl;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + qi);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + qi);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 8 * s2 + 4 * half + r;
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[g][e], a.c, -l4[r] * kLog2e));
-            p8[4 * half + r] = p;
-            d8[4 * half + r] = p * (pacc[g][e] - d4[r]);
-          }
-        }
-        pk[u2] = __builtin_convertvector(p8, bf16x8);
-        dsk[u2] = __builtin_convertvector(d8, bf16x8);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (d on M, keys on N, queries contracted).
-#pragma unroll
-      for (int u2 = 0; u2 < 4; ++u2)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int u = 4 * h + u2;
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              read_tr<D>(gt, tb0, tx0, tb1, tx1, u, db), pk[u2], dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              read_tr<D>(qt, tb0, tx0, tb1, tx1, u, db), dsk[u2], dk[db], 0, 0, 0);
-        }
+  // Wait for this P-side wave's copies of the half about to be used, leaving the next
+  // half's (issued one phase later) in flight when there is one.
+  auto wait_half = [&](int p) {
+    if (p + 1 < halves) {
+      if (w < 2) wait_copies<2 * M::kCopies + 1>();
+      else wait_copies<2 * M::kCopies>();
+    } else {
+      wait_copies<0>();
     }
-  }
-  if (krow < n) {
-    const int64_t off = base + static_cast<int64_t>(krow) * a.stride_s;
-    store_rows<D>(a.dv + off, dv, 1.0f, hl);
-    store_rows<D>(a.dk + off, dk, a.scale, hl);
+  };
+  if (w < 4 && lane == 0) flags[wi] = 0;
+  char* const xw = xb + wi * 4096 + lane * 16;  // this SIMD's exchange area, lane part
+  const int64_t out_off = base + static_cast<int64_t>(krow) * a.stride_s;
+
+  if (w < 4) {
+    // ---- P side: S, P, dV ----
+    if (L > 0) {
+      copy_half(0);
+      copy_half(1);
+    }
+    u32x4 kf[NS];  // K as MFMA B operand: d = 16s + 8hl .. +7 of this lane's key
+    load_b_operand<D>(a.k + base, k0, n, row_bytes, 32 * wi + lq, hl, kf);
+    __builtin_amdgcn_s_waitcnt(0);
+    f32x16 dv[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dv[i] = f32x16{};
+    bf16x8 pk[4];  // P of the previous half, packed as the B operands of dV^T
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
+
+    for (int p = 0; p <= halves; ++p) {
+      wait_half(p);
+      lds_barrier();
+      if (p >= 1) {
+        // dV^T += dO^T P for half p - 1 (d on M, keys on N, queries contracted).
+        const char* const gt = slot(p - 1) + M::kHalfBytes;
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                read_tr<D>(gt, tb0, tx0, tb1, tx1, u2, db), pk[u2], dv[db], 0, 0, 0);
+      }
+      if (p < halves) {
+        const int t = p >> 1, h = p & 1;
+        const int qb = qblock(t);
+        // A row block outside [0, nb) was copied as zeros; all of its queries are masked
+        // as padding, so P is zero there (no second path through the loop).
+        const bool valid = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
+        const int n_eff = valid ? n : qb * kBlock;
+        const char* const qt = slot(p);
+        // S = Q K^T for the half's 64 queries (queries on M, this wave's keys on N).
+        f32x16 sacc[2];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          bf16x8 qf[2];
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            qf[g] = *reinterpret_cast<const bf16x8*>(qt + rbase + g * 32 * T::kRowBytes +
+                                                      ((s << 5) ^ rx));
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                qf[g], __builtin_bit_cast(bf16x8, kf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+        }
+        const int row0 = qb * kBlock + 64 * h;
+        if (n_eff - row0 < 64) pad_mask_tile<2>(row0, n_eff, lane, sacc);
+        if constexpr (E != 0)
+          if (valid)
+            element_mask_any<E, 2>(k0 + 32 * wi, row0, a.elem_s, a.elem_gw, a.elem_w0 - 1,
+                                   lane, sacc);
+        // P = 2^(c s - lse2) per entry (query 32g + 8(e/4) + 4hl + e%4 of the half).
+        const float* const lt = reinterpret_cast<const float*>(qt + M::kLse);
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const int g = u2 >> 1, s2 = u2 & 1;
+          f32x8 p8;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const f32x4 l4 =
+                *reinterpret_cast<const f32x4*>(lt + 32 * g + 8 * (2 * s2 + half) + 4 * hl);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              p8[4 * half + r] = __builtin_amdgcn_exp2f(
+                  fmaf(sacc[g][8 * s2 + 4 * half + r], a.c, -l4[r] * kLog2e));
+          }
+          pk[u2] = __builtin_convertvector(p8, bf16x8);
+        }
+        // Half p + 2 goes into the slot that half p - 2 left at this phase's barrier; it
+        // has until the barrier after next to land. (Issued here, where this wave would
+        // otherwise wait for the dS wave: a copy instruction can wait several cycles for
+        // the vector-memory path.)
+        if (p + 2 < halves) copy_half(p + 2);
+        // The dS wave has read half p - 1's P (it marks p after reading in phase p).
+        if (p >= 1)
+          while (__builtin_amdgcn_readfirstlane(flags[wi]) < p) __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) *reinterpret_cast<bf16x8*>(xw + u2 * 1024) = pk[u2];
+      }
+    }
+    if (krow < n) store_rows<D>(a.dv + out_off, dv, 1.0f, hl);
+  } else {
+    // ---- dS side: dP, dS, dK ----
+    u32x4 vf[NS];  // V as MFMA B operand
+    load_b_operand<D>(a.v + base, k0, n, row_bytes, 32 * wi + lq, hl, vf);
+    __builtin_amdgcn_s_waitcnt(0);
+    f32x16 dk[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dk[i] = f32x16{};
+    f32x16 pacc[2];  // dP of the previous half
+    pacc[0] = pacc[1] = f32x16{};
+
+    for (int p = 0; p <= halves; ++p) {
+      lds_barrier();  // (the P side waits for the copies before it)
+      const char* const qt = slot(p - 1);
+      bf16x8 pv[4];
+      f32x4 d4[8];  // D of query 32g + 8j + 4hl + r at d4[4g + j][r]
+      if (p >= 1) {
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) pv[u2] = *reinterpret_cast<const bf16x8*>(xw + u2 * 1024);
+        const float* const dt = reinterpret_cast<const float*>(qt + M::kLse + 256);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          d4[i] = *reinterpret_cast<const f32x4*>(dt + 32 * (i >> 2) + 8 * (i & 3) + 4 * hl);
+      }
+      if (p >= 1) {
+        // Mark the buffer read (the reads have returned) so the P wave may overwrite it.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (lane == 0) flags[wi] = p;
+        // dS = P (dP - D) for half p - 1, then dK^T += Q^T dS (d on M, keys on N,
+        // queries contracted).
+        bf16x8 dsk[4];
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2) {
+          const int g = u2 >> 1, s2 = u2 & 1;
+          f32x8 d8;
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              d8[4 * half + r] = static_cast<float>(pv[u2][4 * half + r]) *
+                                 (pacc[g][8 * s2 + 4 * half + r] - d4[4 * g + 2 * s2 + half][r]);
+          dsk[u2] = __builtin_convertvector(d8, bf16x8);
+        }
+#pragma unroll
+        for (int u2 = 0; u2 < 4; ++u2)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                read_tr<D>(qt, tb0, tx0, tb1, tx1, u2, db), dsk[u2], dk[db], 0, 0, 0);
+      }
+      if (p < halves) {
+        // dP = dO V^T for half p (queries on M, this wave's keys on N).
+        const char* const gt = slot(p) + M::kHalfBytes;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          bf16x8 gf[2];
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            gf[g] = *reinterpret_cast<const bf16x8*>(gt + rbase + g * 32 * T::kRowBytes +
+                                                      ((s << 5) ^ rx));
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                gf[g], __builtin_bit_cast(bf16x8, vf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
+        }
+      }
+    }
+    if (krow < n) store_rows<D>(a.dk + out_off, dk, a.scale, hl);
   }
 }
 
@@ -502,7 +635,7 @@ void launch_bwd(const BwdArgs& args, int rows_total, int items, hipStream_t st) 
   hipLaunchKernelGGL((radial_bwd_delta_kernel<D>), dim3((rows_total + kRowsPerBlock - 1) / kRowsPerBlock),
                      dim3(kBwdThreads), 0, st, args, rows_total);
   hipLaunchKernelGGL((radial_bwd_dq_kernel<D, E>), dim3(items), dim3(kBwdThreads), 0, st, args);
-  hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, E>), dim3(items), dim3(kBwdThreads), 0, st, args);
+  hipLaunchKernelGGL((radial_bwd_dkdv_kernel<D, E>), dim3(items), dim3(kDkdvThreads), 0, st, args);
 }
 
 // The three kernels of one call, at the template instance of head_dim and the element
