@@ -348,15 +348,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
 // bf16 values that also enter dV's MFMAs.
 //
 // The query tiles of the column are walked in halves of 64 queries, one half per phase,
-// with one workgroup barrier between phases. In phase p the P side finishes dV for half
-// p - 1 (P kept in registers) and computes S and P of half p, which it writes to the
-// exchange buffer; the dS side reads P of half p - 1 from that buffer, finishes dK for
-// it, and computes dP of half p. The dS wave of a SIMD marks in an LDS word when it has
-// read the buffer, and the P wave waits for that mark before writing the next half
-// (the dS wave reads first thing after the barrier, so the wait is normally already
-// over). Q and dO halves, with the lse and D of their 64 queries, sit in a ring of four
-// slots: phase p reads halves p - 1 and p, and copies half p + 2, two phases ahead of
-// its use.
+// with one workgroup barrier between phases. In phase p both sides work on half p: the
+// P side computes S and P, writes P to the exchange buffer and marks it written in an
+// LDS word of its SIMD, then accumulates dV; the dS side computes dP meanwhile, waits
+// for the mark, reads P and accumulates dK. (The dS side reads the buffer before the
+// next barrier, and the P side writes it after that barrier, so one buffer serves.) Q
+// and dO halves, with the lse and D of their 64 queries, sit in a ring of four slots:
+// phase p reads half p and copies half p + 3.
 constexpr int kDkdvThreads = 512;
 
 template <int D>
@@ -379,6 +377,67 @@ __device__ __forceinline__ void copy_256(const i32x4& desc, uint32_t lds, int by
                :
                : "s"(lds), "v"(byte_offset), "s"(desc)
                : "memory");
+}
+
+// acc[g] = (rows 32g .. 32g + 31 of a half tile) x B^T over all d: the row reads of
+// step s + 2 are issued beside the MFMAs of step s (one read after each MFMA), pinned
+// with sched_group_barrier; left to itself the compiler waits for each step's reads
+// right before its MFMAs. tile_base is the half tile plus this lane's row offset.
+template <int D>
+__device__ __forceinline__ void half_rows_times(const char* tile_base, int x,
+                                                const u32x4 (&b)[D / 16], f32x16 (&acc)[2]) {
+  constexpr int NS = D / 16;
+  bf16x8 f[2][2];
+  auto rd = [&](int s, bf16x8 (&dst)[2]) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      dst[g] = *reinterpret_cast<const bf16x8*>(tile_base + g * 32 * Tile<D>::kRowBytes +
+                                                 ((s << 5) ^ x));
+  };
+  rd(0, f[0]);
+  rd(1, f[1]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          f[s & 1][g], __builtin_bit_cast(bf16x8, b[s]), s == 0 ? f32x16{} : acc[g], 0, 0, 0);
+    if (s + 2 < NS) rd(s + 2, f[s & 1]);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+}
+
+// acc[db] += (half tile)^T x B over the half's 64 rows, four steps of 16 rows with B
+// operands b[u]: the transposed reads of step u + 1 are issued beside the MFMAs of step
+// u (two reads after each MFMA), pinned as in half_rows_times.
+template <int D>
+__device__ __forceinline__ void half_trans_times(const char* tile, int b0, int x0, int b1, int x1,
+                                                 const bf16x8 (&b)[4], f32x16 (&acc)[D / 32]) {
+  constexpr int NDB = D / 32;
+  bf16x8 f[2][NDB];
+  auto rd = [&](int u, bf16x8 (&dst)[NDB]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dst[db] = read_tr<D>(tile, b0, x0, b1, x1, u, db);
+  };
+  rd(0, f[0]);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDB, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (u + 1 < 4) rd(u + 1, f[(u + 1) & 1]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[u & 1][db], b[u], acc[db], 0, 0, 0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (u + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  }
 }
 
 template <int D, int E>
@@ -454,106 +513,80 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
                sb + M::kLse + w * 256, lane * 4);
     }
   };
-  // Wait for this P-side wave's copies of the half about to be used, leaving the next
-  // half's (issued one phase later) in flight when there is one.
+  // Wait for this P-side wave's copies of half p, leaving those of halves p + 1 and
+  // p + 2 (issued in the two phases before) in flight where they exist.
   auto wait_half = [&](int p) {
-    if (p + 1 < halves) {
-      if (w < 2) wait_copies<2 * M::kCopies + 1>();
-      else wait_copies<2 * M::kCopies>();
+    constexpr int N = 2 * M::kCopies;  // per half, plus one for waves 0 and 1
+    if (p + 2 < halves) {
+      if (w < 2) wait_copies<2 * (N + 1)>();
+      else wait_copies<2 * N>();
+    } else if (p + 1 < halves) {
+      if (w < 2) wait_copies<N + 1>();
+      else wait_copies<N>();
     } else {
       wait_copies<0>();
     }
   };
-  if (w < 4 && lane == 0) flags[wi] = 0;
+  if (w < 4 && lane == 0) flags[wi] = 0;  // P of half p is written when flags[wi] > p
   char* const xw = xb + wi * 4096 + lane * 16;  // this SIMD's exchange area, lane part
   const int64_t out_off = base + static_cast<int64_t>(krow) * a.stride_s;
 
   if (w < 4) {
     // ---- P side: S, P, dV ----
-    if (L > 0) {
-      copy_half(0);
-      copy_half(1);
-    }
+    for (int j = 0; j < 3 && j < halves; ++j) copy_half(j);
     u32x4 kf[NS];  // K as MFMA B operand: d = 16s + 8hl .. +7 of this lane's key
     load_b_operand<D>(a.k + base, k0, n, row_bytes, 32 * wi + lq, hl, kf);
     __builtin_amdgcn_s_waitcnt(0);
     f32x16 dv[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dv[i] = f32x16{};
-    bf16x8 pk[4];  // P of the previous half, packed as the B operands of dV^T
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
-
-    for (int p = 0; p <= halves; ++p) {
+    for (int p = 0; p < halves; ++p) {
       wait_half(p);
       lds_barrier();
-      if (p >= 1) {
-        // dV^T += dO^T P for half p - 1 (d on M, keys on N, queries contracted).
-        const char* const gt = slot(p - 1) + M::kHalfBytes;
+      const int t = p >> 1, h = p & 1;
+      const int qb = qblock(t);
+      // A row block outside [0, nb) was copied as zeros; all of its queries are masked
+      // as padding, so P is zero there (no second path through the loop).
+      const bool valid = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
+      const int n_eff = valid ? n : qb * kBlock;
+      const char* const qt = slot(p);
+      // S = Q K^T for the half's 64 queries (queries on M, this wave's keys on N).
+      f32x16 sacc[2];
+      half_rows_times<D>(qt + rbase, rx, kf, sacc);
+      const int row0 = qb * kBlock + 64 * h;
+      if (n_eff - row0 < 64) pad_mask_tile<2>(row0, n_eff, lane, sacc);
+      if constexpr (E != 0)
+        if (valid)
+          element_mask_any<E, 2>(k0 + 32 * wi, row0, a.elem_s, a.elem_gw, a.elem_w0 - 1,
+                                 lane, sacc);
+      // P = 2^(c s - lse2) per entry (query 32g + 8(e/4) + 4hl + e%4 of the half), packed
+      // as the B operands of dV^T, written for the dS wave and marked.
+      const float* const lt = reinterpret_cast<const float*>(qt + M::kLse);
+      bf16x8 pk[4];
 #pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2)
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const int g = u2 >> 1, s2 = u2 & 1;
+        f32x8 p8;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                read_tr<D>(gt, tb0, tx0, tb1, tx1, u2, db), pk[u2], dv[db], 0, 0, 0);
-      }
-      if (p < halves) {
-        const int t = p >> 1, h = p & 1;
-        const int qb = qblock(t);
-        // A row block outside [0, nb) was copied as zeros; all of its queries are masked
-        // as padding, so P is zero there (no second path through the loop).
-        const bool valid = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
-        const int n_eff = valid ? n : qb * kBlock;
-        const char* const qt = slot(p);
-        // S = Q K^T for the half's 64 queries (queries on M, this wave's keys on N).
-        f32x16 sacc[2];
+        for (int half = 0; half < 2; ++half) {
+          const f32x4 l4 =
+              *reinterpret_cast<const f32x4*>(lt + 32 * g + 8 * (2 * s2 + half) + 4 * hl);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          bf16x8 qf[2];
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            qf[g] = *reinterpret_cast<const bf16x8*>(qt + rbase + g * 32 * T::kRowBytes +
-                                                      ((s << 5) ^ rx));
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            sacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                qf[g], __builtin_bit_cast(bf16x8, kf[s]), s == 0 ? f32x16{} : sacc[g], 0, 0, 0);
+          for (int r = 0; r < 4; ++r)
+            p8[4 * half + r] = __builtin_amdgcn_exp2f(
+                fmaf(sacc[g][8 * s2 + 4 * half + r], a.c, -l4[r] * kLog2e));
         }
-        const int row0 = qb * kBlock + 64 * h;
-        if (n_eff - row0 < 64) pad_mask_tile<2>(row0, n_eff, lane, sacc);
-        if constexpr (E != 0)
-          if (valid)
-            element_mask_any<E, 2>(k0 + 32 * wi, row0, a.elem_s, a.elem_gw, a.elem_w0 - 1,
-                                   lane, sacc);
-        // P = 2^(c s - lse2) per entry (query 32g + 8(e/4) + 4hl + e%4 of the half).
-        const float* const lt = reinterpret_cast<const float*>(qt + M::kLse);
-#pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) {
-          const int g = u2 >> 1, s2 = u2 & 1;
-          f32x8 p8;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x4 l4 =
-                *reinterpret_cast<const f32x4*>(lt + 32 * g + 8 * (2 * s2 + half) + 4 * hl);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              p8[4 * half + r] = __builtin_amdgcn_exp2f(
-                  fmaf(sacc[g][8 * s2 + 4 * half + r], a.c, -l4[r] * kLog2e));
-          }
-          pk[u2] = __builtin_convertvector(p8, bf16x8);
-        }
-        // Half p + 2 goes into the slot that half p - 2 left at this phase's barrier; it
-        // has until the barrier after next to land. (Issued here, where this wave would
-        // otherwise wait for the dS wave: a copy instruction can wait several cycles for
-        // the vector-memory path.)
-        if (p + 2 < halves) copy_half(p + 2);
-        // The dS wave has read half p - 1's P (it marks p after reading in phase p).
-        if (p >= 1)
-          while (__builtin_amdgcn_readfirstlane(flags[wi]) < p) __builtin_amdgcn_s_sleep(1);
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) *reinterpret_cast<bf16x8*>(xw + u2 * 1024) = pk[u2];
+        pk[u2] = __builtin_convertvector(p8, bf16x8);
+        *reinterpret_cast<bf16x8*>(xw + u2 * 1024) = pk[u2];
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane == 0) flags[wi] = p + 1;
+      // dV^T += dO^T P (d on M, keys on N, queries contracted).
+      half_trans_times<D>(qt + M::kHalfBytes, tb0, tx0, tb1, tx1, pk, dv);
+      // Half p + 3 goes into the slot that half p - 1 left at this phase's barrier.
+      // (The copies are issued by this side, which has the shorter path through a phase:
+      // a copy instruction can wait several cycles for the vector-memory path.)
+      if (p + 3 < halves) copy_half(p + 3);
     }
     if (krow < n) store_rows<D>(a.dv + out_off, dv, 1.0f, hl);
   } else {
@@ -564,64 +597,39 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
     f32x16 dk[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dk[i] = f32x16{};
-    f32x16 pacc[2];  // dP of the previous half
-    pacc[0] = pacc[1] = f32x16{};
-
-    for (int p = 0; p <= halves; ++p) {
+    for (int p = 0; p < halves; ++p) {
       lds_barrier();  // (the P side waits for the copies before it)
-      const char* const qt = slot(p - 1);
+      const char* const qt = slot(p);
+      // D of query 32g + 8j + 4hl + r of the half at d4[4g + j][r].
+      const float* const dt = reinterpret_cast<const float*>(qt + M::kLse + 256);
+      f32x4 d4[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        d4[i] = *reinterpret_cast<const f32x4*>(dt + 32 * (i >> 2) + 8 * (i & 3) + 4 * hl);
+      // dP = dO V^T for the half (queries on M, this wave's keys on N).
+      f32x16 pacc[2];
+      half_rows_times<D>(qt + M::kHalfBytes + rbase, rx, vf, pacc);
+      // The P wave has written P of this half (it marks p + 1 after writing).
+      while (__builtin_amdgcn_readfirstlane(flags[wi]) <= p) __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");
       bf16x8 pv[4];
-      f32x4 d4[8];  // D of query 32g + 8j + 4hl + r at d4[4g + j][r]
-      if (p >= 1) {
 #pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) pv[u2] = *reinterpret_cast<const bf16x8*>(xw + u2 * 1024);
-        const float* const dt = reinterpret_cast<const float*>(qt + M::kLse + 256);
+      for (int u2 = 0; u2 < 4; ++u2) pv[u2] = *reinterpret_cast<const bf16x8*>(xw + u2 * 1024);
+      // dS = P (dP - D), then dK^T += Q^T dS (d on M, keys on N, queries contracted).
+      bf16x8 dsk[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          d4[i] = *reinterpret_cast<const f32x4*>(dt + 32 * (i >> 2) + 8 * (i & 3) + 4 * hl);
+      for (int u2 = 0; u2 < 4; ++u2) {
+        const int g = u2 >> 1, s2 = u2 & 1;
+        f32x8 d8;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            d8[4 * half + r] = static_cast<float>(pv[u2][4 * half + r]) *
+                               (pacc[g][8 * s2 + 4 * half + r] - d4[4 * g + 2 * s2 + half][r]);
+        dsk[u2] = __builtin_convertvector(d8, bf16x8);
       }
-      if (p >= 1) {
-        // Mark the buffer read (the reads have returned) so the P wave may overwrite it.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (lane == 0) flags[wi] = p;
-        // dS = P (dP - D) for half p - 1, then dK^T += Q^T dS (d on M, keys on N,
-        // queries contracted).
-        bf16x8 dsk[4];
-#pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) {
-          const int g = u2 >> 1, s2 = u2 & 1;
-          f32x8 d8;
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              d8[4 * half + r] = static_cast<float>(pv[u2][4 * half + r]) *
-                                 (pacc[g][8 * s2 + 4 * half + r] - d4[4 * g + 2 * s2 + half][r]);
-          dsk[u2] = __builtin_convertvector(d8, bf16x8);
-        }
-#pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                read_tr<D>(qt, tb0, tx0, tb1, tx1, u2, db), dsk[u2], dk[db], 0, 0, 0);
-      }
-      if (p < halves) {
-        // dP = dO V^T for half p (queries on M, this wave's keys on N).
-        const char* const gt = slot(p) + M::kHalfBytes;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          bf16x8 gf[2];
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            gf[g] = *reinterpret_cast<const bf16x8*>(gt + rbase + g * 32 * T::kRowBytes +
-                                                      ((s << 5) ^ rx));
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            pacc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                gf[g], __builtin_bit_cast(bf16x8, vf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
-        }
-      }
+      half_trans_times<D>(qt, tb0, tx0, tb1, tx1, dsk, dk);
     }
     if (krow < n) store_rows<D>(a.dk + out_off, dk, a.scale, hl);
   }
