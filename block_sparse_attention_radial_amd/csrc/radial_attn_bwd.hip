@@ -92,6 +92,16 @@ struct BwdGeometry {
   int n, nb, blk;
 };
 
+// The block that the j-th workgroup of a (batch, head) works on. The hardware deals
+// workgroup ids to the 8 XCDs round-robin; in each group of 32 blocks this gives each
+// XCD a run of 4 neighbours (whose rows, or columns, of the mask are nearly the same, so
+// they share that XCD's L2) while every XCD still samples the whole head evenly. The
+// blocks past the last whole group keep their place.
+__device__ __forceinline__ int block_of(int j, int nb) {
+  if (j >= (nb & ~31)) return j;
+  return (j & ~31) | ((j & 7) << 2) | ((j >> 3) & 3);
+}
+
 __device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
   BwdGeometry g;
   if (a.varlen == 0) {
@@ -104,7 +114,7 @@ __device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
     g.col_ptr = a.col_ptr;
     g.n = a.n;
     g.nb = a.nb;
-    g.blk = wg - bh * a.nb;
+    g.blk = block_of(wg - bh * a.nb, a.nb);
     return g;
   }
   const BwdArgsPtr ap = (BwdArgsPtr)(__builtin_amdgcn_kernarg_segment_ptr());
@@ -123,7 +133,7 @@ __device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
   g.col_ptr = a.col_ptr + rp0;
   g.n = ap->plan[lo].n;
   g.nb = nb;
-  g.blk = wg - ap->plan[lo].wg0 - h * nb;
+  g.blk = block_of(wg - ap->plan[lo].wg0 - h * nb, nb);
   return g;
 }
 
