@@ -221,8 +221,9 @@ __device__ __forceinline__ void store_rows(__bf16* dst_row, const f32x16 (&acc)[
 // Two workgroups share a CU (64 KiB of LDS and at most 256 registers per wave each), so
 // each SIMD runs two dQ waves from different workgroups and interleaves them: while one
 // waits for its tile copy or works through its VALU steps, the other issues MFMAs. The
-// K and V tiles are therefore single-buffered: tile t + 1 is copied after every wave
-// is done with tile t.
+// K and V tiles are therefore single-buffered, but in halves of 64 keys: once every wave
+// is done with one half, the next half is copied into its rows while the waves work on
+// the other half.
 template <int D, int E>
 __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const BwdArgs a) {
   using T = Tile<D>;
@@ -248,27 +249,51 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
     lse2 = geo.lse[qrow] * kLog2e;
     dlt = geo.delta[qrow];
   }
-  int copy_off[T::kOffsetPeriod];
-  copy_offsets<D>(wi, lane, row_bytes, copy_off);
+  // A half tile (64 rows) of K or V is HC KiB per wave: lane offsets of copy i of wave
+  // wi, which fills KiB wi * HC + i of the half (chunk position p of row r holds global
+  // chunk p ^ swz(r)).
+  constexpr int HC = 64 * T::kRowBytes / 1024 / 4;
+  int copy_off[HC];
+#pragma unroll
+  for (int i = 0; i < HC; ++i) {
+    const int ci = (wi * HC + i) * 64 + lane;
+    const int row = ci / T::kChunks, pos = ci % T::kChunks;
+    copy_off[i] = row * row_bytes + ((pos ^ swz<D>(row)) << 4);
+  }
   int rbase, rx, tb0, tx0, tb1, tx1;
   row_read_offsets<D>(lane, rbase, rx);
   tr_read_offsets<D>(lane, tb0, tx0, tb1, tx1);
 
   const int r0 = geo.row_ptr[qb];
   const int L = geo.row_ptr[qb + 1] - r0;
-  auto column = [&](int t) { return __builtin_amdgcn_readfirstlane(a.col_idx[r0 + t]); };
-  auto copy_tile = [&](int t) {
+  // The row's key blocks through the constant address space (scalar loads): a vector
+  // load would be waited for with vmcnt(0), which counts the copies in flight too.
+  ConstI32* const cols_of = (ConstI32*)(a.col_idx + r0);
+  auto column = [&](int t) { return cols_of[t]; };
+  // Half j of the walk (key block column(j / 2), keys 64 (j % 2) ..) into rows
+  // 64 (j % 2) .. of the K and V buffers.
+  auto copy_half = [&](int j) {
+    const int t = j >> 1, h = j & 1;
     const int kb = column(t);
     const bool on = static_cast<unsigned>(kb) < static_cast<unsigned>(nb);
-    const Stage<D> sk = stage_rows<D>(kb0, kh, kb * kBlock, n, row_bytes, wi, on);
-    const Stage<D> sv = stage_rows<D>(vb0, vh, kb * kBlock, n, row_bytes, wi, on);
+    const int row0 = on ? kb * kBlock + 64 * h : 0;
+    const int left = n - row0;
+    // (readfirstlane: the compiler clamps with a vector instruction, and the descriptors
+    // built from this must be scalar.)
+    const int rows = __builtin_amdgcn_readfirstlane(on ? (left < 64 ? (left > 0 ? left : 0) : 64) : 0);
+    const int bytes = rows > 0 ? (rows - 1) * row_bytes + T::kRowBytes : 0;
+    const i32x4 dk_ = raw_descriptor(kh + static_cast<int64_t>(row0) * row_bytes, bytes);
+    const i32x4 dv_ = raw_descriptor(vh + static_cast<int64_t>(row0) * row_bytes, bytes);
+    const uint32_t off = h * 64 * T::kRowBytes + wi * HC * 1024;
+    const uint32_t kd = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)kb0)) + off;
+    const uint32_t vd = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)vb0)) + off;
 #pragma unroll
-    for (int i = 0; i < T::kCopiesPerWave; ++i) {
-      stage_issue<D>(sk, copy_off, i);
-      stage_issue<D>(sv, copy_off, i);
+    for (int i = 0; i < HC; ++i) {
+      copy_1k(dk_, kd + i * 1024, copy_off[i]);
+      copy_1k(dv_, vd + i * 1024, copy_off[i]);
     }
   };
-  if (L > 0) copy_tile(0);
+  if (L > 0) copy_half(0);
 
   // Q^T and dO^T as MFMA B operands: d = 16s + 8hl .. +7 of this lane's query.
   u32x4 qf[NS], gf[NS];
@@ -281,8 +306,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
 
   for (int t = 0; t < L; ++t) {
-    wait_copies<0>();  // this wave's part of tile t
-    lds_barrier();     // every wave's part landed
     const int kb = column(t);
     // A column outside [0, nb) was copied as zeros; every one of its keys is masked as
     // padding (n_eff = its first token), so it adds nothing. No branch skips it: a second
@@ -295,6 +318,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
     // The tile in two halves of 64 keys, so that only half of S^T and dP^T is live.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      wait_copies<0>();  // this wave's part of half (t, h)
+      lds_barrier();     // every wave's part landed, and every wave is done with the
+                         // previous half, whose rows the next half now takes
+      if (2 * t + h + 1 < 2 * L) copy_half(2 * t + h + 1);
       // S^T = K Q^T and dP^T = V dO^T for keys 64h .. 64h + 63 (keys on M, this wave's
       // queries on N).
       f32x16 sacc[2], pacc[2];
@@ -342,8 +369,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
               read_tr<D>(kt, tb0, tx0, tb1, tx1, 4 * h + u2, db), dsk, dq[db], 0, 0, 0);
       }
     }
-    lds_barrier();  // every wave is done with tile t
-    if (t + 1 < L) copy_tile(t + 1);
   }
   if (qrow < n) store_rows<D>(a.dq + base + static_cast<int64_t>(qrow) * a.stride_s, dq, a.scale, hl);
 }
