@@ -19,13 +19,13 @@
 //     the mask (the transposed CSR). Per query tile: S = Q K^T and dP = dO V^T (queries
 //     on M, keys on N, Q and dO rows from LDS, K and V in registers), P and dS, then
 //     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from transposing LDS reads.
-// A workgroup is four wave64, one per SIMD; wave i owns rows (dq) or keys (dkdv)
-// 32i .. 32i+31 of its block. Tiles are copied HBM/L2 -> LDS with LDS-DMA. dkdv runs one
-// workgroup per CU and double-buffers its tiles (tile t+1 is in flight while tile t is
-// used); dq runs two workgroups per CU with single buffers, and each SIMD interleaves
-// the two workgroups' waves. Accumulation is fp32; P and dS
-// enter the MFMAs as bf16. Padding (rows or keys at or past n) and element masking work
-// as in the forward.
+// Tiles are copied HBM/L2 -> LDS with LDS-DMA. A dq workgroup is four wave64, one per
+// SIMD, wave i owning rows 32i .. 32i+31 of its block; two of them share a CU, and each
+// SIMD interleaves the two workgroups' waves. A dkdv workgroup is eight wave64 in two
+// roles (S, P and dV beside dP, dS and dK), waves i and i + 4 sharing SIMD i and keys
+// 32i .. 32i+31; one per CU (see the kernel). Accumulation is fp32; P and dS enter the
+// MFMAs as bf16. Padding (rows or keys at or past n) and element masking work as in the
+// forward.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
