@@ -55,9 +55,13 @@ enum {
 
 /*
  * radial_mask_dims — sizes of the block mask for a video of `frames` x `tokens_per_frame`
- * tokens with base window `w0`. It writes the number of block rows
- * nb = ceil(frames * tokens_per_frame / 128) to *nb_out, and the number of active
- * blocks to *nnz_out. It runs on the host only.
+ * tokens with base window `w0`. The mask is the static radial mask of "Radial Attention:
+ * A Breakthrough in Efficient Long Video Generation", How Radial Attention Works (the
+ * spatial window halves each time the temporal distance doubles, applied in 128x128
+ * blocks), with frame-major tokens as on the radial-attention-video SKILL.md page,
+ * Step 1; the rule is the one stated at the top of this header. It writes the number of
+ * block rows nb = ceil(frames * tokens_per_frame / 128) to *nb_out, and the number of
+ * active blocks to *nnz_out. It runs on the host only.
  *
  * Errors: INVALID_ARG if frames, tokens_per_frame or w0 is <= 0, if block != 128, or if
  * an output pointer is null. TOO_LARGE if the sequence length or the active-block count
@@ -67,8 +71,9 @@ int32_t radial_mask_dims(int32_t frames, int32_t tokens_per_frame, int32_t w0, i
                          int32_t* nb_out, int64_t* nnz_out);
 
 /*
- * radial_build_mask — fill the block mask in compressed-row form. This is host code and
- * is deterministic.
+ * radial_build_mask — fill the block mask of radial_mask_dims (the same pages: a block is
+ * active iff one of its (query, key) pairs passes the rule) in compressed-row form. This
+ * is host code and is deterministic.
  *
  * row_ptr: caller-owned host array of nb + 1 int32. row_ptr[0] = 0, and row r's active key
  *          blocks are col_idx[row_ptr[r] .. row_ptr[r+1]).
