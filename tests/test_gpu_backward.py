@@ -262,3 +262,30 @@ def test_backward_full_size_one_head_wan():
                                 *oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0), wl.scale)
     for got, r in zip(grads, ref):
         check(got, r)
+
+
+@pytest.mark.parametrize("wlname", ["wan", "wan-grid"])
+def test_backward_full_size_sampled_element(wlname):
+    """Element masking at full size (the 1-D rule at Wan, the grid rule at the Wan grid),
+    one head: dq on sampled query blocks, dk and dv on sampled key blocks (the first,
+    one inside, the ragged last), against the oracle's element option."""
+    wl = WORKLOADS[wlname]
+    q, k, v = draw_qkv(wl, seed=0, device="cuda", heads=range(1))
+    g = torch.Generator(device="cuda").manual_seed(13)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    md = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w).to("cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(q, k, v, md, lse=lse, element=True)
+    dq, dk, dv = radial.attn_bwd(q, k, v, o, do, lse, md, element=True)
+    torch.cuda.synchronize()
+    qbs, kbs = [0, 97, wl.nb - 1], [5, 200, wl.nb - 1]
+    element = ((wl.tokens_per_frame, wl.w0) if wl.grid_w is None
+               else (wl.tokens_per_frame, wl.w0, wl.grid_w))
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do),
+                                *oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0, wl.grid_w),
+                                wl.scale, element=element, query_blocks=qbs, key_blocks=kbs)
+    rows_q = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in qbs])
+    rows_k = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in kbs])
+    check(dq, ref[0], rows=rows_q)
+    check(dk, ref[1], rows=rows_k)
+    check(dv, ref[2], rows=rows_k)
