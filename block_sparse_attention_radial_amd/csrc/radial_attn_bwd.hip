@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
   u32x4 qf[NS], gf[NS];
   load_b_operand<D>(a.q + base, q0, n, row_bytes, 32 * wi + lq, hl, qf);
   load_b_operand<D>(a.g + base, q0, n, row_bytes, 32 * wi + lq, hl, gf);
-  __builtin_amdgcn_s_waitcnt(0);  // Q, dO and the first tile (see the forward prologue)
+  __builtin_amdgcn_s_waitcnt(0);  // Q, dO and the first half tile (see the forward prologue)
 
   f32x16 dq[NDB];
 #pragma unroll
