@@ -246,10 +246,13 @@ def test_backward_skips_out_of_range_columns():
         assert torch.equal(a, b)
 
 
-def test_backward_full_size_one_head_wan():
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_backward_full_size_one_head_wan(head_dim):
     """Every dq, dk and dv row of one Wan-shaped head (n = 32760, 256 blocks, every
-    column of the mask walked), against the oracle over the whole head."""
-    wl = WORKLOADS["wan"]
+    column of the mask walked), against the oracle over the whole head; at D = 128 (the
+    Wan head) and D = 64 (the kernels' other instance, same mask)."""
+    w = WORKLOADS["wan"]
+    wl = Workload(w.name, 1, w.heads, head_dim, w.frames, w.tokens_per_frame, w.w0, w.sigma)
     q, k, v = draw_qkv(wl, seed=0, device="cuda", heads=range(1))
     g = torch.Generator(device="cuda").manual_seed(12)
     do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
