@@ -374,7 +374,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     elem_s, elem_w0, elem_gw = _element_args(mask, element)
     dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
                   for _ in range(3))
-    delta = torch.empty(B, H, n, dtype=torch.float32, device=q.device)
+    delta = torch.empty(2, B, H, n, dtype=torch.float32, device=q.device)  # D_i, base-2 lse
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check("radial_attn_bwd", lib().radial_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
@@ -644,7 +644,7 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     elem_s, elem_w0, elem_gw = _element_args(mask, element)
     dq, dk, dv = (torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
                   for _ in range(3))
-    delta = torch.empty(H, total, dtype=torch.float32, device=q.device)
+    delta = torch.empty(2, H, total, dtype=torch.float32, device=q.device)  # D_i, base-2 lse
     seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check("radial_attn_bwd_varlen", lib().radial_attn_bwd_varlen(

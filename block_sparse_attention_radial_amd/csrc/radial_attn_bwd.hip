@@ -9,7 +9,7 @@
 // P is recomputed from the forward's log-sum-exp: P_ij = exp(scale s_ij - lse_i).
 //
 // Three kernels, one stream:
-//  1. delta: D_i for every row (fp32, into a caller workspace).
+//  1. delta: D_i and lse_i log2(e) for every row (fp32, into a caller workspace).
 //  2. dq: one workgroup per (batch, head, query block), walking the block's CSR row. Per
 //     key tile: S^T = K Q^T and dP^T = V dO^T on MFMA (keys on M, queries on N, K and V
 //     rows from LDS, Q^T and dO^T in registers), P^T and dS^T in registers, then
@@ -60,7 +60,8 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* delta;
+  float* delta;  // D_i per row: the first half of the workspace
+  float* lse2;   // lse_i log2(e) per row: its second half
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const int32_t* col_ptr;
@@ -71,7 +72,8 @@ struct BwdArgs {
   float c;      // scale * log2(e), at least FLT_MIN (base2_scale)
   float scale;
   // varlen: 0 for a uniform batch, else the number of samples in `plan`; q, k, v, o, dO,
-  // dq, dk, dv are then one packed sequence of n tokens, and lse, delta are [heads, n].
+  // dq, dk, dv are then one packed sequence of n tokens, and lse, delta, lse2 are
+  // [heads, n].
   int varlen;
   BwdSample plan[kMaxBwdVarlen];
 };
@@ -79,13 +81,13 @@ typedef __attribute__((address_space(4))) const BwdArgs* BwdArgsPtr;
 typedef __attribute__((address_space(4))) const int32_t ConstI32;
 typedef __attribute__((address_space(3))) volatile int LdsFlag;
 
-// Where a dq or dkdv workgroup works: the (batch, head) element offset, its rows of lse
-// and delta, its mask rows (row_ptr / col_ptr point at its sample's), its sequence length
+// Where a dq or dkdv workgroup works: the (batch, head) element offset, its rows of
+// lse2 and delta, its mask rows (row_ptr / col_ptr point at its sample's), its sequence length
 // and block count, and its block. Varlen plans are read from the kernel-argument segment
 // (scalar loads; a copy of the plan would go to scratch memory under a dynamic index).
 struct BwdGeometry {
   int64_t base;
-  const float* lse;
+  const float* lse2;
   const float* delta;
   const int32_t* row_ptr;
   const int32_t* col_ptr;
@@ -108,7 +110,7 @@ __device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
     const int bh = wg / a.nb;
     const int b = bh / a.heads, h = bh - b * a.heads;
     g.base = b * a.stride_b + h * a.stride_h;
-    g.lse = a.lse + static_cast<int64_t>(bh) * a.n;
+    g.lse2 = a.lse2 + static_cast<int64_t>(bh) * a.n;
     g.delta = a.delta + static_cast<int64_t>(bh) * a.n;
     g.row_ptr = a.row_ptr;
     g.col_ptr = a.col_ptr;
@@ -127,7 +129,7 @@ __device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
   const int tok0 = ap->plan[lo].tok0, nb = ap->plan[lo].nb, rp0 = ap->plan[lo].rp0;
   const int h = (wg - ap->plan[lo].wg0) / nb;
   g.base = static_cast<int64_t>(tok0) * a.stride_s + h * a.stride_h;
-  g.lse = a.lse + static_cast<int64_t>(h) * a.n + tok0;
+  g.lse2 = a.lse2 + static_cast<int64_t>(h) * a.n + tok0;
   g.delta = a.delta + static_cast<int64_t>(h) * a.n + tok0;
   g.row_ptr = a.row_ptr + rp0;
   g.col_ptr = a.col_ptr + rp0;
@@ -137,8 +139,11 @@ __device__ __forceinline__ BwdGeometry bwd_geometry(const BwdArgs& a, int wg) {
   return g;
 }
 
-// ---- 1. D_i = <do_i, o_i> ----
-// D / 8 lanes per row, 8 bf16 each; 256 / (D / 8) rows per workgroup.
+// ---- 1. D_i = <do_i, o_i>, and lse_i in base 2 ----
+// D / 8 lanes per row, 8 bf16 each; 256 / (D / 8) rows per workgroup. The base-2 lse
+// (lse_i log2(e), the exponent offset of P in 2^(c s - lse2)) is written beside D_i once
+// per row, so that the dq and dkdv kernels, which read it once per tile, need no multiply
+// per score for it.
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void radial_bwd_delta_kernel(const BwdArgs a,
                                                                        int rows_total) {
@@ -148,7 +153,8 @@ __global__ __launch_bounds__(kBwdThreads) void radial_bwd_delta_kernel(const Bwd
   const int ch = tid % kLanes;
   float acc = 0.f;
   if (r < rows_total) {
-    // Row r of delta's layout: [batch, heads, n], or [heads, n] of a packed varlen batch.
+    // Row r of the layout of delta, lse2 and lse: [batch, heads, n], or [heads, n] of a
+    // packed varlen batch.
     const int bh = r / a.n, i = r - bh * a.n;
     const int b = a.varlen ? 0 : bh / a.heads, h = a.varlen ? bh : bh - b * a.heads;
     const int64_t off = b * a.stride_b + h * a.stride_h + static_cast<int64_t>(i) * a.stride_s +
@@ -160,7 +166,10 @@ __global__ __launch_bounds__(kBwdThreads) void radial_bwd_delta_kernel(const Bwd
   }
 #pragma unroll
   for (int m = kLanes / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
-  if (r < rows_total && ch == 0) a.delta[r] = acc;
+  if (r < rows_total && ch == 0) {
+    a.delta[r] = acc;
+    a.lse2[r] = a.lse[r] * kLog2e;
+  }
 }
 
 // Row-read A operands of k-step s for the four 32-row groups of a tile (see
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
   // This lane's query: its log-sum-exp in base 2 and D_i.
   float lse2 = 0.f, dlt = 0.f;
   if (qrow < n) {
-    lse2 = geo.lse[qrow] * kLog2e;
+    lse2 = geo.lse2[qrow];
     dlt = geo.delta[qrow];
   }
   // A half tile (64 rows) of K or V is HC KiB per wave: lane offsets of copy i of wave
@@ -423,6 +432,10 @@ __device__ __forceinline__ void half_rows_times(const char* tile_base, int x,
                                                 const u32x4 (&b)[D / 16], f32x16 (&acc)[2]) {
   constexpr int NS = D / 16;
   bf16x8 f[2][2];
+  // LDS reads that the caller issued before (the lse or D values of the half) stay ahead
+  // of this fence; otherwise the pinned groups below count them as this product's first
+  // reads, and each MFMA then waits for the read issued just before it.
+  __builtin_amdgcn_sched_barrier(0);
   auto rd = [&](int s, bf16x8 (&dst)[2]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g)
@@ -522,7 +535,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
   auto slot = [&](int j) { return smem + (j & 3) * M::kSlot; };
   // Copy half j (query tile j / 2, rows 64 (j % 2) ..) into its slot; the P-side waves
   // issue the copies (the dS side is the longer path through a phase), wave 0 also copies
-  // the half's lse and wave 1 its D, one instruction more per half.
+  // the half's base-2 lse and wave 1 its D, one instruction more per half.
   auto copy_half = [&](int j) {
     const int t = j >> 1, h = j & 1;
     const int qb = qblock(t);
@@ -543,7 +556,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
       copy_1k(dg_, dst + M::kHalfBytes + i * 1024, copy_off[i]);
     }
     if (w < 2) {
-      const float* src = (w == 0 ? geo.lse : geo.delta) + row0;
+      const float* src = (w == 0 ? geo.lse2 : geo.delta) + row0;
       copy_256(raw_descriptor(reinterpret_cast<const char*>(src), rows * 4),
                sb + M::kLse + w * 256, lane * 4);
     }
@@ -576,15 +589,25 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dv[i] = f32x16{};
     for (int p = 0; p < halves; ++p) {
+      const int t = p >> 1, h = p & 1;
+      // (The scalar load of the row block is waited for before the barrier: a wait after
+      // it would also wait for the LDS reads issued below.)
+      int qb = qblock(t);
+      asm volatile("" : "+s"(qb));
       wait_half(p);
       lds_barrier();
-      const int t = p >> 1, h = p & 1;
-      const int qb = qblock(t);
       // A row block outside [0, nb) was copied as zeros; all of its queries are masked
       // as padding, so P is zero there (no second path through the loop).
       const bool valid = static_cast<unsigned>(qb) < static_cast<unsigned>(nb);
       const int n_eff = valid ? n : qb * kBlock;
       const char* const qt = slot(p);
+      // The base-2 lse of query 32g + 8j + 4hl + r of the half at l4[4g + j][r], read
+      // now so that they land while S is computed.
+      const float* const lt = reinterpret_cast<const float*>(qt + M::kLse);
+      f32x4 l4[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        l4[i] = *reinterpret_cast<const f32x4*>(lt + 32 * (i >> 2) + 8 * (i & 3) + 4 * hl);
       // S = Q K^T for the half's 64 queries (queries on M, this wave's keys on N).
       f32x16 sacc[2];
       half_rows_times<D>(qt + rbase, rx, kf, sacc);
@@ -596,7 +619,6 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
                                  lane, sacc);
       // P = 2^(c s - lse2) per entry (query 32g + 8(e/4) + 4hl + e%4 of the half), packed
       // as the B operands of dV^T, written for the dS wave and marked.
-      const float* const lt = reinterpret_cast<const float*>(qt + M::kLse);
       bf16x8 pk[4];
 #pragma unroll
       for (int u2 = 0; u2 < 4; ++u2) {
@@ -604,12 +626,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
         f32x8 p8;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const f32x4 l4 =
-              *reinterpret_cast<const f32x4*>(lt + 32 * g + 8 * (2 * s2 + half) + 4 * hl);
+          const f32x4 lh = l4[4 * g + 2 * s2 + half];
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            p8[4 * half + r] = __builtin_amdgcn_exp2f(
-                fmaf(sacc[g][8 * s2 + 4 * half + r], a.c, -l4[r] * kLog2e));
+            p8[4 * half + r] =
+                __builtin_amdgcn_exp2f(fmaf(sacc[g][8 * s2 + 4 * half + r], a.c, -lh[r]));
         }
         pk[u2] = __builtin_convertvector(p8, bf16x8);
         *reinterpret_cast<bf16x8*>(xw + u2 * 1024) = pk[u2];
@@ -703,9 +724,10 @@ int32_t launch_all(const BwdArgs& args, int rows_total, int items, int head_dim,
 
 namespace {
 
-// The uniform backward: checks, then the three kernels. delta is the D_i workspace
-// (caller-owned, or the static scratch of radial_attn_bwd_noalloc); max_rows bounds
-// batch * heads * seqlen (the workspace's size), or is 0 for no bound.
+// The uniform backward: checks, then the three kernels. delta is the workspace of two
+// fp32 per row, D_i then the base-2 lse (caller-owned, or the static scratch of
+// radial_attn_bwd_noalloc); max_rows bounds batch * heads * seqlen (the rows the
+// workspace holds), or is 0 for no bound.
 int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
                     float* delta, int64_t max_rows, const int32_t* row_ptr,
@@ -746,6 +768,7 @@ int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
   args.dk = static_cast<__bf16*>(dk);
   args.dv = static_cast<__bf16*>(dv);
   args.delta = delta;
+  args.lse2 = delta + rows_total;
   args.row_ptr = row_ptr;
   args.col_idx = col_idx;
   args.col_ptr = col_ptr;
@@ -766,8 +789,8 @@ int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
                     element_tokens_per_frame, element_grid_w, stream);
 }
 
-// radial_attn_bwd_noalloc's workspace: the backward's D_i, one fp32 per row, for at most
-// kScratchRows rows (32 MiB per device, held until the process ends). Host code never
+// radial_attn_bwd_noalloc's workspace: the backward's D_i and base-2 lse, two fp32 per
+// row, for at most kScratchRows rows (64 MiB per device, held until the process ends). Host code never
 // uses the array's name as an address: each device's address comes from
 // hipGetSymbolAddress, once per device, with that device current.
 constexpr int64_t kScratchRows = int64_t(1) << 23;
@@ -777,7 +800,7 @@ std::mutex g_scratch_mu;
 
 }  // namespace
 
-static __device__ __align__(256) float scratch[kScratchRows];
+static __device__ __align__(256) float scratch[2 * kScratchRows];
 
 namespace {
 
@@ -905,6 +928,7 @@ extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const vo
     return RADIAL_ERR_TOO_LARGE;
   args.n = static_cast<int>(tok);  // the packed sequence; lse and delta are [heads, n]
   args.nb = 0;                     // per sample, from the plan
+  args.lse2 = delta + heads * tok;
   return launch_all(args, static_cast<int>(heads * tok), static_cast<int>(wgs), head_dim,
                     element_tokens_per_frame, element_grid_w, stream);
 }

@@ -354,7 +354,9 @@ int32_t radial_transpose_mask(int32_t nb, const int32_t* row_ptr, const int32_t*
  *             set of element strides (as in radial_attn_fwd); o is the forward's output
  *             for these q, k, v and mask. dq, dk, dv are written for rows < seqlen.
  * lse:        the forward's lse output (fp32 [batch, heads, seqlen], contiguous).
- * delta:      caller-owned device workspace of batch * heads * seqlen fp32 (D_i).
+ * delta:      caller-owned device workspace of 2 * batch * heads * seqlen fp32: the
+ *             call writes D_i into the first half and lse_i log2(e) into the second,
+ *             both [batch, heads, seqlen], and reads them back in its later kernels.
  * row_ptr, col_idx: the block mask used by the forward (device).
  * col_ptr, row_idx: its transpose from radial_transpose_mask (device). For a radial mask
  *             these may be row_ptr and col_idx themselves.
@@ -377,9 +379,10 @@ int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void*
 /*
  * radial_attn_bwd_noalloc — radial_attn_bwd without the delta workspace argument, for
  * callers that cannot allocate device memory: code under graph capture, tight serving
- * loops, harnesses that forbid hipMalloc. The call allocates nothing: its D_i workspace
- * is a static device array of the library, 2^23 fp32 values (32 MiB) on each device
- * the library runs on, held until the process ends.
+ * loops, harnesses that forbid hipMalloc. The call allocates nothing: its workspace (D_i
+ * and the base-2 lse, two fp32 per row) is a static device array of the library,
+ * 2 * 2^23 fp32 values (64 MiB) on each device the library runs on, held until the
+ * process ends.
  *
  * Arguments, results and numerics are radial_attn_bwd's (the same kernels), without
  * `delta`. The workspace keeps the last call's values; nothing needs to start at zero.
@@ -388,7 +391,7 @@ int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void*
  * wrong gradients; calls on one stream are ordered and safe.
  *
  * Errors: as radial_attn_bwd, plus TOO_LARGE when batch * heads * seqlen exceeds 2^23
- * (the workspace), checked before any HIP call; HIP also when the workspace's device
+ * (the rows the workspace holds), checked before any HIP call; HIP also when the workspace's device
  * address cannot be looked up.
  */
 int32_t radial_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
@@ -409,7 +412,8 @@ int32_t radial_attn_bwd_noalloc(const void* q, const void* k, const void* v, con
  *             strides stride_s between tokens and stride_h between heads, shared by all
  *             eight, head_dim contiguous; sample b holds the next seq_tokens[b] tokens.
  * lse:        the forward's fp32 [heads, total_tokens] output (contiguous).
- * delta:      caller-owned fp32 workspace of heads * total_tokens.
+ * delta:      caller-owned fp32 workspace of 2 * heads * total_tokens (D_i, then
+ *             lse_i log2(e), each [heads, total_tokens]).
  * seq_tokens: host array of batch lengths (each >= 1); 1 <= batch <= 64.
  * row_ptr, col_idx, col_ptr, row_idx: the samples' block masks and their transposes
  *             (device), each concatenated as radial_attn_fwd_varlen takes row_ptr and

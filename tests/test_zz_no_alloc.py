@@ -1,7 +1,7 @@
 """radial_attn_bwd_noalloc against radial_attn_bwd, through the C ABI (GPU).
 
-The allocation-free entry point keeps the backward's D_i workspace in the library's
-static device memory instead of a caller buffer. Its gradients must equal those of
+The allocation-free entry point keeps the backward's workspace (D_i and the base-2 lse)
+in the library's static device memory instead of a caller buffer. Its gradients must equal those of
 radial_attn_bwd (the same kernels) bit for bit: on two calls in a row, the second with a
 smaller input, so that the second call runs on the workspace the first one left behind.
 A shape past the workspace is refused.
