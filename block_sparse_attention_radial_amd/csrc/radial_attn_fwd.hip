@@ -435,18 +435,33 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
   __builtin_amdgcn_s_setprio(0);
 }
 
-// One work item: the two query-block rows of pair p (from the pair table, or 2p and
+// The pair that item `pid` of a varlen sample's head works on, the head's items being
+// the ids [first_id, first_id + np). Item ids are taken by the XCDs round-robin (XCD =
+// id % 8), in id order on each XCD (see radial_fwd_kernel); the ids of the head that land
+// on XCD x take one contiguous run of its pair table, in order.
+__device__ __forceinline__ int varlen_pair(int pid, int first_id, int np) {
+  const int xcd = pid & 7;
+  int seg = 0;  // pairs of this head taken by XCDs 0 .. xcd-1
+  for (int y = 0; y < xcd; ++y)
+    seg += ((first_id + np - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
+  const int first_here = first_id + ((xcd - first_id) & 7);  // first id of this head on xcd
+  return seg + ((pid - first_here) >> 3);
+}
+
+// One work item: the two query-block rows of pair `pair` (from the pair table, or 2p and
 // 2p+1) of one (batch, head). q, k, v, o point at row 0 of this (batch, head), lse (if
-// not null) at its row 0's entry; the ids [first_id, first_id + np) are this head's
-// items. smem holds two K and two V buffers at fixed offsets, then the union list;
-// counts holds the per-wave sums of the list compaction, then the union length.
+// not null) at its row 0's entry. smem holds two K and two V buffers at fixed offsets,
+// then the union list; counts holds the per-wave sums of the list compaction, then the
+// union length. The host orders the pair table so that neighbouring pairs have nearly
+// equal length and lie close in the sequence: taken together by one XCD, they walk their
+// lists in step and share that XCD's L2 (radial_build_pairs).
 template <int D, int E>
 __device__ __forceinline__ void run_item(
-    int pid, int first_id, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
+    int pair, int tid, char* smem, int* counts, const __bf16* __restrict__ q,
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
-    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int np, int nb,
-    int n, float c, int stride_s, int es, int egw, int ew0, RulePtr rule) {
+    const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int nb, int n,
+    float c, int stride_s, int es, int egw, int ew0, RulePtr rule) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -454,19 +469,6 @@ __device__ __forceinline__ void run_item(
   char* const v1 = smem + 3 * T::kBytes;
   uint16_t* const list = reinterpret_cast<uint16_t*>(smem + 4 * T::kBytes);
 
-  // Work mapping. Item ids are taken by the XCDs round-robin (XCD = id % 8), in id order
-  // on each XCD (see radial_fwd_kernel). The ids of one head are contiguous, so the whole
-  // chip works on one or two heads at a time and their K/V stays in the shared Infinity
-  // Cache. Inside a head, the ids that land on XCD x take one contiguous run of the pair
-  // table, in order; the host orders the table so that a run holds pairs of nearly
-  // equal length close in the sequence, which walk their lists in step and share that
-  // XCD's L2 (radial_build_pairs).
-  const int xcd = pid & 7;
-  int seg = 0;  // pairs of this head taken by XCDs 0 .. xcd-1
-  for (int y = 0; y < xcd; ++y)
-    seg += ((first_id + np - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
-  const int first_here = first_id + ((xcd - first_id) & 7);  // first id of this head on xcd
-  const int pair = seg + ((pid - first_here) >> 3);
   // The pair's rows. A row outside [0, nb) (the second row of an odd nb's last pair, or
   // an absent entry of the table) adds no key blocks and has no queries: -1.
   int ra = 2 * pair, rb = 2 * pair + 1;
@@ -637,9 +639,12 @@ __device__ int g_work[kCounterSlots][16];
 
 // Persistent grid: one workgroup per CU (a multiple of 8 workgroups). The hardware
 // deals workgroup ids to the 8 XCDs round-robin, so workgroup i runs on XCD i % 8 and
-// takes the items x, x + 8, x + 16, ... of its XCD x from counter x, in order, until
-// they run out; then it helps the other XCDs, taking from counters x + 1, x + 2, ...
-// (mod 8) in turn. A CU that finishes early takes the next item at once: with one
+// takes the items of its XCD x's list from counter x, in order, until they run out;
+// then it helps the other XCDs, taking from counters x + 1, x + 2, ... (mod 8) in turn.
+// A uniform batch's lists come from XCD groups (xg in FwdArgs): the XCDs form 8 / xg
+// groups of xg; group g takes the (batch, head)s g, g + 8 / xg, ... one after another,
+// and each XCD of the group one contiguous run of a head's pair table, the run rotating
+// from head to head. A varlen batch's list x holds the items x, x + 8, x + 16, ... A CU that finishes early takes the next item at once: with one
 // workgroup per item, the dispatcher left CUs idle between workgroups and the last CUs
 // finished whole items after the rest, and under the chip's power limit the XCDs run
 // at different clocks, so a fixed share per XCD left the faster ones idle at the end.
@@ -671,6 +676,9 @@ struct FwdArgs {
   // then one packed sequence of n tokens, and lse is [heads, n])
   int varlen;
   VarlenSample plan[kMaxVarlen];
+  // Uniform batches: XCDs per group (1, 2, 4 or 8), the pairs of one XCD's run of a
+  // head (ceil(npairs / xg)), and batch * heads. Set by launch_fwd.
+  int xg, run_len, bh_total;
 };
 typedef __attribute__((address_space(4))) const FwdArgs* ArgsPtr;
 
@@ -699,6 +707,9 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.items = ap->items;
   a.slot = ap->slot;
   a.varlen = ap->varlen;
+  a.xg = ap->xg;
+  a.run_len = ap->run_len;
+  a.bh_total = ap->bh_total;
   return a;
 }
 
@@ -707,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes + kListBytes];
   __shared__ int counts[9];
-  __shared__ int next_item;
+  __shared__ int next_item, next_pair;
   (void)args;
   // The arguments are read again (scalar loads from the kernel-argument segment) for
   // every item: kept in scalar registers across the item loop, they would not fit beside
@@ -726,30 +737,47 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     const FwdArgs a = load_args(ap);
     const int x = blockIdx.x & 7;
     if (tid == 0) {
-      int item = -1;
-      for (int e = lists_done; e < 8; ++e) {
+      int item = -1, pair = 0;
+      for (int e = lists_done; e < 8 && item < 0; ++e) {
         const int y = (x + e) & 7;
-        const int64_t it = y + 8 * static_cast<int64_t>(atomicAdd(&g_work[a.slot][y], 1));
-        if (it < a.items) {
-          item = static_cast<int>(it);
-          break;
+        if (a.varlen == 0) {
+          // Entry j of list y: head round h = j / run_len of XCD group y / xg takes the
+          // (batch, head) y / xg + h * (8 / xg); XCD y % xg of the group takes run
+          // (y % xg + h) % xg of its pair table. Entries past the table's end (the last
+          // run can be short) are skipped.
+          for (;;) {
+            const int j = atomicAdd(&g_work[a.slot][y], 1);
+            const int h = j / a.run_len;
+            const int bh = y / a.xg + (8 / a.xg) * h;
+            if (bh >= a.bh_total) break;  // list y is empty
+            const int p = ((y % a.xg + h) % a.xg) * a.run_len + (j - h * a.run_len);
+            if (p < a.npairs) {
+              item = bh * a.npairs + p;
+              pair = p;
+              break;
+            }
+          }
+        } else {
+          const int64_t it = y + 8 * static_cast<int64_t>(atomicAdd(&g_work[a.slot][y], 1));
+          if (it < a.items) item = static_cast<int>(it);
         }
-        lists_done = e + 1;
+        if (item < 0) lists_done = e + 1;
       }
       next_item = item;
+      next_pair = pair;
     }
     __syncthreads();  // every wave read the previous item's id before run_item's barriers
     const int item = __builtin_amdgcn_readfirstlane(next_item);
+    int pair = __builtin_amdgcn_readfirstlane(next_pair);
     if (item < 0) break;
     // The item's (batch, head), and its head's first item.
     int64_t base;
     float* lse_row = nullptr;
     const int32_t* row_ptr = a.row_ptr;
     const int32_t* pairs = a.pairs;
-    int np = a.npairs, nb = a.nb, n = a.n, first_id;
+    int nb = a.nb, n = a.n;
     if (a.varlen == 0) {
-      const int bh = item / np;
-      first_id = bh * np;
+      const int bh = item / a.npairs;
       const int b = bh / a.heads, h = bh - b * a.heads;
       base = b * a.stride_b + h * a.stride_h;
       if (a.lse != nullptr) lse_row = a.lse + static_cast<int64_t>(bh) * n;
@@ -763,19 +791,19 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
         else hi = mid - 1;
       }
       const int tok0 = ap->plan[lo].tok0, it0 = ap->plan[lo].it0;
-      np = ap->plan[lo].np;
+      const int np = ap->plan[lo].np;
       nb = ap->plan[lo].nb;
       n = ap->plan[lo].n;
       row_ptr += ap->plan[lo].rp0;
       if (pairs != nullptr) pairs += 2 * ap->plan[lo].pr0;
       const int h = (item - it0) / np;
-      first_id = it0 + h * np;
+      pair = varlen_pair(item, it0 + h * np, np);
       base = static_cast<int64_t>(tok0) * a.stride_s + h * a.stride_h;
       if (a.lse != nullptr) lse_row = a.lse + static_cast<int64_t>(h) * a.n + tok0;
     }
-    run_item<D, E>(item, first_id, tid, smem, counts, a.q + base, a.k + base, a.v + base,
-                   a.o + base, lse_row, row_ptr, a.col_idx, pairs, np, nb, n, a.c, a.stride_s,
-                   a.elem_s, a.elem_gw, a.elem_w0, &ap->rule);
+    run_item<D, E>(pair, tid, smem, counts, a.q + base, a.k + base, a.v + base, a.o + base,
+                   lse_row, row_ptr, a.col_idx, pairs, nb, n, a.c, a.stride_s, a.elem_s,
+                   a.elem_gw, a.elem_w0, &ap->rule);
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -846,6 +874,10 @@ struct EagerSlots {
 EagerSlots g_eager[kMaxDevices];
 std::atomic<uint32_t> g_next_capture_slot{0};
 
+// Bytes of K and V that the heads in flight of a uniform batch may hold: about half of
+// the 256 MB Infinity Cache.
+constexpr int64_t kKvInFlight = int64_t(160) << 20;
+
 // The launch shared by the uniform and the varlen entry points: a persistent grid of one
 // workgroup per CU (a multiple of 8, at most one per item) and a counter slot.
 int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, void* stream) {
@@ -856,6 +888,20 @@ int32_t launch_fwd(FwdArgs& args, int64_t items, int head_dim, void* stream) {
   hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   if (st != nullptr && hipStreamIsCapturing(st, &capture) != hipSuccess) return RADIAL_ERR_HIP;
   args.items = static_cast<int>(items);
+  if (args.varlen == 0) {
+    // XCD groups: the smallest xg (XCDs per group) whose 8 / xg heads in flight keep
+    // their K and V within kKvInFlight bytes of the Infinity Cache, with a head for every
+    // group. Small heads then run one per XCD (each XCD's L2 serves one head, and every
+    // XCD ends on the shortest pairs of its last head); large ones are shared by several
+    // XCDs, so that the K and V in flight still fit the Infinity Cache.
+    const int64_t bh = items / args.npairs;
+    const int64_t kv = int64_t(4) * args.n * head_dim;  // bytes of one head's K and V
+    int xg = 1;
+    while (xg < 8 && ((8 / xg) * kv > kKvInFlight || 8 / xg > bh)) xg *= 2;
+    args.xg = xg;
+    args.run_len = (args.npairs + xg - 1) / xg;
+    args.bh_total = static_cast<int>(bh);
+  }
   if (capture == hipStreamCaptureStatusActive) {
     const uint32_t turn = g_next_capture_slot.fetch_add(1, std::memory_order_relaxed);
     args.slot = static_cast<int>(kEagerSlots + turn % kEagerSlots);

@@ -118,8 +118,9 @@ extern "C" int32_t radial_build_pairs(int32_t nb, const int32_t* row_ptr, const 
     out.push_back(waiting);
     out.push_back(-1);
   }
-  // The order of the table is the order the kernel takes the pairs in: the items of one
-  // head are dealt out to the 8 XCDs in contiguous runs of the table. Pairs are ordered
+  // The order of the table is the order the kernel takes the pairs in: each XCD takes a
+  // head's pairs in contiguous runs of the table (the whole table, or one of 2, 4 or 8
+  // runs when several XCDs share a head). Pairs are ordered
   // by their union length in bands of kBand key blocks, longest band first, and by
   // first row within a band. A run then holds pairs of nearly equal length that are
   // close in the sequence: the workgroups of an XCD start them together, walk their

@@ -131,11 +131,11 @@ int32_t radial_build_mask_grid(int32_t frames, int32_t grid_h, int32_t grid_w, i
  *            (a, -1) for a row that runs alone. Every row of [0, nb) appears exactly
  *            once. The pairs come in the order the kernel should take them: by the
  *            length of their union (the number of distinct key blocks of the two rows)
- *            in bands of 16 blocks, longest band first, and by a within a band. The
- *            kernel deals each head's pairs to the 8 XCDs in contiguous runs of the
- *            table, so a run holds pairs of nearly equal length close in the sequence,
- *            whose workgroups walk their lists in step and share K/V tiles in that
- *            XCD's L2.
+ *            in bands of 16 blocks, longest band first, and by a within a band. Each
+ *            XCD takes a head's pairs in contiguous runs of the table (the whole table,
+ *            or one of 2, 4 or 8 runs when XCDs share a head), so the pairs it runs at
+ *            once have nearly equal length and lie close in the sequence: their
+ *            workgroups walk their lists in step and share K/V tiles in that XCD's L2.
  * npairs_out: receives the pair count, between ceil(nb / 2) and nb (ceil(nb / 2) unless
  *            rows are left alone).
  * Cost: about 18 * nnz merge steps. Above 2^28 steps (dense masks of many thousand
