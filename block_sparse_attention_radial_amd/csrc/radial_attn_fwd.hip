@@ -435,19 +435,6 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
   __builtin_amdgcn_s_setprio(0);
 }
 
-// The pair that item `pid` of a varlen sample's head works on, the head's items being
-// the ids [first_id, first_id + np). Item ids are taken by the XCDs round-robin (XCD =
-// id % 8), in id order on each XCD (see radial_fwd_kernel); the ids of the head that land
-// on XCD x take one contiguous run of its pair table, in order.
-__device__ __forceinline__ int varlen_pair(int pid, int first_id, int np) {
-  const int xcd = pid & 7;
-  int seg = 0;  // pairs of this head taken by XCDs 0 .. xcd-1
-  for (int y = 0; y < xcd; ++y)
-    seg += ((first_id + np - 1 - y) >> 3) - ((first_id - 1 - y) >> 3);
-  const int first_here = first_id + ((xcd - first_id) & 7);  // first id of this head on xcd
-  return seg + ((pid - first_here) >> 3);
-}
-
 // One work item: the two query-block rows of pair `pair` (from the pair table, or 2p and
 // 2p+1) of one (batch, head). q, k, v, o point at row 0 of this (batch, head), lse (if
 // not null) at its row 0's entry. smem holds two K and two V buffers at fixed offsets,
@@ -641,19 +628,20 @@ __device__ int g_work[kCounterSlots][16];
 // deals workgroup ids to the 8 XCDs round-robin, so workgroup i runs on XCD i % 8 and
 // takes the items of its XCD x's list from counter x, in order, until they run out;
 // then it helps the other XCDs, taking from counters x + 1, x + 2, ... (mod 8) in turn.
-// A uniform batch's lists come from XCD groups (xg in FwdArgs): the XCDs form 8 / xg
-// groups of xg; group g takes the (batch, head)s g, g + 8 / xg, ... one after another,
-// and each XCD of the group one contiguous run of a head's pair table, the run rotating
-// from head to head. A varlen batch's list x holds the items x, x + 8, x + 16, ... A CU that finishes early takes the next item at once: with one
+// The lists come from XCD groups (xg in FwdArgs): the XCDs form 8 / xg groups of xg;
+// group g takes the (batch, head)s g, g + 8 / xg, ... one after another (for a varlen
+// batch: those heads of sample 0, then of sample 1, ...), and each XCD of the group one
+// contiguous run of a head's pair table, the run rotating from head to head. A CU that finishes early takes the next item at once: with one
 // workgroup per item, the dispatcher left CUs idle between workgroups and the last CUs
 // finished whole items after the rest, and under the chip's power limit the XCDs run
 // at different clocks, so a fixed share per XCD left the faster ones idle at the end.
 // The last workgroup to finish resets the counters.
 // One sample of a varlen batch: its first token in the packed sequence, its tokens and
 // query blocks, where its row_ptr array starts in the concatenated one, where its pairs
-// start in the concatenated pair table, its pair count, and its first work item.
+// start in the concatenated pair table, its pair count, its first work item, and its
+// first entry in every XCD's list.
 struct VarlenSample {
-  int tok0, n, nb, rp0, pr0, np, it0, pad;
+  int tok0, n, nb, rp0, pr0, np, it0, lo;
 };
 constexpr int kMaxVarlen = 64;
 
@@ -676,9 +664,10 @@ struct FwdArgs {
   // then one packed sequence of n tokens, and lse is [heads, n])
   int varlen;
   VarlenSample plan[kMaxVarlen];
-  // Uniform batches: XCDs per group (1, 2, 4 or 8), the pairs of one XCD's run of a
-  // head (ceil(npairs / xg)), and batch * heads. Set by launch_fwd.
-  int xg, run_len, bh_total;
+  // XCDs per group (1, 2, 4 or 8); for a uniform batch the pairs of one XCD's run of a
+  // head (ceil(npairs / xg)) and batch * heads, for a varlen batch the entries of every
+  // XCD's list.
+  int xg, run_len, bh_total, list_len;
 };
 typedef __attribute__((address_space(4))) const FwdArgs* ArgsPtr;
 
@@ -710,6 +699,7 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.xg = ap->xg;
   a.run_len = ap->run_len;
   a.bh_total = ap->bh_total;
+  a.list_len = ap->list_len;
   return a;
 }
 
@@ -758,8 +748,27 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
             }
           }
         } else {
-          const int64_t it = y + 8 * static_cast<int64_t>(atomicAdd(&g_work[a.slot][y], 1));
-          if (it < a.items) item = static_cast<int>(it);
+          // Entry j of list y: sample s, the last whose first list entry lo is at most j
+          // (plan read with scalar loads); head round h = (j - lo) / run of it, as above,
+          // with the sample's run length.
+          for (;;) {
+            const int j = atomicAdd(&g_work[a.slot][y], 1);
+            if (j >= a.list_len) break;  // list y is empty
+            int lo = 0, hi = a.varlen - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (ap->plan[mid].lo <= j) lo = mid;
+              else hi = mid - 1;
+            }
+            const int np = ap->plan[lo].np, run = (np + a.xg - 1) / a.xg;
+            const int r = j - ap->plan[lo].lo, h = r / run;
+            const int p = ((y % a.xg + h) % a.xg) * run + (r - h * run);
+            if (p < np) {
+              item = ap->plan[lo].it0 + (y / a.xg + (8 / a.xg) * h) * np + p;
+              pair = p;
+              break;
+            }
+          }
         }
         if (item < 0) lists_done = e + 1;
       }
@@ -768,7 +777,7 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     }
     __syncthreads();  // every wave read the previous item's id before run_item's barriers
     const int item = __builtin_amdgcn_readfirstlane(next_item);
-    int pair = __builtin_amdgcn_readfirstlane(next_pair);
+    const int pair = __builtin_amdgcn_readfirstlane(next_pair);
     if (item < 0) break;
     // The item's (batch, head), and its head's first item.
     int64_t base;
@@ -797,7 +806,6 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
       row_ptr += ap->plan[lo].rp0;
       if (pairs != nullptr) pairs += 2 * ap->plan[lo].pr0;
       const int h = (item - it0) / np;
-      pair = varlen_pair(item, it0 + h * np, np);
       base = static_cast<int64_t>(tok0) * a.stride_s + h * a.stride_h;
       if (a.lse != nullptr) lse_row = a.lse + static_cast<int64_t>(h) * a.n + tok0;
     }
@@ -959,7 +967,7 @@ int32_t launch_varlen(FwdArgs& args, const int32_t* tokens, int32_t batch,
                       const int32_t* pairs, const int32_t* npairs, int32_t heads,
                       int32_t head_dim, void* stream) {
   const bool rule = args.rule.s > 0;
-  int64_t tok = 0, rows = 0, prs = 0, items = 0;
+  int64_t tok = 0, rows = 0, prs = 0, items = 0, max_n = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t n = tokens[b];
     if (n <= 0) return RADIAL_ERR_INVALID_ARG;
@@ -975,9 +983,24 @@ int32_t launch_varlen(FwdArgs& args, const int32_t* tokens, int32_t batch,
     rows += nb + 1;
     prs += np;
     items += static_cast<int64_t>(heads) * np;
+    max_n = std::max<int64_t>(max_n, n);
   }
   if (tok > INT32_MAX || items > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
   args.n = static_cast<int>(tok);  // the packed sequence; lse is [heads, n]
+  // XCD groups as for a uniform batch (launch_fwd), sized by the longest sample, with
+  // the same number of each sample's heads for every group. Every XCD's list then holds
+  // heads / (8 / xg) runs of each sample, sample by sample.
+  int xg = 1;
+  const int64_t kv = int64_t(4) * max_n * head_dim;
+  while (xg < 8 && ((8 / xg) * kv > kKvInFlight || heads % (8 / xg) != 0)) xg *= 2;
+  int64_t entries = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    args.plan[b].lo = static_cast<int>(entries);
+    entries += static_cast<int64_t>(heads / (8 / xg)) * ((args.plan[b].np + xg - 1) / xg);
+  }
+  if (entries > INT32_MAX / 2) return RADIAL_ERR_TOO_LARGE;
+  args.xg = xg;
+  args.list_len = static_cast<int>(entries);
   return launch_fwd(args, items, head_dim, stream);
 }
 
