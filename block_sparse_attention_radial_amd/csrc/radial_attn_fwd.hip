@@ -631,11 +631,12 @@ __device__ int g_work[kCounterSlots][16];
 // The lists come from XCD groups (xg in FwdArgs): the XCDs form 8 / xg groups of xg;
 // group g takes the (batch, head)s g, g + 8 / xg, ... one after another (for a varlen
 // batch: those heads of sample 0, then of sample 1, ...), and each XCD of the group one
-// contiguous run of a head's pair table, the run rotating from head to head. A CU that finishes early takes the next item at once: with one
-// workgroup per item, the dispatcher left CUs idle between workgroups and the last CUs
-// finished whole items after the rest, and under the chip's power limit the XCDs run
-// at different clocks, so a fixed share per XCD left the faster ones idle at the end.
-// The last workgroup to finish resets the counters.
+// contiguous run of a head's pair table, the run rotating from head to head. A CU that
+// finishes early takes the next item at once: with one workgroup per item, the
+// dispatcher left CUs idle between workgroups and the last CUs finished whole items
+// after the rest, and under the chip's power limit the XCDs run at different clocks, so
+// a fixed share per XCD left the faster ones idle at the end. The last workgroup to
+// finish resets the counters.
 // One sample of a varlen batch: its first token in the packed sequence, its tokens and
 // query blocks, where its row_ptr array starts in the concatenated one, where its pairs
 // start in the concatenated pair table, its pair count, its first work item, and its
@@ -779,7 +780,7 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     const int item = __builtin_amdgcn_readfirstlane(next_item);
     const int pair = __builtin_amdgcn_readfirstlane(next_pair);
     if (item < 0) break;
-    // The item's (batch, head), and its head's first item.
+    // The item's (batch, head), or its sample and head.
     int64_t base;
     float* lse_row = nullptr;
     const int32_t* row_ptr = a.row_ptr;
