@@ -69,6 +69,8 @@ SMALL = [
     ("single-token", 1, 1, 64, 1, 1, 1, 1.0),
     ("two-blocks-1-tail", 1, 1, 128, 1, 129, 1, 1.0),
     ("wide-values", 1, 2, 128, 4, 500, 300, 4.0),
+    # 12 (batch, head)s: one XCD per head, four XCDs with two heads and four with one
+    ("twelve-heads", 3, 4, 64, 5, 700, 200, 1.0),
 ]
 
 

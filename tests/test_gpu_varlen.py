@@ -39,6 +39,9 @@ CASES = [
     ([5, 12, 1, 7], 1000, 300, 3, 64, False, False, "thd"),
     ([6, 2, 9], 300, 40, 2, 128, True, True, "htd"),
     ([4], 256, 256, 1, 64, True, False, "thd"),
+    # heads in multiples of 8 and of 4: the XCD groups of one and two XCDs per head
+    ([5, 12, 1, 7], 1000, 300, 8, 64, True, False, "thd"),
+    ([3, 9, 2], 600, 150, 4, 128, False, True, "htd"),
 ]
 
 
