@@ -82,9 +82,10 @@ typedef __attribute__((address_space(4))) const int32_t ConstI32;
 typedef __attribute__((address_space(3))) volatile int LdsFlag;
 
 // Where a dq or dkdv workgroup works: the (batch, head) element offset, its rows of
-// lse2 and delta, its mask rows (row_ptr / col_ptr point at its sample's), its sequence length
-// and block count, and its block. Varlen plans are read from the kernel-argument segment
-// (scalar loads; a copy of the plan would go to scratch memory under a dynamic index).
+// lse2 and delta, its mask rows (row_ptr / col_ptr point at its sample's), its sequence
+// length and block count, and its block. Varlen plans are read from the kernel-argument
+// segment (scalar loads; a copy of the plan would go to scratch memory under a dynamic
+// index).
 struct BwdGeometry {
   int64_t base;
   const float* lse2;
