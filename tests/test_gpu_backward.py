@@ -292,3 +292,29 @@ def test_backward_full_size_sampled_element(wlname):
     check(dq, ref[0], rows=rows_q)
     check(dk, ref[1], rows=rows_k)
     check(dv, ref[2], rows=rows_k)
+
+
+@pytest.mark.parametrize("wlname", ["hunyuan", "long4x"])
+def test_backward_full_size_sampled_large(wlname):
+    """The two large workloads at full size, one head: dq on sampled query blocks (the
+    first, a middle one, the ragged last) and dk, dv on the ragged last key block, whose
+    column reaches hundreds of query blocks (the oracle recomputes each of their rows in
+    full, which bounds what can be sampled)."""
+    wl = WORKLOADS[wlname]
+    q, k, v = draw_qkv(wl, seed=0, device="cuda", heads=range(1))
+    g = torch.Generator(device="cuda").manual_seed(14)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    md = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0).to("cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(q, k, v, md, lse=lse)
+    dq, dk, dv = radial.attn_bwd(q, k, v, o, do, lse, md)
+    torch.cuda.synchronize()
+    qbs, kbs = [0, wl.nb // 2, wl.nb - 1], [wl.nb - 1]
+    ref = ro.attention_backward(f64(q), f64(k), f64(v), f64(do),
+                                *oracle_csr(wl.frames, wl.tokens_per_frame, wl.w0),
+                                wl.scale, query_blocks=qbs, key_blocks=kbs)
+    rows_q = np.concatenate([np.arange(b * 128, min(wl.n, b * 128 + 128)) for b in qbs])
+    rows_k = np.arange((wl.nb - 1) * 128, wl.n)
+    check(dq, ref[0], rows=rows_q)
+    check(dk, ref[1], rows=rows_k)
+    check(dv, ref[2], rows=rows_k)
