@@ -122,6 +122,8 @@ BWD_CASES = [
     ([7, 3, 11], 300, 40, None, 2, 128, False),
     ([5, 2, 9], 300, 40, None, 2, 64, True),
     ([4, 6], 200, 9, 8, 1, 128, True),
+    # the Wan-shaped batch at full size, 8 heads (the forward's XCD groups of one XCD)
+    ([21, 16, 11, 5], 1560, 1560, None, 8, 128, False),
 ]
 
 
