@@ -288,7 +288,12 @@ def main():
                          "timings that the line otherwise carries")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--element", action="store_true",
-                    help="element masking inside the active blocks (block semantics otherwise)")
+                    help="element masking inside the active blocks (block semantics "
+                         "otherwise); the forward reads the decisions from an element "
+                         "table built once per mask, outside the timed region")
+    ap.add_argument("--element-rule", action="store_true",
+                    help="with --element, evaluate the rule in the kernel on every tile "
+                         "instead of reading an element table")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv) instead of the forward")
     ap.add_argument("--rule", action="store_true",
@@ -333,6 +338,13 @@ def main():
     mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w)
     mask_ms = (time.perf_counter() - t0) * 1e3
     mdev = mask.to(dev)
+    table_ms = None
+    if args.element and not args.element_rule and not args.rule and not args.backward:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        mdev.with_element_table()
+        torch.cuda.synchronize()
+        table_ms = (time.perf_counter() - t0) * 1e3
     if args.rule:
         if args.backward:
             print("--rule times the forward only", file=sys.stderr)
@@ -365,7 +377,8 @@ def main():
     ms = tm["mean"]
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"{'backward' if args.backward else 'sparse'}"
-        f"{' (element masking)' if args.element else ''}: {ms:.3f} ms/step "
+        f"{' (element masking' + (', table)' if table_ms is not None else ')') if args.element else ''}"
+        f": {ms:.3f} ms/step "
         f"(median {tm['median']:.3f}, min {tm['min']:.3f}), {tflops:.1f} TFLOP/s "
         f"({tflops / PEAK_BF16_TFLOPS:.1%} of peak)")
 
@@ -388,7 +401,8 @@ def main():
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
     traffic = None if args.backward or args.rule else traffic_bytes(
-        wl.name + ("-element" if args.element else ""))
+        wl.name + ("-element" if args.element else "")
+        + ("-table" if table_ms is not None else ""))
     line = result_line(args, tflops, tm, {
         "workload": wl.name, "batch": wl.batch, "heads": wl.heads,
         "head_dim": wl.head_dim, "frames": wl.frames,
@@ -398,10 +412,15 @@ def main():
         "semantics": "element" if args.element else "block",
         "pass": "backward" if args.backward else "forward",
         "mask": "rule (in-kernel)" if args.rule else "csr",
+        "element_decisions": None if not args.element else (
+            "table" if table_ms is not None else "rule (in-kernel)"),
     }, traffic=traffic, cpu=cpu)
     line["speedup_vs_dense"] = None if dense is None else round(dense["speedup"], 3)
     line["dense"] = None if dense is None else {k_: round(v_, 4) for k_, v_ in dense.items()}
     line["mask_build_ms"] = round(mask_ms, 3)
+    if table_ms is not None:
+        line["element_table_build_ms"] = round(table_ms, 3)
+        line["element_table_bytes"] = mdev.element_table.numel() * 8
 
     plain = not (args.backward or args.element or args.rule or args.no_extra)
     if plain and args.workload == "wan":

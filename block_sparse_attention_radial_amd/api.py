@@ -38,6 +38,14 @@ _SIGNATURES = {
     "radial_attn_fwd": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_element_table_bytes": (ctypes.c_int32, [ctypes.c_int64,
+                                                    ctypes.POINTER(ctypes.c_int64)]),
+    "radial_build_element_table": (ctypes.c_int32, [ctypes.c_void_p] * 2 + [
+        ctypes.c_int32, ctypes.c_int64] + [ctypes.c_int32] * 3 + [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
+    "radial_attn_fwd_element_table": (ctypes.c_int32, [ctypes.c_void_p] * 7 + [
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+        + [ctypes.c_int32] * 4 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_attn_fwd_rule": (ctypes.c_int32, [ctypes.c_void_p] * 5 + [ctypes.c_int32] * 5 + [
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 3
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
@@ -110,7 +118,10 @@ class Mask:
     `col_ptr` / `row_idx` (optional) are the transposed mask the backward pass walks;
     `transposed()` builds them when absent. `grid_w` is 0 for the 1-D spatial distance,
     or the width of the latent grid a frame is stored as (rows of grid_w tokens; the
-    spatial distance is then the Manhattan distance on the grid).
+    spatial distance is then the Manhattan distance on the grid). `element_table`
+    (optional, int64 [nnz, 256], from `with_element_table()`) holds the element rule's
+    decisions for every active block; the forward's element masking then reads them
+    instead of evaluating the rule, with the same result bit for bit.
     """
 
     row_ptr: torch.Tensor
@@ -122,6 +133,7 @@ class Mask:
     col_ptr: torch.Tensor | None = None
     row_idx: torch.Tensor | None = None
     grid_w: int = 0
+    element_table: torch.Tensor | None = None
 
     @property
     def n(self) -> int:
@@ -143,7 +155,14 @@ class Mask:
         mv = lambda t: None if t is None else t.to(device)  # noqa: E731
         return Mask(self.row_ptr.to(device), self.col_idx.to(device), self.frames,
                     self.tokens_per_frame, self.w0, mv(self.pairs), mv(self.col_ptr),
-                    mv(self.row_idx), self.grid_w)
+                    mv(self.row_idx), self.grid_w, mv(self.element_table))
+
+    def with_element_table(self) -> "Mask":
+        """This mask with element_table filled in (built on the mask's GPU when absent,
+        radial_build_element_table, on torch's current stream)."""
+        if self.element_table is None:
+            self.element_table = build_element_table(self)
+        return self
 
     def transposed(self) -> "Mask":
         """This mask with col_ptr / row_idx filled in (radial_transpose_mask, on the host,
@@ -158,6 +177,24 @@ class Mask:
             self.col_ptr = cp.to(self.device)
             self.row_idx = ri[:int(cp[-1])].to(self.device)
         return self
+
+
+def build_element_table(mask: Mask) -> torch.Tensor:
+    """The element table of a mask on the GPU (radial_build_element_table): int64
+    [nnz, 256], 2048 bytes per active block, with the decisions of element masking by the
+    mask's frame length, W0 and grid width. Asynchronous on torch's current stream."""
+    if not mask.row_ptr.is_cuda or mask.col_idx.device != mask.row_ptr.device:
+        raise ValueError("the mask must be on a GPU (Mask.to(device))")
+    elem_s, elem_w0, elem_gw = _element_args(mask, True)
+    nbytes = ctypes.c_int64(0)
+    _check("radial_element_table_bytes",
+           lib().radial_element_table_bytes(mask.nnz, ctypes.byref(nbytes)))
+    table = torch.empty(max(nbytes.value // 8, 256), dtype=torch.int64, device=mask.device)
+    stream = torch.cuda.current_stream(mask.device).cuda_stream
+    _check("radial_build_element_table", lib().radial_build_element_table(
+        mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb, mask.nnz, elem_s, elem_w0,
+        elem_gw, table.data_ptr(), table.numel() * 8, stream))
+    return table[:nbytes.value // 8].view(-1, 256)
 
 
 def _grid_rows(tokens_per_frame: int, grid_w: int | None) -> int:
@@ -291,9 +328,10 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask | Ru
     e.g. a [B, n, H, D] buffer viewed as [B, H, n, D]. `lse` (optional, fp32 [B, H, n],
     contiguous) receives the natural-log log-sum-exp of every row. `element` applies the
     radial rule to single entries inside the active blocks, with the mask's frame length,
-    W0 and distance (its grid width; block semantics otherwise). With a RuleMask the
-    kernel derives the key blocks from the rule instead of reading a CSR. The call is asynchronous on torch's current
-    stream.
+    W0 and distance (its grid width; block semantics otherwise); a Mask that carries an
+    element table (Mask.with_element_table) gives the same decisions from the table. With
+    a RuleMask the kernel derives the key blocks from the rule instead of reading a CSR.
+    The call is asynchronous on torch's current stream.
     """
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share the shape [B, H, n, D]")
@@ -333,6 +371,20 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask | Ru
             None if mask.pairs is None else mask.pairs.data_ptr(),
             0 if mask.pairs is None else mask.pairs.shape[0], float(scale), B, H, D,
             q.stride(0), q.stride(1), q.stride(2), stream))
+        return out
+    table = mask.element_table if element else None
+    if table is not None:
+        if (table.device != q.device or table.dtype != torch.int64
+                or table.numel() != 256 * mask.nnz or not table.is_contiguous()):
+            raise ValueError("mask.element_table must be the mask's contiguous int64 "
+                             "[nnz, 256] table on q's device (Mask.with_element_table)")
+        _check("radial_attn_fwd_element_table", lib().radial_attn_fwd_element_table(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(),
+            mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb,
+            None if mask.pairs is None else mask.pairs.data_ptr(),
+            0 if mask.pairs is None else mask.pairs.shape[0], float(scale), table.data_ptr(),
+            B, H, n, D, q.stride(0), q.stride(1), q.stride(2), stream))
         return out
     _check("radial_attn_fwd", lib().radial_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

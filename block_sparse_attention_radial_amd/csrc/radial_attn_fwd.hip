@@ -101,6 +101,10 @@ struct WaveState {
   // element rule (element masking only): frame length, W0 - 1, and the first query of
   // the group's row
   int es, egw, ew0m1, q0;
+  // element table (E = 3): this wave's part of the group's next table entry, and the
+  // bits of the tile in hand
+  const char* etab;
+  uint64_t ebits;
 };
 
 // This wave's quarter of the copy of key block kb (K or V) into buf.
@@ -263,7 +267,10 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
                                              bf16x8 (&pk)[8], Hook&& hook) {
   // Keys at or past n (only in the last key block) are padding.
   if (w.n - kb * kBlock < kBlock) pad_mask_tile(kb * kBlock, w.n, w.lane, sacc);
-  if constexpr (E != 0) element_mask<D, E>(w, kb, sacc);
+  if constexpr (E == 3)
+    element_mask_stored(w.ebits, sacc);
+  else if constexpr (E != 0)
+    element_mask<D, E>(w, kb, sacc);
   if (w.first) {
     if constexpr (E != 0) {
       const float tm = tile_max(w, sacc);
@@ -290,6 +297,12 @@ __device__ __forceinline__ void softmax_tile(WaveState<D>& w, int kb, f32x16 (&s
 
 // Most marking steps per row that radial_attn_fwd_rule accepts.
 constexpr int64_t kMaxRuleSteps = 1 << 16;
+
+typedef __attribute__((address_space(1))) const uint64_t GlobalU64;
+
+// Bytes of one element-table entry: the 128 x 128 decisions of an active block, 64 bits
+// per lane of each of the four query waves (element_mask_stored's layout).
+constexpr int kTableEntryBytes = 2048;
 
 // Union-list entry bits.
 constexpr uint32_t kInA = 1u << 14, kInB = 1u << 15, kKbMask = kInA - 1;
@@ -406,6 +419,20 @@ __device__ __forceinline__ void run_group(WaveState<D>& w, const uint16_t* list,
     const bool prev_mine = (e_prev & kMine) != 0;  // e_prev = 0 for t = 0
     const bool cur_mine = t < U && (e_cur & kMine) != 0;
     f32x16 sacc[4];  // S(t)
+    if constexpr (E == 3) {
+      // This wave's stored bits of tile t (the next entry of the group's row), loaded
+      // under the MFMA phase. Group 1's wait for its copies at the end of the phase
+      // covers the load; group 0 has no other vector-memory load in flight.
+      if (cur_mine) {
+        // (A global load from a scalar base: a generic pointer would make it a flat load,
+        // which the LDS waits of the MFMA phase would count too.)
+        const char* entry = w.etab;
+        asm volatile("" : "+s"(entry));
+        w.ebits = *(GlobalU64*)(entry + w.lane * 8);
+        w.etab = entry + kTableEntryBytes;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // ---- MFMA phase of tile t ----
     __builtin_amdgcn_s_setprio(1);
     run_mfma(w, prev_mine, cur_mine, pick(t - 1, v0, v1), pick(t, k0, k1), pk, sacc);
@@ -448,7 +475,7 @@ __device__ __forceinline__ void run_item(
     const __bf16* __restrict__ k, const __bf16* __restrict__ v, __bf16* __restrict__ o,
     float* __restrict__ lse, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col_idx, const int32_t* __restrict__ pairs, int nb, int n,
-    float c, int stride_s, int es, int egw, int ew0, RulePtr rule) {
+    float c, int stride_s, int es, int egw, int ew0, RulePtr rule, const char* etab) {
   using T = Tile<D>;
   char* const k0 = smem;
   char* const k1 = smem + T::kBytes;
@@ -583,6 +610,15 @@ __device__ __forceinline__ void run_item(
   w.egw = egw;
   w.ew0m1 = ew0 - 1;
   w.q0 = q0;
+  if constexpr (E == 3) {
+    // The table's entries follow the CSR: entry row_ptr[r] + i is the i-th key block of
+    // row r, whose union tiles come in the same ascending order.
+    const int r = grp == 0 ? ra : rb;
+    const int first = __builtin_amdgcn_readfirstlane(r >= 0 ? row_ptr[r] : 0);
+    w.etab = etab + (static_cast<int64_t>(first) * kTableEntryBytes +
+                     w.wi * (kTableEntryBytes / 4));
+    w.ebits = ~0ull;
+  }
 
   __syncthreads();  // K(0) is in LDS
   if (grp == 0)
@@ -669,6 +705,9 @@ struct FwdArgs {
   // head (ceil(npairs / xg)) and batch * heads, for a varlen batch the entries of every
   // XCD's list.
   int xg, run_len, bh_total, list_len;
+  // element table (radial_build_element_table) for element masking from stored bits, or
+  // null
+  const uint64_t* etab;
 };
 typedef __attribute__((address_space(4))) const FwdArgs* ArgsPtr;
 
@@ -701,6 +740,7 @@ __device__ __forceinline__ FwdArgs load_args(ArgsPtr ap) {
   a.run_len = ap->run_len;
   a.bh_total = ap->bh_total;
   a.list_len = ap->list_len;
+  a.etab = ap->etab;
   return a;
 }
 
@@ -812,7 +852,7 @@ __global__ __launch_bounds__(kThreads, 1) void radial_fwd_kernel(const FwdArgs a
     }
     run_item<D, E>(pair, tid, smem, counts, a.q + base, a.k + base, a.v + base, a.o + base,
                    lse_row, row_ptr, a.col_idx, pairs, nb, n, a.c, a.stride_s, a.elem_s,
-                   a.elem_gw, a.elem_w0, &ap->rule);
+                   a.elem_gw, a.elem_w0, &ap->rule, reinterpret_cast<const char*>(a.etab));
   }
   if (wave64 + lane_id_fresh() == 0) {
     int* const ctr = g_work[ap->slot];
@@ -847,16 +887,20 @@ int cu_count() {
 // One launch of the forward kernel for these arguments (slot and item count set).
 int32_t launch_kernel(const FwdArgs& args, int64_t per_xcd, int head_dim, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>(8 * per_xcd)), block(kThreads);
-  const int mode = args.elem_s == 0 ? 0 : (args.elem_gw == 0 ? 1 : 2);
+  const int mode = args.etab != nullptr ? 3 : (args.elem_s == 0 ? 0 : (args.elem_gw == 0 ? 1 : 2));
   if (head_dim == 128) {
-    if (mode == 2)
+    if (mode == 3)
+      hipLaunchKernelGGL((radial_fwd_kernel<128, 3>), grid, block, 0, st, args);
+    else if (mode == 2)
       hipLaunchKernelGGL((radial_fwd_kernel<128, 2>), grid, block, 0, st, args);
     else if (mode == 1)
       hipLaunchKernelGGL((radial_fwd_kernel<128, 1>), grid, block, 0, st, args);
     else
       hipLaunchKernelGGL((radial_fwd_kernel<128, 0>), grid, block, 0, st, args);
   } else {
-    if (mode == 2)
+    if (mode == 3)
+      hipLaunchKernelGGL((radial_fwd_kernel<64, 3>), grid, block, 0, st, args);
+    else if (mode == 2)
       hipLaunchKernelGGL((radial_fwd_kernel<64, 2>), grid, block, 0, st, args);
     else if (mode == 1)
       hipLaunchKernelGGL((radial_fwd_kernel<64, 1>), grid, block, 0, st, args);
@@ -1005,16 +1049,51 @@ int32_t launch_varlen(FwdArgs& args, const int32_t* tokens, int32_t batch,
   return launch_fwd(args, items, head_dim, stream);
 }
 
-}  // namespace
+// Element table: one workgroup per active block (CSR entry j = blockIdx.x), one wave per
+// 32 queries. Each wave runs the in-kernel element rule (element_mask_any, E = 1 or 2)
+// on a tile of zeros and stores which entries it kept, 64 bits per lane: the decisions
+// the forward would take for this block, in the layout element_mask_stored reads. A
+// column outside [0, nb) gets no bits (the forward never visits it).
+template <int E>
+__global__ __launch_bounds__(256) void radial_element_table_kernel(
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int nb, int S,
+    int gw, int ew0m1, uint64_t* __restrict__ table) {
+  const int j = blockIdx.x;
+  // The row of entry j: the last r with row_ptr[r] <= j.
+  int lo = 0, hi = nb - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (__builtin_amdgcn_readfirstlane(row_ptr[mid]) <= j) lo = mid;
+    else hi = mid - 1;
+  }
+  const int qb = lo;
+  const int kb = __builtin_amdgcn_readfirstlane(col_idx[j]);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  uint64_t bits = 0;
+  if (static_cast<unsigned>(kb) < static_cast<unsigned>(nb)) {
+    f32x16 sacc[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) sacc[g] = f32x16{};
+    element_mask_any<E>(qb * kBlock + 32 * w, kb * kBlock, S, gw, ew0m1, lane, sacc);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (sacc[g][e] == 0.f) bits |= 1ull << (16 * g + e);
+  }
+  table[static_cast<int64_t>(j) * (kTableEntryBytes / 8) + w * 64 + lane] = bits;
+}
 
-extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
-                                   float* lse, const int32_t* row_ptr, const int32_t* col_idx,
-                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
-                                   int32_t element_tokens_per_frame, int32_t element_w0,
-                                   int32_t element_grid_w, int32_t batch, int32_t heads,
-                                   int32_t seqlen, int32_t head_dim,
-                                   int64_t stride_b, int64_t stride_h, int64_t stride_s,
-                                   void* stream) {
+// The CSR forward for radial_attn_fwd and radial_attn_fwd_element_table: etab null
+// takes the element arguments (zero frame length: block semantics), else the table.
+int32_t fwd_csr(const void* q, const void* k, const void* v, void* o, float* lse,
+                const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,
+                const int32_t* pairs, int32_t npairs, float scale,
+                int32_t element_tokens_per_frame, int32_t element_w0, int32_t element_grid_w,
+                const void* etab, int32_t batch, int32_t heads, int32_t seqlen,
+                int32_t head_dim, int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                void* stream) {
   if (!row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
   const int32_t err = check_common(q, k, v, o, heads, scale, element_tokens_per_frame,
                                    element_w0, element_grid_w, head_dim);
@@ -1023,6 +1102,7 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
   if (nb != (seqlen + kBlock - 1) / kBlock) return RADIAL_ERR_SHAPE_MISMATCH;
   if (stride_s < head_dim || stride_h < 0 || stride_b < 0) return RADIAL_ERR_INVALID_ARG;
   if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
+  if (etab != nullptr && !aligned16(etab)) return RADIAL_ERR_MISALIGNED;
   if (pairs == nullptr) npairs = (nb + 1) / 2;
   else if (npairs < (nb + 1) / 2 || npairs > nb) return RADIAL_ERR_INVALID_ARG;
   const int64_t items = static_cast<int64_t>(batch) * heads * npairs;
@@ -1035,7 +1115,68 @@ extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, 
                pairs, stride_b, stride_h, npairs, nb, heads, seqlen,
                static_cast<int>(stride_s), element_tokens_per_frame, element_grid_w,
                element_w0, MaskRule{0, 0, 0}, base2_scale(scale), 0, 0, 0, {}};
+  args.etab = static_cast<const uint64_t*>(etab);
   return launch_fwd(args, items, head_dim, stream);
+}
+
+}  // namespace
+
+extern "C" int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, const int32_t* row_ptr, const int32_t* col_idx,
+                                   int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
+                                   int32_t element_tokens_per_frame, int32_t element_w0,
+                                   int32_t element_grid_w, int32_t batch, int32_t heads,
+                                   int32_t seqlen, int32_t head_dim,
+                                   int64_t stride_b, int64_t stride_h, int64_t stride_s,
+                                   void* stream) {
+  return fwd_csr(q, k, v, o, lse, row_ptr, col_idx, nb, pairs, npairs, scale,
+                 element_tokens_per_frame, element_w0, element_grid_w, nullptr, batch, heads,
+                 seqlen, head_dim, stride_b, stride_h, stride_s, stream);
+}
+
+extern "C" int32_t radial_element_table_bytes(int64_t nnz, int64_t* bytes) {
+  if (bytes == nullptr || nnz < 0) return RADIAL_ERR_INVALID_ARG;
+  if (nnz > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  *bytes = nnz * kTableEntryBytes;
+  return RADIAL_OK;
+}
+
+extern "C" int32_t radial_build_element_table(const int32_t* row_ptr, const int32_t* col_idx,
+                                              int32_t nb, int64_t nnz,
+                                              int32_t element_tokens_per_frame,
+                                              int32_t element_w0, int32_t element_grid_w,
+                                              void* table, int64_t table_bytes,
+                                              void* stream) {
+  if (!row_ptr || !col_idx || !table) return RADIAL_ERR_INVALID_ARG;
+  if (nb <= 0 || nnz < 0) return RADIAL_ERR_INVALID_ARG;
+  if (element_tokens_per_frame == 0 ||
+      !element_args_valid(element_tokens_per_frame, element_w0, element_grid_w))
+    return RADIAL_ERR_INVALID_ARG;
+  if (nb > kMaxBlocks || nnz > INT32_MAX) return RADIAL_ERR_TOO_LARGE;
+  if (table_bytes < nnz * kTableEntryBytes) return RADIAL_ERR_CAPACITY;
+  if (!aligned16(table)) return RADIAL_ERR_MISALIGNED;
+  if (nnz == 0) return RADIAL_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(nnz)), block(256);
+  uint64_t* const t = static_cast<uint64_t*>(table);
+  if (element_grid_w == 0)
+    hipLaunchKernelGGL((radial_element_table_kernel<1>), grid, block, 0, st, row_ptr, col_idx,
+                       nb, element_tokens_per_frame, 0, element_w0 - 1, t);
+  else
+    hipLaunchKernelGGL((radial_element_table_kernel<2>), grid, block, 0, st, row_ptr, col_idx,
+                       nb, element_tokens_per_frame, element_grid_w, element_w0 - 1, t);
+  return hipGetLastError() == hipSuccess ? RADIAL_OK : RADIAL_ERR_HIP;
+}
+
+extern "C" int32_t radial_attn_fwd_element_table(
+    const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* row_ptr,
+    const int32_t* col_idx, int32_t nb, const int32_t* pairs, int32_t npairs, float scale,
+    const void* element_table, int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
+    int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream) {
+  if (element_table == nullptr) return RADIAL_ERR_INVALID_ARG;
+  return fwd_csr(q, k, v, o, lse, row_ptr, col_idx, nb, pairs, npairs, scale, 0, 0, 0,
+                 element_table, batch, heads, seqlen, head_dim, stride_b, stride_h, stride_s,
+                 stream);
 }
 
 extern "C" int32_t radial_attn_fwd_rule(const void* q, const void* k, const void* v, void* o,

@@ -385,6 +385,27 @@ __device__ __forceinline__ void element_mask_any(int own0, int ent0, int S, int 
     element_mask_tile<NG>(own0, ent0, S, ew0m1, lane, sacc);
 }
 
+// Element masking from stored bits (an element table, radial_build_element_table): bit
+// 16g + e of `bits` keeps accumulator entry (g, e) of this lane (the lanes and entries
+// of element_mask_tile), a clear bit makes it -inf. The table holds the same decisions
+// as element_mask_any, taken once per mask instead of once per tile visit. A tile that
+// every lane keeps whole is left alone.
+template <int NG = 4>
+__device__ __forceinline__ void element_mask_stored(uint64_t bits, f32x16 (&sacc)[NG]) {
+  constexpr uint64_t kAll = NG == 4 ? ~0ull : (1ull << (16 * NG)) - 1;
+  if (__builtin_amdgcn_ballot_w64((bits & kAll) != kAll) == 0) return;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint32_t word = static_cast<uint32_t>(bits >> (32 * (g >> 1)));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t keep = static_cast<uint32_t>(
+          __builtin_amdgcn_sbfe(static_cast<int>(word), 16 * (g & 1) + e, 1));
+      sacc[g][e] = __uint_as_float((keep & __float_as_uint(sacc[g][e])) | (~keep & 0xff800000u));
+    }
+  }
+}
+
 // Padding of the entries of a tile in accumulator layout: entry (g, e) of a lane is
 // token ent0 + 4 hl + 32g + 8(e/4) + e%4 (g < NG), and tokens at or past n get -inf. Applied
 // arithmetically, min(s, +inf or -inf), so that the 64 tests need no lane masks; the

@@ -230,6 +230,72 @@ int32_t radial_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int64_t stride_h, int64_t stride_s, void* stream);
 
 /*
+ * radial_element_table_bytes — size of the element table of a mask with nnz active
+ * blocks: 2048 bytes per block (its 128 x 128 element decisions, one bit each).
+ *
+ * nnz:    the CSR's number of active blocks (row_ptr[nb]), >= 0.
+ * bytes:  out (host): nnz * 2048.
+ *
+ * Errors: INVALID_ARG (null bytes, nnz < 0), TOO_LARGE (nnz above 2^31 - 1).
+ */
+int32_t radial_element_table_bytes(int64_t nnz, int64_t* bytes);
+
+/*
+ * radial_build_element_table — stores the element rule's decisions for every active block
+ * of a CSR, once per mask, so that radial_attn_fwd_element_table reads them instead of
+ * evaluating the rule on every tile it visits. The call is asynchronous on `stream` (one
+ * small kernel; the mask is static, "Radial Attention: A Breakthrough in Efficient Long
+ * Video Generation", How Radial Attention Works).
+ *
+ * The decisions are those of radial_attn_fwd's element masking with the same
+ * element_tokens_per_frame, element_w0 and element_grid_w (the rule of that page applied
+ * to single entries, with frame-major coordinates as on the radial-attention-video
+ * SKILL.md page, Step 1), taken by the same device code, so the forward from the table
+ * equals the forward with those arguments bit for bit.
+ *
+ * row_ptr, col_idx:  the block mask (device, int32, nb + 1 and nnz entries), each row's
+ *                    columns strictly ascending within [0, nb), as radial_build_mask and
+ *                    radial_build_mask_grid give. A column outside [0, nb) gets no bits.
+ * nb, nnz:           blocks per side and active blocks (row_ptr[nb], known to the host).
+ * element_tokens_per_frame, element_w0, element_grid_w: as for radial_attn_fwd's element
+ *                    masking; the frame length must be set (128 .. 2^22).
+ * table:             device, caller-owned, 16-byte aligned, at least table_bytes >=
+ *                    radial_element_table_bytes(nnz) bytes. Entry j (2048 bytes) belongs to
+ *                    CSR entry j: for the query wave w (queries 32w .. 32w + 31 of the
+ *                    block's row) and lane l, the 8 bytes at 512w + 8l hold bit 16g + e =
+ *                    whether query 32w + l % 32 meets key 32g + 8(e / 4) + 4(l / 32) + e % 4
+ *                    of the block (g < 4, e < 16; block-relative indices).
+ * stream:            a hipStream_t, or null for the default stream.
+ *
+ * Errors: INVALID_ARG (null pointer, nb <= 0, nnz < 0, element arguments radial_attn_fwd
+ * would refuse, or a zero frame length), TOO_LARGE (nb above 16352, nnz above 2^31 - 1),
+ * CAPACITY (table_bytes too small), MISALIGNED (table), HIP (the launch failed).
+ */
+int32_t radial_build_element_table(const int32_t* row_ptr, const int32_t* col_idx, int32_t nb,
+                                   int64_t nnz, int32_t element_tokens_per_frame,
+                                   int32_t element_w0, int32_t element_grid_w, void* table,
+                                   int64_t table_bytes, void* stream);
+
+/*
+ * radial_attn_fwd_element_table — radial_attn_fwd with element masking from an element
+ * table (radial_build_element_table on the same row_ptr and col_idx) instead of the
+ * element arguments. Every other argument, the scheduling state and the errors are
+ * radial_attn_fwd's; element_table (device) must be non-null and 16-byte aligned
+ * (INVALID_ARG, MISALIGNED). The output and lse equal radial_attn_fwd's with the
+ * table's element arguments bit for bit. The kernel takes the table entry of each
+ * active block by its position in the block's CSR row, so the CSR must be the one the
+ * table was built from, rows strictly ascending within [0, nb); for any other CSR the
+ * masking is unspecified (reads stay within the row's entries).
+ */
+int32_t radial_attn_fwd_element_table(const void* q, const void* k, const void* v, void* o,
+                                      float* lse, const int32_t* row_ptr,
+                                      const int32_t* col_idx, int32_t nb, const int32_t* pairs,
+                                      int32_t npairs, float scale, const void* element_table,
+                                      int32_t batch, int32_t heads, int32_t seqlen,
+                                      int32_t head_dim, int64_t stride_b, int64_t stride_h,
+                                      int64_t stride_s, void* stream);
+
+/*
  * radial_attn_fwd_rule — radial_attn_fwd with the block mask derived on the fly in the
  * kernel instead of read from a CSR. The call is asynchronous on `stream`.
  *

@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
          "radial_build_mask_grid", "radial_build_pairs", "radial_attn_fwd", "radial_attn_fwd_rule",
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
          "radial_attn_bwd_varlen", "radial_attn_fwd_varlen_rule", "radial_attn_bwd_noalloc",
-         "radial_error_string"])
+         "radial_element_table_bytes", "radial_build_element_table",
+         "radial_attn_fwd_element_table", "radial_error_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -149,6 +150,69 @@ def fwd(**kw):
 ])
 def test_attn_fwd_validation(kw, code):
     assert fwd(**kw) == code
+
+
+def test_element_table_bytes():
+    lib = radial.lib()
+    out = ctypes.c_int64(-9)
+    assert lib.radial_element_table_bytes(10, ctypes.byref(out)) == OK and out.value == 20480
+    assert lib.radial_element_table_bytes(0, ctypes.byref(out)) == OK and out.value == 0
+    assert lib.radial_element_table_bytes(-1, ctypes.byref(out)) == INVALID
+    assert lib.radial_element_table_bytes(10, None) == INVALID
+    assert lib.radial_element_table_bytes(1 << 31, ctypes.byref(out)) == TOO_LARGE
+
+
+def build_table(**kw):
+    """Call radial_build_element_table with valid-looking defaults, overridden by kw (every
+    case below fails before the launch)."""
+    a = dict(row_ptr=0x10000, col_idx=0x20000, nb=256, nnz=36720, elem_s=1560, elem_w0=1560,
+             elem_gw=0, table=0x30000, table_bytes=36720 * 2048, stream=None)
+    a.update(kw)
+    return radial.lib().radial_build_element_table(
+        a["row_ptr"], a["col_idx"], a["nb"], a["nnz"], a["elem_s"], a["elem_w0"], a["elem_gw"],
+        a["table"], a["table_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(row_ptr=None), INVALID), (dict(col_idx=None), INVALID), (dict(table=None), INVALID),
+    (dict(nb=0), INVALID), (dict(nnz=-1), INVALID),
+    # The table holds element decisions: a frame length of 128 .. 2^22 tokens is needed.
+    (dict(elem_s=0, elem_w0=0), INVALID), (dict(elem_s=100), INVALID),
+    (dict(elem_w0=0), INVALID), (dict(elem_gw=7), INVALID), (dict(elem_gw=-52), INVALID),
+    (dict(nb=16353), TOO_LARGE), (dict(nnz=1 << 31, table_bytes=1 << 50), TOO_LARGE),
+    (dict(table_bytes=36720 * 2048 - 1), CAPACITY), (dict(table=0x30008), MISALIGNED),
+])
+def test_build_element_table_validation(kw, code):
+    assert build_table(**kw) == code
+
+
+def test_build_element_table_of_no_blocks_launches_nothing():
+    assert build_table(nnz=0, table_bytes=0) == OK
+
+
+def fwd_table(**kw):
+    """Call radial_attn_fwd_element_table with valid-looking defaults, overridden by kw."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=None, row_ptr=0x50000,
+             col_idx=0x60000, nb=8, pairs=None, npairs=0, scale=0.125, table=0x70000,
+             batch=1, heads=2, seqlen=1000, head_dim=128, stride_b=2 * 1000 * 128,
+             stride_h=1000 * 128, stride_s=128, stream=None)
+    a.update(kw)
+    return radial.lib().radial_attn_fwd_element_table(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], a["row_ptr"], a["col_idx"], a["nb"],
+        a["pairs"], a["npairs"], a["scale"], a["table"], a["batch"], a["heads"], a["seqlen"],
+        a["head_dim"], a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), INVALID), (dict(table=0x70008), MISALIGNED),
+    (dict(q=None), INVALID), (dict(row_ptr=None), INVALID), (dict(nb=9), SHAPE),
+    (dict(head_dim=96), HEADDIM), (dict(scale=-1.0), INVALID), (dict(q=0x10008), MISALIGNED),
+    (dict(pairs=0x80000, npairs=3), INVALID),
+    (dict(heads=1, seqlen=16353 * 128, nb=16353, stride_h=16353 * 128 * 128,
+          stride_b=16353 * 128 * 128), TOO_LARGE),
+])
+def test_attn_fwd_element_table_validation(kw, code):
+    assert fwd_table(**kw) == code
 
 
 def test_python_wrapper_checks_before_the_library():
