@@ -292,7 +292,7 @@ def main():
                          "otherwise); the forward reads the decisions from an element "
                          "table built once per mask, outside the timed region")
     ap.add_argument("--element-rule", action="store_true",
-                    help="with --element, evaluate the rule in the kernel on every tile "
+                    help="with --element, evaluate the rule in the kernels on every tile "
                          "instead of reading an element table")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv) instead of the forward")
@@ -339,7 +339,7 @@ def main():
     mask_ms = (time.perf_counter() - t0) * 1e3
     mdev = mask.to(dev)
     table_ms = None
-    if args.element and not args.element_rule and not args.rule and not args.backward:
+    if args.element and not args.element_rule and not args.rule:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         mdev.with_element_table()

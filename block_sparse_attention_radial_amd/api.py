@@ -59,6 +59,9 @@ _SIGNATURES = {
     "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
         ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
+    "radial_attn_bwd_element_table": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
+        ctypes.c_int32, ctypes.c_float, ctypes.c_void_p] + [ctypes.c_int32] * 4
+        + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
     "radial_attn_bwd_noalloc": (ctypes.c_int32, [ctypes.c_void_p] * 13 + [
         ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
         + [ctypes.c_int64] * 3 + [ctypes.c_void_p]),
@@ -134,6 +137,7 @@ class Mask:
     row_idx: torch.Tensor | None = None
     grid_w: int = 0
     element_table: torch.Tensor | None = None
+    _symmetric: bool | None = field(default=None, repr=False, compare=False)
 
     @property
     def n(self) -> int:
@@ -156,6 +160,15 @@ class Mask:
         return Mask(self.row_ptr.to(device), self.col_idx.to(device), self.frames,
                     self.tokens_per_frame, self.w0, mv(self.pairs), mv(self.col_ptr),
                     mv(self.row_idx), self.grid_w, mv(self.element_table))
+
+    def symmetric(self) -> bool:
+        """Whether the mask equals its transpose (every radial mask does; the backward reads
+        an element table only then). Computed once, with the transposed mask."""
+        if self._symmetric is None:
+            t = self.transposed()
+            self._symmetric = bool(torch.equal(t.row_ptr.cpu(), t.col_ptr.cpu())
+                                   and torch.equal(t.col_idx.cpu(), t.row_idx.cpu()))
+        return self._symmetric
 
     def with_element_table(self) -> "Mask":
         """This mask with element_table filled in (built on the mask's GPU when absent,
@@ -403,7 +416,8 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """Gradients (dq, dk, dv) of attn_fwd for the output gradient `do`, from the forward's
     output `o` and log-sum-exp `lse` (all on the GPU; layouts as for attn_fwd). The call
     is asynchronous on torch's current stream. A RuleMask is walked as the CSR its rule
-    gives (built on the host once)."""
+    gives (built on the host once). With element masking, a symmetric Mask that carries an
+    element table gives the decisions from the table (the same ones, bit for bit)."""
     if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, do)):
         raise ValueError("q, k, v, o, do must share the shape [B, H, n, D]")
     if any(t.dtype != torch.bfloat16 for t in (q, k, v, o, do)):
@@ -428,6 +442,19 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                   for _ in range(3))
     delta = torch.empty(2, B, H, n, dtype=torch.float32, device=q.device)  # D_i, base-2 lse
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    table = mask.element_table if element else None
+    if table is not None and mask.symmetric():
+        if (table.device != q.device or table.dtype != torch.int64
+                or table.numel() != 256 * mask.nnz or not table.is_contiguous()):
+            raise ValueError("mask.element_table must be the mask's contiguous int64 "
+                             "[nnz, 256] table on q's device (Mask.with_element_table)")
+        _check("radial_attn_bwd_element_table", lib().radial_attn_bwd_element_table(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+            mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.col_ptr.data_ptr(),
+            mask.row_idx.data_ptr(), mask.nb, float(scale), table.data_ptr(), B, H, n, D,
+            q.stride(0), q.stride(1), q.stride(2), stream))
+        return dq, dk, dv
     _check("radial_attn_bwd", lib().radial_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),

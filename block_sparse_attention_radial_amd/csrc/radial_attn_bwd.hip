@@ -76,7 +76,14 @@ struct BwdArgs {
   // [heads, n].
   int varlen;
   BwdSample plan[kMaxBwdVarlen];
+  // element table (radial_build_element_table) for element masking from stored
+  // decisions, or null
+  const uint64_t* etab;
 };
+// Bytes of one element-table entry (one active block): for each of the four 32-token
+// waves of the block's row and each lane, 64 decision bits, bit 16g + e for accumulator
+// entry (g, e) of element_mask_tile's layout, as radial_build_element_table writes them.
+constexpr int kEntryBytes = 2048;
 typedef __attribute__((address_space(4))) const BwdArgs* BwdArgsPtr;
 typedef __attribute__((address_space(4))) const int32_t ConstI32;
 typedef __attribute__((address_space(3))) volatile int LdsFlag;
@@ -227,6 +234,15 @@ __device__ __forceinline__ void store_rows(__bf16* dst_row, const f32x16 (&acc)[
     }
 }
 
+// One 256-byte copy instruction: lane l's 4 bytes at byte_offset land at lds + 4 l
+// (buffer_load_dword ... lds), ordered like copy_1k.
+__device__ __forceinline__ void copy_256(const i32x4& desc, uint32_t lds, int byte_offset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(byte_offset), "s"(desc)
+               : "memory");
+}
+
 // ---- 2. dQ ----
 // Two workgroups share a CU (64 KiB of LDS and at most 256 registers per wave each), so
 // each SIMD runs two dQ waves from different workgroups and interleaves them: while one
@@ -238,9 +254,12 @@ template <int D, int E>
 __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const BwdArgs a) {
   using T = Tile<D>;
   constexpr int NDB = D / 32, NS = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * T::kBytes];
+  // K and V tiles, then (element table only) this half's decision words of the four
+  // waves, 256 bytes each, for each half parity.
+  __shared__ __attribute__((aligned(1024))) char smem[2 * T::kBytes + (E == 3 ? 2048 : 0)];
   char* const kb0 = smem;
   char* const vb0 = smem + T::kBytes;
+  char* const words = smem + 2 * T::kBytes;
 
   const BwdGeometry geo = bwd_geometry(a, blockIdx.x);
   const int nb = geo.nb, n = geo.n, qb = geo.blk;
@@ -302,6 +321,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
       copy_1k(dk_, kd + i * 1024, copy_off[i]);
       copy_1k(dv_, vd + i * 1024, copy_off[i]);
     }
+    if constexpr (E == 3) {
+      // This wave's decisions for the half: dword h of every lane's entry bits (the
+      // table entry is CSR entry r0 + t, this block's t-th key block).
+      const char* ent = reinterpret_cast<const char*>(a.etab) +
+                        (static_cast<int64_t>(r0 + t) * kEntryBytes + wi * (kEntryBytes / 4));
+      const uint32_t wd = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)words));
+      copy_256(raw_descriptor(ent, kEntryBytes / 4), wd + h * 1024 + wi * 256, lane * 8 + h * 4);
+    }
   };
   if (L > 0) copy_half(0);
 
@@ -332,6 +359,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
       lds_barrier();     // every wave's part landed, and every wave is done with the
                          // previous half, whose rows the next half now takes
       if (2 * t + h + 1 < 2 * L) copy_half(2 * t + h + 1);
+      uint32_t ew = 0;  // this lane's decisions for the half (element table)
+      if constexpr (E == 3)
+        ew = *reinterpret_cast<const uint32_t*>(words + h * 1024 + wi * 256 + lane * 4);
       // S^T = K Q^T and dP^T = V dO^T for keys 64h .. 64h + 63 (keys on M, this wave's
       // queries on N).
       f32x16 sacc[2], pacc[2];
@@ -354,10 +384,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
       }
       const int key0 = kb * kBlock + 64 * h;
       if (n_eff - key0 < 64) pad_mask_tile<2>(key0, n_eff, lane, sacc);
-      if constexpr (E != 0)
+      if constexpr (E == 3) {
+        if (valid) element_mask_stored<2>(ew, sacc);
+      } else if constexpr (E != 0) {
         if (valid)
           element_mask_any<E, 2>(q0 + 32 * wi, key0, a.elem_s, a.elem_gw, a.elem_w0 - 1, lane,
                                  sacc);
+      }
 
       // Per step u of 16 keys: P^T = 2^(c s - lse2) and dS^T = P^T (dP^T - D), packed as
       // the B operand of dQ^T += K^T dS^T (d on M, queries on N, keys contracted in
@@ -407,22 +440,14 @@ struct DkdvLds {
   static constexpr int kHalfBytes = 64 * D * 2;             // 64 rows of Q or dO
   static constexpr int kCopies = kHalfBytes / 1024 / 4;     // per P-side wave and operand
   static constexpr int kLse = 2 * kHalfBytes;               // then 64 lse, then 64 D
-  static constexpr int kSlot = 2 * kHalfBytes + 512;
+  static constexpr int kWords = kLse + 512;  // then the element table's decision words
+  static constexpr int kSlot = kWords + 1024;
   static constexpr int kExchange = 4 * kSlot;               // P: 64 queries x 128 keys, bf16
   static constexpr int kFlags = kExchange + 16384;          // one word per SIMD
   static constexpr int kBytes = kFlags + 16;
   static_assert(kCopies * 4 * 1024 == kHalfBytes, "four waves' copies must cover a half");
   static_assert(kSlot % 256 == 0, "slots keep the bank swizzle");
 };
-
-// One 256-byte copy instruction: lane l's 4 bytes at byte_offset land at lds + 4 l
-// (buffer_load_dword ... lds), ordered like copy_1k.
-__device__ __forceinline__ void copy_256(const i32x4& desc, uint32_t lds, int byte_offset) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(byte_offset), "s"(desc)
-               : "memory");
-}
 
 // acc[g] = (rows 32g .. 32g + 31 of a half tile) x B^T over all d: the row reads of
 // step s + 2 are issued beside the MFMAs of step s (one read after each MFMA), pinned
@@ -528,6 +553,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
   const int c0 = geo.col_ptr[kb];
   const int L = geo.col_ptr[kb + 1] - c0;
   const int halves = 2 * L;
+  // Element table: the decisions of (key block kb, query block) pairs are row kb's
+  // entries, in the same ascending order as the column walk when the mask is symmetric.
+  const int rk0 = E == 3 ? geo.row_ptr[kb] : 0;
+  const int rkl = E == 3 ? geo.row_ptr[kb + 1] - rk0 : 0;
   // The column's row blocks, read through the constant address space so that the
   // compiler uses scalar loads: a vector load would be waited for with vmcnt(0), which
   // also waits for the tile copies in flight.
@@ -561,11 +590,21 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
       copy_256(raw_descriptor(reinterpret_cast<const char*>(src), rows * 4),
                sb + M::kLse + w * 256, lane * 4);
     }
+    if constexpr (E == 3) {
+      // This wave's decisions for the half: dword h of every lane's entry bits (its keys
+      // are the table's queries). A walk longer than row kb (a mask that is not
+      // symmetric) copies zeros past the row's entries.
+      const char* ent = reinterpret_cast<const char*>(a.etab) +
+                        (static_cast<int64_t>(rk0 + t) * kEntryBytes + wi * (kEntryBytes / 4));
+      copy_256(raw_descriptor(ent, t < rkl ? kEntryBytes / 4 : 0), sb + M::kWords + wi * 256,
+               lane * 8 + h * 4);
+    }
   };
   // Wait for this P-side wave's copies of half p, leaving those of halves p + 1 and
   // p + 2 (issued in the two phases before) in flight where they exist.
   auto wait_half = [&](int p) {
-    constexpr int N = 2 * M::kCopies;  // per half, plus one for waves 0 and 1
+    // per half, plus one for waves 0 and 1, plus one with the element table
+    constexpr int N = 2 * M::kCopies + (E == 3 ? 1 : 0);
     if (p + 2 < halves) {
       if (w < 2) wait_copies<2 * (N + 1)>();
       else wait_copies<2 * N>();
@@ -609,15 +648,21 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void radial_bwd_dkdv_kernel(const 
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         l4[i] = *reinterpret_cast<const f32x4*>(lt + 32 * (i >> 2) + 8 * (i & 3) + 4 * hl);
+      uint32_t ew = 0;  // this lane's decisions for the half (element table)
+      if constexpr (E == 3)
+        ew = *reinterpret_cast<const uint32_t*>(qt + M::kWords + wi * 256 + lane * 4);
       // S = Q K^T for the half's 64 queries (queries on M, this wave's keys on N).
       f32x16 sacc[2];
       half_rows_times<D>(qt + rbase, rx, kf, sacc);
       const int row0 = qb * kBlock + 64 * h;
       if (n_eff - row0 < 64) pad_mask_tile<2>(row0, n_eff, lane, sacc);
-      if constexpr (E != 0)
+      if constexpr (E == 3) {
+        if (valid) element_mask_stored<2>(ew, sacc);
+      } else if constexpr (E != 0) {
         if (valid)
           element_mask_any<E, 2>(k0 + 32 * wi, row0, a.elem_s, a.elem_gw, a.elem_w0 - 1,
                                  lane, sacc);
+      }
       // P = 2^(c s - lse2) per entry (query 32g + 8(e/4) + 4hl + e%4 of the half), packed
       // as the B operands of dV^T, written for the dS wave and marked.
       bf16x8 pk[4];
@@ -704,17 +749,20 @@ void launch_bwd(const BwdArgs& args, int rows_total, int items, hipStream_t st) 
 }
 
 // The three kernels of one call, at the template instance of head_dim and the element
-// mode (none, 1-D distance, grid distance).
+// mode (none, 1-D distance, grid distance, element table).
 int32_t launch_all(const BwdArgs& args, int rows_total, int items, int head_dim,
                    int32_t element_tokens_per_frame, int32_t element_grid_w, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int mode = element_tokens_per_frame == 0 ? 0 : (element_grid_w == 0 ? 1 : 2);
+  const int mode = args.etab != nullptr ? 3
+                   : element_tokens_per_frame == 0 ? 0 : (element_grid_w == 0 ? 1 : 2);
   if (head_dim == 128) {
-    if (mode == 2) launch_bwd<128, 2>(args, rows_total, items, st);
+    if (mode == 3) launch_bwd<128, 3>(args, rows_total, items, st);
+    else if (mode == 2) launch_bwd<128, 2>(args, rows_total, items, st);
     else if (mode == 1) launch_bwd<128, 1>(args, rows_total, items, st);
     else launch_bwd<128, 0>(args, rows_total, items, st);
   } else {
-    if (mode == 2) launch_bwd<64, 2>(args, rows_total, items, st);
+    if (mode == 3) launch_bwd<64, 3>(args, rows_total, items, st);
+    else if (mode == 2) launch_bwd<64, 2>(args, rows_total, items, st);
     else if (mode == 1) launch_bwd<64, 1>(args, rows_total, items, st);
     else launch_bwd<64, 0>(args, rows_total, items, st);
   }
@@ -728,15 +776,16 @@ namespace {
 // The uniform backward: checks, then the three kernels. delta is the workspace of two
 // fp32 per row, D_i then the base-2 lse (caller-owned, or the static scratch of
 // radial_attn_bwd_noalloc); max_rows bounds batch * heads * seqlen (the rows the
-// workspace holds), or is 0 for no bound.
+// workspace holds), or is 0 for no bound. etab (an element table) replaces the element
+// arguments when not null.
 int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const float* lse, void* dq, void* dk, void* dv,
                     float* delta, int64_t max_rows, const int32_t* row_ptr,
                     const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx,
                     int32_t nb, float scale, int32_t element_tokens_per_frame,
-                    int32_t element_w0, int32_t element_grid_w, int32_t batch, int32_t heads,
-                    int32_t seqlen, int32_t head_dim, int64_t stride_b, int64_t stride_h,
-                    int64_t stride_s, void* stream) {
+                    int32_t element_w0, int32_t element_grid_w, const void* etab,
+                    int32_t batch, int32_t heads, int32_t seqlen, int32_t head_dim,
+                    int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta || !row_ptr ||
       !col_idx || !col_ptr || !row_idx)
     return RADIAL_ERR_INVALID_ARG;
@@ -751,6 +800,7 @@ int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
   for (const void* p : ptrs)
     if (!aligned(p, 16)) return RADIAL_ERR_MISALIGNED;
   if (!aligned(lse, 4) || !aligned(delta, 4)) return RADIAL_ERR_MISALIGNED;
+  if (etab != nullptr && !aligned(etab, 16)) return RADIAL_ERR_MISALIGNED;
   if ((stride_s | stride_h | stride_b) & 7) return RADIAL_ERR_MISALIGNED;
   const int64_t items = static_cast<int64_t>(batch) * heads * nb;
   const int64_t rows_total = static_cast<int64_t>(batch) * heads * seqlen;
@@ -786,6 +836,7 @@ int32_t bwd_uniform(const void* q, const void* k, const void* v, const void* o,
   args.c = base2_scale(scale);
   args.scale = scale;
   args.varlen = 0;
+  args.etab = static_cast<const uint64_t*>(etab);
   return launch_all(args, static_cast<int>(rows_total), static_cast<int>(items), head_dim,
                     element_tokens_per_frame, element_grid_w, stream);
 }
@@ -835,7 +886,20 @@ extern "C" int32_t radial_attn_bwd(const void* q, const void* k, const void* v, 
                                    int64_t stride_s, void* stream) {
   return bwd_uniform(q, k, v, o, dout, lse, dq, dk, dv, delta, 0, row_ptr, col_idx, col_ptr,
                      row_idx, nb, scale, element_tokens_per_frame, element_w0, element_grid_w,
-                     batch, heads, seqlen, head_dim, stride_b, stride_h, stride_s, stream);
+                     nullptr, batch, heads, seqlen, head_dim, stride_b, stride_h, stride_s,
+                     stream);
+}
+
+extern "C" int32_t radial_attn_bwd_element_table(
+    const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv, float* delta, const int32_t* row_ptr,
+    const int32_t* col_idx, const int32_t* col_ptr, const int32_t* row_idx, int32_t nb,
+    float scale, const void* element_table, int32_t batch, int32_t heads, int32_t seqlen,
+    int32_t head_dim, int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream) {
+  if (element_table == nullptr) return RADIAL_ERR_INVALID_ARG;
+  return bwd_uniform(q, k, v, o, dout, lse, dq, dk, dv, delta, 0, row_ptr, col_idx, col_ptr,
+                     row_idx, nb, scale, 0, 0, 0, element_table, batch, heads, seqlen,
+                     head_dim, stride_b, stride_h, stride_s, stream);
 }
 
 extern "C" int32_t radial_attn_bwd_noalloc(
@@ -857,8 +921,8 @@ extern "C" int32_t radial_attn_bwd_noalloc(
   if (err != RADIAL_OK) return err;
   return bwd_uniform(q, k, v, o, dout, lse, dq, dk, dv, delta, kScratchRows, row_ptr, col_idx,
                      col_ptr, row_idx, nb, scale, element_tokens_per_frame, element_w0,
-                     element_grid_w, batch, heads, seqlen, head_dim, stride_b, stride_h,
-                     stride_s, stream);
+                     element_grid_w, nullptr, batch, heads, seqlen, head_dim, stride_b,
+                     stride_h, stride_s, stream);
 }
 
 extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v,
@@ -913,6 +977,7 @@ extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const vo
   args.c = base2_scale(scale);
   args.scale = scale;
   args.varlen = batch;
+  args.etab = nullptr;
   int64_t tok = 0, rows = 0, wgs = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t n = seq_tokens[b];

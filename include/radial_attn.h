@@ -443,6 +443,31 @@ int32_t radial_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int64_t stride_b, int64_t stride_h, int64_t stride_s, void* stream);
 
 /*
+ * radial_attn_bwd_element_table — radial_attn_bwd with element masking from an element
+ * table (radial_build_element_table on the same row_ptr and col_idx) instead of the
+ * element arguments. Every other argument, the workspace and the errors are
+ * radial_attn_bwd's; element_table (device) must be non-null and 16-byte aligned
+ * (INVALID_ARG, MISALIGNED). The gradients equal radial_attn_bwd's with the table's
+ * element arguments bit for bit.
+ *
+ * The dq kernel takes the decisions of row block i's t-th active block from table entry
+ * row_ptr[i] + t. The dK/dV kernel walks key block j's column (col_ptr, row_idx) and,
+ * since the rule is symmetric, takes the decisions of its t-th entry from row j's t-th
+ * entry row_ptr[j] + t: the mask must be symmetric (its transpose equal to itself, as
+ * every radial mask is). For any other mask dK and dV use unspecified decisions (entries
+ * past row j's end read as all masked; reads stay within the table).
+ */
+int32_t radial_attn_bwd_element_table(const void* q, const void* k, const void* v,
+                                      const void* o, const void* dout, const float* lse,
+                                      void* dq, void* dk, void* dv, float* delta,
+                                      const int32_t* row_ptr, const int32_t* col_idx,
+                                      const int32_t* col_ptr, const int32_t* row_idx,
+                                      int32_t nb, float scale, const void* element_table,
+                                      int32_t batch, int32_t heads, int32_t seqlen,
+                                      int32_t head_dim, int64_t stride_b, int64_t stride_h,
+                                      int64_t stride_s, void* stream);
+
+/*
  * radial_attn_bwd_noalloc — radial_attn_bwd without the delta workspace argument, for
  * callers that cannot allocate device memory: code under graph capture, tight serving
  * loops, harnesses that forbid hipMalloc. The call allocates nothing: its workspace (D_i

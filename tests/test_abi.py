@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
          "radial_attn_fwd_varlen", "radial_transpose_mask", "radial_attn_bwd",
          "radial_attn_bwd_varlen", "radial_attn_fwd_varlen_rule", "radial_attn_bwd_noalloc",
          "radial_element_table_bytes", "radial_build_element_table",
-         "radial_attn_fwd_element_table", "radial_error_string"])
+         "radial_attn_fwd_element_table", "radial_attn_bwd_element_table",
+         "radial_error_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -256,6 +257,31 @@ def bwd(**kw):
 ])
 def test_attn_bwd_validation(kw, code):
     assert bwd(**kw) == code
+
+
+def bwd_table(**kw):
+    """Call radial_attn_bwd_element_table with valid-looking defaults, overridden by kw."""
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, do=0x50000, lse=0x60000,
+             dq=0x70000, dk=0x80000, dv=0x90000, delta=0xa0000, row_ptr=0xb0000,
+             col_idx=0xc0000, col_ptr=0xd0000, row_idx=0xe0000, nb=8, scale=0.125,
+             table=0xf0000, batch=1, heads=2, seqlen=1000, head_dim=128,
+             stride_b=2 * 1000 * 128, stride_h=1000 * 128, stride_s=128, stream=None)
+    a.update(kw)
+    return radial.lib().radial_attn_bwd_element_table(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+        a["delta"], a["row_ptr"], a["col_idx"], a["col_ptr"], a["row_idx"], a["nb"],
+        a["scale"], a["table"], a["batch"], a["heads"], a["seqlen"], a["head_dim"],
+        a["stride_b"], a["stride_h"], a["stride_s"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), INVALID), (dict(table=0xf0008), MISALIGNED),
+    (dict(dq=None), INVALID), (dict(col_ptr=None), INVALID), (dict(nb=9), SHAPE),
+    (dict(head_dim=96), HEADDIM), (dict(scale=float("nan")), INVALID),
+    (dict(delta=0xa0001), MISALIGNED),
+])
+def test_attn_bwd_element_table_validation(kw, code):
+    assert bwd_table(**kw) == code
 
 
 def test_transpose_mask_errors_and_a_small_case():

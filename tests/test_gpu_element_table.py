@@ -1,11 +1,12 @@
-"""Element masking from a stored element table (radial_build_element_table and
-radial_attn_fwd_element_table).
+"""Element masking from a stored element table (radial_build_element_table,
+radial_attn_fwd_element_table and radial_attn_bwd_element_table).
 
 The table must hold exactly the rule's decisions, in the layout the kernel reads: every
 stored bit of every active block is decoded here and compared with the oracle's n x n
 element mask. The forward from the table must equal the forward that evaluates the rule
 in the kernel, bit for bit (output and lse), and so inherits that path's oracle parity;
-one small case is also checked against the oracle directly.
+one small case is also checked against the oracle directly. The same holds for the
+backward pass's gradients.
 """
 import numpy as np
 import pytest
@@ -176,3 +177,59 @@ def test_python_wrapper_checks_the_table():
         radial.build_element_table(radial.build_mask(6, 300, 40))  # a CPU mask
     with pytest.raises(ValueError):
         radial.build_element_table(radial.build_mask(6, 100, 40).to("cuda"))  # frame < 128
+
+
+def bwd_both(wl, gw=None, seed=9, mask=None):
+    """Element-masked gradients evaluating the rule in the kernels and from the table,
+    on the same forward output and lse."""
+    q, k, v = (x.cuda() for x in draw_qkv(wl, seed=seed))
+    g = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+    if mask is None:
+        mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=gw)
+    mask = mask.to("cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    o = radial.attn_fwd(q, k, v, mask, lse=lse, element=True)
+    grads = []
+    for use_table in (False, True):
+        m = radial.Mask(**{**mask.__dict__, "element_table": None})
+        if use_table:
+            m.with_element_table()
+        grads.append(radial.attn_bwd(q, k, v, o, do, lse, m, element=True))
+    torch.cuda.synchronize()
+    return grads
+
+
+@pytest.mark.parametrize("name,B,H,D,F,S,w0,gw", SMALL, ids=[c[0] for c in SMALL])
+def test_table_backward_equals_rule_backward(name, B, H, D, F, S, w0, gw):
+    wl = Workload(name, B, H, D, F, S, w0, 1.0)
+    rule, table = bwd_both(wl, gw)
+    for a, b in zip(rule, table):
+        assert torch.isfinite(b.float()).all()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("key", ["wan", "wan-grid"])
+def test_table_backward_equals_rule_backward_full_size(key):
+    wl = WORKLOADS[key]
+    wl = Workload(wl.name, 1, 2, wl.head_dim, wl.frames, wl.tokens_per_frame, wl.w0, 1.0,
+                  grid_w=wl.grid_w)  # two of the 40 heads: every block of the mask
+    rule, table = bwd_both(wl, wl.grid_w)
+    for a, b in zip(rule, table):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_table_backward_of_a_mask_that_is_not_symmetric():
+    """A CSR whose transpose differs (row 0 sees every block, the others only the
+    diagonal): the forward reads the table, the backward falls back to the rule (dK/dV
+    walks columns), and everything equals the rule path."""
+    nb, F, S = 6, 4, 192
+    rows = [list(range(nb))] + [[r] for r in range(1, nb)]
+    row_ptr = torch.tensor(np.cumsum([0] + [len(r) for r in rows]), dtype=torch.int32)
+    col_idx = torch.tensor([c for r in rows for c in r], dtype=torch.int32)
+    mask = radial.Mask(row_ptr, col_idx, F, S, 50)
+    assert not mask.symmetric()
+    wl = Workload("asym", 1, 2, 128, F, S, 50, 1.0)
+    rule, table = bwd_both(wl, mask=mask)
+    for a, b in zip(rule, table):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
