@@ -171,6 +171,11 @@ def bench_varlen(args, wl, dev):
         vdev = radial.VarlenRuleMask(frames, wl.tokens_per_frame, wl.w0, wl.grid_w or 0,
                                      vmask.pairs, vmask.npairs).to(dev)
     mdevs = [m.to(dev) for m in masks]
+    if args.element and not args.element_rule and not args.rule:
+        # element decisions from tables built once, for the packed batch and the samples
+        vdev.with_element_table()
+        for m in mdevs:
+            m.with_element_table()
     total = sum(m.n for m in masks)
     q, k, v = draw_packed_qkv(total, wl.heads, wl.head_dim, wl.sigma, seed=0, device=dev)
     o = torch.empty_like(q)

@@ -55,6 +55,12 @@ _SIGNATURES = {
     "radial_attn_fwd_varlen": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32] + [
         ctypes.c_void_p] * 4 + [ctypes.c_float] + [ctypes.c_int32] * 5 + [ctypes.c_int64] * 2
         + [ctypes.c_void_p]),
+    "radial_attn_fwd_varlen_element_table": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [
+        ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_float, ctypes.c_void_p]
+        + [ctypes.c_int32] * 2 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]),
+    "radial_attn_bwd_varlen_element_table": (ctypes.c_int32, [ctypes.c_void_p] * 11 + [
+        ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_float, ctypes.c_void_p]
+        + [ctypes.c_int32] * 2 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]),
     "radial_transpose_mask": (ctypes.c_int32, [ctypes.c_int32] + [ctypes.c_void_p] * 4),
     "radial_attn_bwd": (ctypes.c_int32, [ctypes.c_void_p] * 14 + [
         ctypes.c_int32, ctypes.c_float] + [ctypes.c_int32] * 7
@@ -208,6 +214,13 @@ def build_element_table(mask: Mask) -> torch.Tensor:
         mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(), mask.nb, mask.nnz, elem_s, elem_w0,
         elem_gw, table.data_ptr(), table.numel() * 8, stream))
     return table[:nbytes.value // 8].view(-1, 256)
+
+
+def _check_table(table: torch.Tensor, nnz: int, device) -> None:
+    if (table.device != device or table.dtype != torch.int64 or table.numel() != 256 * nnz
+            or not table.is_contiguous()):
+        raise ValueError("the mask's element_table must be its contiguous int64 [nnz, 256] "
+                         "table on q's device (with_element_table)")
 
 
 def _grid_rows(tokens_per_frame: int, grid_w: int | None) -> int:
@@ -387,10 +400,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: "Mask | Ru
         return out
     table = mask.element_table if element else None
     if table is not None:
-        if (table.device != q.device or table.dtype != torch.int64
-                or table.numel() != 256 * mask.nnz or not table.is_contiguous()):
-            raise ValueError("mask.element_table must be the mask's contiguous int64 "
-                             "[nnz, 256] table on q's device (Mask.with_element_table)")
+        _check_table(table, mask.nnz, q.device)
         _check("radial_attn_fwd_element_table", lib().radial_attn_fwd_element_table(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
             None if lse is None else lse.data_ptr(),
@@ -444,10 +454,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     stream = torch.cuda.current_stream(q.device).cuda_stream
     table = mask.element_table if element else None
     if table is not None and mask.symmetric():
-        if (table.device != q.device or table.dtype != torch.int64
-                or table.numel() != 256 * mask.nnz or not table.is_contiguous()):
-            raise ValueError("mask.element_table must be the mask's contiguous int64 "
-                             "[nnz, 256] table on q's device (Mask.with_element_table)")
+        _check_table(table, mask.nnz, q.device)
         _check("radial_attn_bwd_element_table", lib().radial_attn_bwd_element_table(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
@@ -547,7 +554,8 @@ class VarlenMask:
     """The block masks of a varlen batch, concatenated as radial_attn_fwd_varlen takes
     them: sample b's row_ptr (rebased to index the concatenated col_idx) follows those of
     the samples before it, and likewise its pair table and (for the backward pass) its
-    transposed mask col_ptr / row_idx."""
+    transposed mask col_ptr / row_idx. `element_table` (optional, from
+    `with_element_table()`) is the samples' element tables concatenated likewise."""
 
     seq_tokens: list
     row_ptr: torch.Tensor
@@ -559,6 +567,8 @@ class VarlenMask:
     grid_w: int = 0
     col_ptr: torch.Tensor | None = None
     row_idx: torch.Tensor | None = None
+    element_table: torch.Tensor | None = None
+    _symmetric: bool | None = field(default=None, repr=False, compare=False)
 
     @property
     def batch(self) -> int:
@@ -569,7 +579,35 @@ class VarlenMask:
         return VarlenMask(list(self.seq_tokens), self.row_ptr.to(device), self.col_idx.to(device),
                           self.tokens_per_frame, self.w0, mv(self.pairs),
                           None if self.npairs is None else list(self.npairs), self.grid_w,
-                          mv(self.col_ptr), mv(self.row_idx))
+                          mv(self.col_ptr), mv(self.row_idx), mv(self.element_table))
+
+    def symmetric(self) -> bool:
+        """Whether every sample's mask equals its transpose (computed once)."""
+        if self._symmetric is None:
+            self._symmetric = (self.col_ptr is not None and self.row_idx is not None
+                               and bool(torch.equal(self.row_ptr.cpu(), self.col_ptr.cpu()))
+                               and bool(torch.equal(self.col_idx.cpu(), self.row_idx.cpu())))
+        return self._symmetric
+
+    def with_element_table(self) -> "VarlenMask":
+        """This batch with element_table filled in: each sample's table built on the mask's
+        GPU from its slice of the concatenated CSR, then concatenated (torch's current
+        stream)."""
+        if self.element_table is None:
+            rp = self.row_ptr.cpu()
+            tables, r0 = [], 0
+            for n in self.seq_tokens:
+                nb = (n + BLOCK - 1) // BLOCK
+                if n % self.tokens_per_frame:
+                    raise ValueError("element masking needs whole frames in every sample")
+                lo, hi = int(rp[r0]), int(rp[r0 + nb])
+                m = Mask((self.row_ptr[r0:r0 + nb + 1] - lo).contiguous(),
+                         self.col_idx[lo:hi].contiguous(), n // self.tokens_per_frame,
+                         self.tokens_per_frame, self.w0, grid_w=self.grid_w)
+                tables.append(build_element_table(m))
+                r0 += nb + 1
+            self.element_table = torch.cat(tables)
+        return self
 
 
 def concat_masks(masks: list) -> VarlenMask:
@@ -684,6 +722,15 @@ def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             q.stride(1), q.stride(0), stream))
         return out
     seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
+    table = mask.element_table if element else None
+    if table is not None:
+        _check_table(table, mask.col_idx.numel(), q.device)
+        _check("radial_attn_fwd_varlen_element_table", lib().radial_attn_fwd_varlen_element_table(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), seq, mask.batch, mask.row_ptr.data_ptr(),
+            mask.col_idx.data_ptr(), None if mask.pairs is None else mask.pairs.data_ptr(),
+            npr, float(scale), table.data_ptr(), H, D, q.stride(1), q.stride(0), stream))
+        return out
     _check("radial_attn_fwd_varlen", lib().radial_attn_fwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
         None if lse is None else lse.data_ptr(), seq, mask.batch, mask.row_ptr.data_ptr(),
@@ -726,6 +773,16 @@ def attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     delta = torch.empty(2, H, total, dtype=torch.float32, device=q.device)  # D_i, base-2 lse
     seq = (ctypes.c_int32 * mask.batch)(*mask.seq_tokens)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    table = mask.element_table if element else None
+    if table is not None and mask.symmetric():
+        _check_table(table, mask.col_idx.numel(), q.device)
+        _check("radial_attn_bwd_varlen_element_table", lib().radial_attn_bwd_varlen_element_table(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), seq,
+            mask.batch, mask.row_ptr.data_ptr(), mask.col_idx.data_ptr(),
+            mask.col_ptr.data_ptr(), mask.row_idx.data_ptr(), float(scale), table.data_ptr(),
+            H, D, q.stride(1), q.stride(0), stream))
+        return dq, dk, dv
     _check("radial_attn_bwd_varlen", lib().radial_attn_bwd_varlen(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), seq, mask.batch,

@@ -925,16 +925,18 @@ extern "C" int32_t radial_attn_bwd_noalloc(
                      stride_h, stride_s, stream);
 }
 
-extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v,
-                                          const void* o, const void* dout, const float* lse,
-                                          void* dq, void* dk, void* dv, float* delta,
-                                          const int32_t* seq_tokens, int32_t batch,
-                                          const int32_t* row_ptr, const int32_t* col_idx,
-                                          const int32_t* col_ptr, const int32_t* row_idx,
-                                          float scale, int32_t element_tokens_per_frame,
-                                          int32_t element_w0, int32_t element_grid_w,
-                                          int32_t heads, int32_t head_dim, int64_t stride_h,
-                                          int64_t stride_s, void* stream) {
+namespace {
+
+// The varlen backward for radial_attn_bwd_varlen and radial_attn_bwd_varlen_element_table:
+// etab null takes the element arguments, else the table.
+int32_t bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   float* delta, const int32_t* seq_tokens, int32_t batch,
+                   const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
+                   const int32_t* row_idx, float scale, int32_t element_tokens_per_frame,
+                   int32_t element_w0, int32_t element_grid_w, const void* etab,
+                   int32_t heads, int32_t head_dim, int64_t stride_h, int64_t stride_s,
+                   void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta || !row_ptr ||
       !col_idx || !col_ptr || !row_idx || !seq_tokens)
     return RADIAL_ERR_INVALID_ARG;
@@ -950,6 +952,7 @@ extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const vo
     if (!aligned(p, 16)) return RADIAL_ERR_MISALIGNED;
   if (!aligned(lse, 4) || !aligned(delta, 4)) return RADIAL_ERR_MISALIGNED;
   if ((stride_s | stride_h) & 7) return RADIAL_ERR_MISALIGNED;
+  if (etab != nullptr && !aligned(etab, 16)) return RADIAL_ERR_MISALIGNED;
   if (stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
 
   BwdArgs args;
@@ -977,7 +980,7 @@ extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const vo
   args.c = base2_scale(scale);
   args.scale = scale;
   args.varlen = batch;
-  args.etab = nullptr;
+  args.etab = static_cast<const uint64_t*>(etab);
   int64_t tok = 0, rows = 0, wgs = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int32_t n = seq_tokens[b];
@@ -997,4 +1000,33 @@ extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const vo
   args.lse2 = delta + heads * tok;
   return launch_all(args, static_cast<int>(heads * tok), static_cast<int>(wgs), head_dim,
                     element_tokens_per_frame, element_grid_w, stream);
+}
+
+}  // namespace
+
+extern "C" int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v,
+                                          const void* o, const void* dout, const float* lse,
+                                          void* dq, void* dk, void* dv, float* delta,
+                                          const int32_t* seq_tokens, int32_t batch,
+                                          const int32_t* row_ptr, const int32_t* col_idx,
+                                          const int32_t* col_ptr, const int32_t* row_idx,
+                                          float scale, int32_t element_tokens_per_frame,
+                                          int32_t element_w0, int32_t element_grid_w,
+                                          int32_t heads, int32_t head_dim, int64_t stride_h,
+                                          int64_t stride_s, void* stream) {
+  return bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, seq_tokens, batch, row_ptr,
+                    col_idx, col_ptr, row_idx, scale, element_tokens_per_frame, element_w0,
+                    element_grid_w, nullptr, heads, head_dim, stride_h, stride_s, stream);
+}
+
+extern "C" int32_t radial_attn_bwd_varlen_element_table(
+    const void* q, const void* k, const void* v, const void* o, const void* dout,
+    const float* lse, void* dq, void* dk, void* dv, float* delta, const int32_t* seq_tokens,
+    int32_t batch, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
+    const int32_t* row_idx, float scale, const void* element_table, int32_t heads,
+    int32_t head_dim, int64_t stride_h, int64_t stride_s, void* stream) {
+  if (element_table == nullptr) return RADIAL_ERR_INVALID_ARG;
+  return bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, delta, seq_tokens, batch, row_ptr,
+                    col_idx, col_ptr, row_idx, scale, 0, 0, 0, element_table, heads, head_dim,
+                    stride_h, stride_s, stream);
 }

@@ -1219,14 +1219,17 @@ extern "C" int32_t radial_attn_fwd_rule(const void* q, const void* k, const void
   return launch_fwd(args, items, head_dim, stream);
 }
 
-extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
-                                          float* lse, const int32_t* seq_tokens, int32_t batch,
-                                          const int32_t* row_ptr, const int32_t* col_idx,
-                                          const int32_t* pairs, const int32_t* npairs,
-                                          float scale, int32_t element_tokens_per_frame,
-                                          int32_t element_w0, int32_t element_grid_w,
-                                          int32_t heads, int32_t head_dim,
-                                          int64_t stride_h, int64_t stride_s, void* stream) {
+namespace {
+
+// The CSR varlen forward for radial_attn_fwd_varlen and
+// radial_attn_fwd_varlen_element_table: etab null takes the element arguments, else the
+// table (the samples' tables concatenated like their CSRs).
+int32_t fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int32_t* seq_tokens, int32_t batch, const int32_t* row_ptr,
+                   const int32_t* col_idx, const int32_t* pairs, const int32_t* npairs,
+                   float scale, int32_t element_tokens_per_frame, int32_t element_w0,
+                   int32_t element_grid_w, const void* etab, int32_t heads, int32_t head_dim,
+                   int64_t stride_h, int64_t stride_s, void* stream) {
   if (!row_ptr || !col_idx) return RADIAL_ERR_INVALID_ARG;
   const int32_t err = check_common(q, k, v, o, heads, scale, element_tokens_per_frame,
                                    element_w0, element_grid_w, head_dim);
@@ -1236,13 +1239,40 @@ extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const vo
   if (batch > kMaxVarlen) return RADIAL_ERR_TOO_LARGE;
   if (stride_s < head_dim || stride_h < 0) return RADIAL_ERR_INVALID_ARG;
   if ((stride_s | stride_h) & 7) return RADIAL_ERR_MISALIGNED;
+  if (etab != nullptr && !aligned16(etab)) return RADIAL_ERR_MISALIGNED;
   if (stride_s > (INT32_MAX / 2) / kBlock) return RADIAL_ERR_TOO_LARGE;
   FwdArgs args{static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, row_ptr, col_idx,
                pairs, 0, stride_h, 0, 0, heads, 0, static_cast<int>(stride_s),
                element_tokens_per_frame, element_grid_w, element_w0, MaskRule{0, 0, 0},
                base2_scale(scale), 0, 0, batch, {}};
+  args.etab = static_cast<const uint64_t*>(etab);
   return launch_varlen(args, seq_tokens, batch, pairs, npairs, heads, head_dim, stream);
+}
+
+}  // namespace
+
+extern "C" int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                                          float* lse, const int32_t* seq_tokens, int32_t batch,
+                                          const int32_t* row_ptr, const int32_t* col_idx,
+                                          const int32_t* pairs, const int32_t* npairs,
+                                          float scale, int32_t element_tokens_per_frame,
+                                          int32_t element_w0, int32_t element_grid_w,
+                                          int32_t heads, int32_t head_dim,
+                                          int64_t stride_h, int64_t stride_s, void* stream) {
+  return fwd_varlen(q, k, v, o, lse, seq_tokens, batch, row_ptr, col_idx, pairs, npairs, scale,
+                    element_tokens_per_frame, element_w0, element_grid_w, nullptr, heads,
+                    head_dim, stride_h, stride_s, stream);
+}
+
+extern "C" int32_t radial_attn_fwd_varlen_element_table(
+    const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* seq_tokens,
+    int32_t batch, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* pairs,
+    const int32_t* npairs, float scale, const void* element_table, int32_t heads,
+    int32_t head_dim, int64_t stride_h, int64_t stride_s, void* stream) {
+  if (element_table == nullptr) return RADIAL_ERR_INVALID_ARG;
+  return fwd_varlen(q, k, v, o, lse, seq_tokens, batch, row_ptr, col_idx, pairs, npairs, scale,
+                    0, 0, 0, element_table, heads, head_dim, stride_h, stride_s, stream);
 }
 
 extern "C" int32_t radial_attn_fwd_varlen_rule(

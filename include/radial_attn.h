@@ -368,6 +368,25 @@ int32_t radial_attn_fwd_varlen(const void* q, const void* k, const void* v, void
                                int64_t stride_s, void* stream);
 
 /*
+ * radial_attn_fwd_varlen_element_table — radial_attn_fwd_varlen with element masking from
+ * an element table instead of the element arguments: the samples' tables
+ * (radial_build_element_table on each sample's own mask) concatenated in sample order, so
+ * that entry j belongs to entry j of the concatenated col_idx. Every other argument and
+ * error is radial_attn_fwd_varlen's; element_table (device) must be non-null and 16-byte
+ * aligned (INVALID_ARG, MISALIGNED). The output and lse equal radial_attn_fwd_varlen's
+ * with the tables' element arguments bit for bit; the CSR rows must be strictly
+ * ascending within each sample's [0, nb), as radial_attn_fwd_element_table requires.
+ */
+int32_t radial_attn_fwd_varlen_element_table(const void* q, const void* k, const void* v,
+                                             void* o, float* lse, const int32_t* seq_tokens,
+                                             int32_t batch, const int32_t* row_ptr,
+                                             const int32_t* col_idx, const int32_t* pairs,
+                                             const int32_t* npairs, float scale,
+                                             const void* element_table, int32_t heads,
+                                             int32_t head_dim, int64_t stride_h,
+                                             int64_t stride_s, void* stream);
+
+/*
  * radial_attn_fwd_varlen_rule — radial_attn_fwd_varlen with each sample's block mask
  * derived on the fly in the kernel (as radial_attn_fwd_rule does) instead of read from a
  * CSR. The call is asynchronous on `stream`.
@@ -527,6 +546,25 @@ int32_t radial_attn_bwd_varlen(const void* q, const void* k, const void* v, cons
                                int32_t element_tokens_per_frame, int32_t element_w0,
                                int32_t element_grid_w, int32_t heads, int32_t head_dim,
                                int64_t stride_h, int64_t stride_s, void* stream);
+
+/*
+ * radial_attn_bwd_varlen_element_table — radial_attn_bwd_varlen with element masking from
+ * the concatenated element table of radial_attn_fwd_varlen_element_table. Every other
+ * argument and error is radial_attn_bwd_varlen's; element_table must be non-null and
+ * 16-byte aligned. Gradients equal radial_attn_bwd_varlen's bit for bit. As for
+ * radial_attn_bwd_element_table, every sample's mask must be symmetric (radial masks
+ * are); otherwise dK and dV use unspecified decisions, with reads inside the table.
+ */
+int32_t radial_attn_bwd_varlen_element_table(const void* q, const void* k, const void* v,
+                                             const void* o, const void* dout,
+                                             const float* lse, void* dq, void* dk, void* dv,
+                                             float* delta, const int32_t* seq_tokens,
+                                             int32_t batch, const int32_t* row_ptr,
+                                             const int32_t* col_idx, const int32_t* col_ptr,
+                                             const int32_t* row_idx, float scale,
+                                             const void* element_table, int32_t heads,
+                                             int32_t head_dim, int64_t stride_h,
+                                             int64_t stride_s, void* stream);
 
 /* radial_error_string — a static, human-readable text for a return code. */
 const char* radial_error_string(int32_t code);

@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
          "radial_attn_bwd_varlen", "radial_attn_fwd_varlen_rule", "radial_attn_bwd_noalloc",
          "radial_element_table_bytes", "radial_build_element_table",
          "radial_attn_fwd_element_table", "radial_attn_bwd_element_table",
+         "radial_attn_fwd_varlen_element_table", "radial_attn_bwd_varlen_element_table",
          "radial_error_string"])
 
 
@@ -444,3 +445,36 @@ def varlen_rule(**kw):
 def test_attn_fwd_varlen_rule_validation(kw, code):
     # Every case here fails a host check: none may reach a launch (the pointers are fake).
     assert varlen_rule(**kw) == code
+
+
+def varlen_tables(**kw):
+    """Call the two varlen element-table entry points with valid-looking defaults."""
+    import ctypes
+    a = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=0x60000, do=0x50000,
+             dq=0x70000, dk=0x80000, dv=0x90000, delta=0xa0000, seq=[1000, 300], batch=2,
+             row_ptr=0xb0000, col_idx=0xc0000, col_ptr=0xd0000, row_idx=0xe0000, pairs=None,
+             npairs=None, scale=0.125, table=0xf0000, heads=2, head_dim=128, stride_h=128,
+             stride_s=256, stream=None)
+    a.update(kw)
+    seq = None if a["seq"] is None else (ctypes.c_int32 * len(a["seq"]))(*a["seq"])
+    lib = radial.lib()
+    f = lib.radial_attn_fwd_varlen_element_table(
+        a["q"], a["k"], a["v"], a["o"], a["lse"], seq, a["batch"], a["row_ptr"], a["col_idx"],
+        a["pairs"], a["npairs"], a["scale"], a["table"], a["heads"], a["head_dim"],
+        a["stride_h"], a["stride_s"], a["stream"])
+    b = lib.radial_attn_bwd_varlen_element_table(
+        a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+        a["delta"], seq, a["batch"], a["row_ptr"], a["col_idx"], a["col_ptr"], a["row_idx"],
+        a["scale"], a["table"], a["heads"], a["head_dim"], a["stride_h"], a["stride_s"],
+        a["stream"])
+    return f, b
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(table=None), INVALID), (dict(table=0xf0004), MISALIGNED), (dict(q=None), INVALID),
+    (dict(seq=None), INVALID), (dict(batch=0), INVALID), (dict(head_dim=80), HEADDIM),
+    (dict(scale=-2.0), INVALID), (dict(stride_h=132), MISALIGNED),
+    (dict(seq=[100] * 65, batch=65), TOO_LARGE),
+])
+def test_varlen_element_table_validation(kw, code):
+    assert varlen_tables(**kw) == (code, code)

@@ -233,3 +233,80 @@ def test_table_backward_of_a_mask_that_is_not_symmetric():
     rule, table = bwd_both(wl, mask=mask)
     for a, b in zip(rule, table):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_graph_capture_of_the_table_paths():
+    """The table forward and backward captured in one graph (the table built outside it)
+    replay bit-identically, with eager rule-path calls in between."""
+    wl = Workload("narrow", 1, 2, 128, 6, 300, 40, 1.0)
+    q, k, v = (x.cuda() for x in draw_qkv(wl, seed=11))
+    g = torch.Generator(device="cuda").manual_seed(12)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    mask = radial.build_mask(6, 300, 40).to("cuda").transposed()
+    tab = radial.Mask(**{**mask.__dict__, "element_table": None}).with_element_table()
+    assert tab.symmetric()
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def work(outs, m):
+        radial.attn_fwd(q, k, v, m, out=outs[0], lse=lse, element=True)
+        for dst, src in zip(outs[1:], radial.attn_bwd(q, k, v, outs[0], do, lse, m,
+                                                       element=True)):
+            dst.copy_(src)
+
+    refs = [torch.empty_like(q) for _ in range(4)]
+    work(refs, mask)  # the rule path: the reference
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(q) for _ in range(4)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work(outs, tab)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work(outs, tab)
+    scratch = [torch.empty_like(q) for _ in range(4)]
+    for r in range(4):
+        for o in outs:
+            o.zero_()
+        graph.replay()
+        work(scratch, mask)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, refs):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), r
+
+
+VARLEN = [
+    # frames per sample, S, W0, grid width, heads, head_dim
+    ([5, 2, 7], 300, 40, None, 2, 128),
+    ([3, 6, 1], 320, 9, 20, 2, 64),
+    ([21, 16, 11, 5], 1560, 1560, None, 2, 128),  # the Wan-shaped batch, two heads
+]
+
+
+@pytest.mark.parametrize("frames,S,w0,gw,H,D", VARLEN, ids=["narrow", "grid", "wan-batch"])
+def test_varlen_table_equals_varlen_rule(frames, S, w0, gw, H, D):
+    """A packed batch: forward (output, lse) and gradients from the concatenated tables
+    equal the varlen path that evaluates the rule, bit for bit."""
+    from block_sparse_attention_radial_amd.inputs import draw_packed_qkv
+    masks = [radial.build_mask(f, S, w0, grid_w=gw) for f in frames]
+    vm = radial.concat_masks(masks).to("cuda")
+    total = sum(m.n for m in masks)
+    q, k, v = draw_packed_qkv(total, H, D, seed=21, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(22)
+    do = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    results = []
+    for use_table in (False, True):
+        m = radial.VarlenMask(**{**vm.__dict__, "element_table": None})
+        if use_table:
+            m.with_element_table()
+            assert m.element_table.shape == (vm.col_idx.numel(), 256)
+            assert m.symmetric()
+        lse = torch.empty(H, total, dtype=torch.float32, device="cuda")
+        o = radial.attn_fwd_varlen(q, k, v, m, lse=lse, element=True)
+        grads = radial.attn_bwd_varlen(q, k, v, o, do, lse, m, element=True)
+        results.append([o, lse.view(torch.int16)] + list(grads))
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(*results)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), i
