@@ -18,9 +18,10 @@
  * A 128x128 block is active iff it contains at least one allowed (query, key) pair.
  * Every real key of an active block takes part in that query block's softmax.
  * Variants: element masking (the rule applied to single entries inside the active
- * blocks), the 2-D grid distance (frames as grids of rows, |s_q - s_k| replaced by the
- * Manhattan distance between grid positions), a mask derived in the kernel instead of
- * read from a CSR, a packed batch of videos of different lengths, and the backward pass.
+ * blocks, evaluated in the kernels or read from an element table built once per mask),
+ * the 2-D grid distance (frames as grids of rows, |s_q - s_k| replaced by the Manhattan
+ * distance between grid positions), a mask derived in the kernel instead of read from a
+ * CSR, a packed batch of videos of different lengths, and the backward pass.
  *
  * Conventions for every call:
  *  - The return value is 0 (RADIAL_OK) on success or a negative RADIAL_ERR_* code.
