@@ -185,6 +185,49 @@ void attention_checks() {
   expect(radial_attn_bwd_noalloc(p, p, p, p, p, lse, p, p, p, ip, ip, ip, ip, 8, 0.1f, 0, 0, 0, 1,
                                  1, 1000, 128, 0, 0, 128, nullptr) == RADIAL_ERR_HIP,
          "bwd noalloc no GPU");
+  // The element table and its entry points.
+  int64_t bytes = -1;
+  expect(radial_element_table_bytes(3, &bytes) == RADIAL_OK && bytes == 3 * 2048, "table bytes");
+  expect(radial_element_table_bytes(-1, &bytes) == RADIAL_ERR_INVALID_ARG, "table bytes < 0");
+  expect(radial_build_element_table(ip, ip, 8, 30, 0, 0, 0, p, 30 * 2048, nullptr) ==
+             RADIAL_ERR_INVALID_ARG, "table no element");
+  expect(radial_build_element_table(ip, ip, 8, 30, 1000, 50, 0, p, 30 * 2048 - 1, nullptr) ==
+             RADIAL_ERR_CAPACITY, "table capacity");
+  expect(radial_build_element_table(ip, ip, 8, 30, 1000, 50, 0, odd, 30 * 2048, nullptr) ==
+             RADIAL_ERR_MISALIGNED, "table align");
+  expect(radial_build_element_table(ip, ip, 8, 0, 1000, 50, 0, p, 0, nullptr) == RADIAL_OK,
+         "table empty");
+  expect(radial_build_element_table(ip, ip, 8, 30, 1000, 50, 0, p, 30 * 2048, nullptr) ==
+             RADIAL_ERR_HIP, "table no GPU");
+  expect(radial_attn_fwd_element_table(p, p, p, p, nullptr, ip, ip, 8, nullptr, 0, 0.1f, nullptr,
+                                       1, 1, 1000, 128, 0, 0, 128, nullptr) ==
+             RADIAL_ERR_INVALID_ARG, "fwd table null");
+  expect(radial_attn_fwd_element_table(p, p, p, p, nullptr, ip, ip, 8, nullptr, 0, 0.1f, odd, 1,
+                                       1, 1000, 128, 0, 0, 128, nullptr) ==
+             RADIAL_ERR_MISALIGNED, "fwd table align");
+  expect(radial_attn_fwd_element_table(p, p, p, p, lse, ip, ip, 8, nullptr, 0, 0.1f, p, 1, 1,
+                                       1000, 128, 0, 0, 128, nullptr) == RADIAL_ERR_HIP,
+         "fwd table no GPU");
+  expect(radial_attn_bwd_element_table(p, p, p, p, p, lse, p, p, p, lse, ip, ip, ip, ip, 8, 0.1f,
+                                       nullptr, 1, 1, 1000, 128, 0, 0, 128, nullptr) ==
+             RADIAL_ERR_INVALID_ARG, "bwd table null");
+  expect(radial_attn_bwd_element_table(p, p, p, p, p, lse, p, p, p, lse, ip, ip, ip, ip, 8, 0.1f,
+                                       p, 1, 1, 1000, 128, 0, 0, 128, nullptr) == RADIAL_ERR_HIP,
+         "bwd table no GPU");
+  expect(radial_attn_fwd_varlen_element_table(p, p, p, p, nullptr, tokens, 2, ip, ip, nullptr,
+                                              nullptr, 0.1f, nullptr, 1, 128, 128, 128,
+                                              nullptr) == RADIAL_ERR_INVALID_ARG,
+         "varlen table null");
+  expect(radial_attn_fwd_varlen_element_table(p, p, p, p, nullptr, tokens, 2, ip, ip, nullptr,
+                                              nullptr, 0.1f, p, 1, 128, 128, 128, nullptr) ==
+             RADIAL_ERR_HIP, "varlen table no GPU");
+  expect(radial_attn_bwd_varlen_element_table(p, p, p, p, p, lse, p, p, p, lse, tokens, 2, ip,
+                                              ip, ip, ip, 0.1f, odd, 1, 128, 128, 128,
+                                              nullptr) == RADIAL_ERR_MISALIGNED,
+         "bwd varlen table align");
+  expect(radial_attn_bwd_varlen_element_table(p, p, p, p, p, lse, p, p, p, lse, tokens, 2, ip,
+                                              ip, ip, ip, 0.1f, p, 1, 128, 128, 128, nullptr) ==
+             RADIAL_ERR_HIP, "bwd varlen table no GPU");
   for (int32_t code = -8; code <= 1; ++code) expect(radial_error_string(code) != nullptr, "text");
 }
 

@@ -3,7 +3,8 @@
 tests/sanitize/host_sweep.cpp drives every C entry point through its host paths: the
 mask builders on a seeded sweep of 1-D and grid shapes (exact-size heap buffers, and a
 col_idx one entry short for the capacity error), the pair table, the transpose, and the
-argument checks of every attention entry point, which return before any HIP call (a
+argument checks of every attention and element-table entry point, which return before
+any HIP call (a
 call that passes them fails at its first HIP call here, with RADIAL_ERR_HIP). The
 library sources are compiled with the sanitizers on the host side only; the device code
 is built as usual and never runs.
