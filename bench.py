@@ -22,7 +22,9 @@ the backward pass likewise). --rule times the forward with the block mask derive
 kernel from the rule instead of read from the CSR (the same key blocks, so the same work
 is counted), also for --varlen. The default run (Wan, block semantics, forward) also
 times the HunyuanVideo and the 4x-long workloads, sparse and dense, and adds them to the
-line under "other_workloads" (--no-extra skips them).
+line under "other_workloads", and element masking at the Wan shape (1-D and grid
+distance; from the element table and with the rule in the kernel, against block
+semantics) under "element_masking" (--no-extra skips both).
 
 Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per tile per
 (batch, head). QK^T and PV each contribute 2 * 128^2 * head_dim.
@@ -435,6 +437,11 @@ def main():
         torch.cuda.empty_cache()
         line["other_workloads"] = {key: other_workload(WORKLOADS[key], dev, args)
                                    for key in ("hunyuan", "long4x")}
+        # Element masking (the rule on single entries inside the active blocks) at the
+        # Wan shape, 1-D and grid distance: block semantics, the decisions read from the
+        # element table, and the rule evaluated in the kernel, interleaved.
+        line["element_masking"] = {key: element_workload(WORKLOADS[key], dev)
+                                   for key in ("wan", "wan-grid")}
     print(json.dumps(line), flush=True)
 
 
@@ -469,6 +476,48 @@ def other_workload(wl, dev, args):
     log(f"{wl.name}: sparse {tm['mean']:.3f} ms ({tflops:.1f} TFLOP/s, "
         f"{tflops / PEAK_BF16_TFLOPS:.1%}), dense {dms:.3f} ms, speedup "
         f"{rec['speedup_vs_dense']:.2f}x (block-count ceiling {rec['block_count_ceiling']:.2f}x)")
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return rec
+
+
+def element_workload(wl, dev):
+    """Forward times of block semantics, element masking from the element table and from
+    the rule in the kernel (10 timed launches each, twice, interleaved)."""
+    import torch
+
+    import block_sparse_attention_radial_amd as radial
+    from block_sparse_attention_radial_amd.inputs import draw_qkv
+
+    mask = radial.build_mask(wl.frames, wl.tokens_per_frame, wl.w0, grid_w=wl.grid_w)
+    rule = mask.to(dev)
+    table = mask.to(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    table.with_element_table()
+    torch.cuda.synchronize()
+    build_ms = (time.perf_counter() - t0) * 1e3
+    q, k, v = draw_qkv(wl, seed=0, device=dev)
+    o = torch.empty_like(q)
+    runs = {"block": lambda: radial.attn_fwd(q, k, v, rule, out=o),
+            "element_table": lambda: radial.attn_fwd(q, k, v, table, out=o, element=True),
+            "element_rule": lambda: radial.attn_fwd(q, k, v, rule, out=o, element=True)}
+    ms = {key: [] for key in runs}
+    for _ in range(2):
+        for key, fn in runs.items():
+            ms[key].append(time_launches(fn, 10, 2)["mean"])
+    avg = {key: sum(v_) / len(v_) for key, v_ in ms.items()}
+    rec = {"block_ms": round(avg["block"], 4),
+           "element_table_ms": round(avg["element_table"], 4),
+           "element_rule_ms": round(avg["element_rule"], 4),
+           "table_overhead": round(avg["element_table"] / avg["block"] - 1, 4),
+           "rule_overhead": round(avg["element_rule"] / avg["block"] - 1, 4),
+           "table_build_ms": round(build_ms, 3),
+           "table_bytes": table.element_table.numel() * 8,
+           "grid_w": wl.grid_w, "w0": wl.w0}
+    log(f"{wl.name} element masking: block {avg['block']:.3f} ms, from the table "
+        f"{avg['element_table']:.3f} ms ({rec['table_overhead']:+.1%}), rule in the kernel "
+        f"{avg['element_rule']:.3f} ms ({rec['rule_overhead']:+.1%})")
     del q, k, v, o
     torch.cuda.empty_cache()
     return rec
