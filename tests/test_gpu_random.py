@@ -4,7 +4,9 @@ Each case draws a video shape (frames, frame length, W0, 1-D or grid distance), 
 semantics (block or element), a pair table or none, CSR or on-the-fly mask, head_dim,
 batch, heads and a storage layout, then checks the GPU output and lse against the fp64
 oracle (max-abs 2e-2, mean-abs 2e-3, lse 1e-3) and, on every third case, the gradients
-(relative bars as in test_gpu_backward). Shapes stay small enough for the oracle.
+(relative bars as in test_gpu_backward). Element masking through a CSR is also run from
+the mask's element table, which must give the same bits. Shapes stay small enough for the
+oracle.
 """
 import numpy as np
 import pytest
@@ -74,6 +76,14 @@ def test_random_case_against_oracle(seed):
     assert np.isfinite(f64(o)).all()
     assert err.max() <= 2e-2 and err.mean() <= 2e-3, (c, err.max(), err.mean())
     assert np.abs(f64(lse) - ref_lse).max() < 1e-3, c
+    table = None
+    if c["element"] and not c["rule"]:
+        table = radial.Mask(**{**md.__dict__, "element_table": None}).with_element_table()
+        lse_t = torch.empty_like(lse)
+        o_t = radial.attn_fwd(qc, kc, vc, table, lse=lse_t, element=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_t.view(torch.int16), o.view(torch.int16)), c
+        assert torch.equal(lse_t.view(torch.int32), lse.view(torch.int32)), c
     if seed % 3:
         return
     g = torch.Generator().manual_seed(seed + 7)
@@ -81,6 +91,10 @@ def test_random_case_against_oracle(seed):
     if c["bnhd"]:
         do = do.transpose(1, 2).contiguous().transpose(1, 2)
     grads = radial.attn_bwd(qc, kc, vc, o, do.cuda(), lse, md, element=c["element"])
+    if table is not None:
+        for a, b in zip(grads, radial.attn_bwd(qc, kc, vc, o, do.cuda(), lse, table,
+                                               element=True)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), c
     torch.cuda.synchronize()
     refs = ro.attention_backward(f64(q), f64(k), f64(v), f64(do), rp, ci, wl.scale,
                                  element=rule)
