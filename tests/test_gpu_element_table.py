@@ -79,9 +79,12 @@ def test_table_holds_the_oracle_element_mask(name, F, S, w0, gw):
     np.testing.assert_array_equal(cover, active.astype(np.int32))
 
 
-def fwd_both(wl, gw=None, pairs=True, seed=4, heads=None):
+def fwd_both(wl, gw=None, pairs=True, seed=4, heads=None, device_draw=False):
     """The element forward evaluating the rule in the kernel and from the table."""
-    q, k, v = (x.cuda() for x in draw_qkv(wl, seed=seed))
+    if device_draw:
+        q, k, v = draw_qkv(wl, seed=seed, device="cuda")
+    else:
+        q, k, v = (x.cuda() for x in draw_qkv(wl, seed=seed))
     if heads is not None:
         q, k, v = (x[:, heads].contiguous() for x in (q, k, v))
     B, H, n, _ = q.shape
@@ -134,12 +137,13 @@ def test_table_forward_against_oracle():
     assert np.abs(f64(lse) - ref_lse).max() < 1e-3
 
 
-@pytest.mark.parametrize("key,gw", [("wan", None), ("wan-grid", 52)], ids=["wan", "wan-grid"])
-def test_table_forward_equals_rule_forward_full_size(key, gw):
-    """The full-size Wan-shaped workloads (1-D and grid distance), all 40 heads: many
-    items per workgroup, both groups of every pair, every table entry in use."""
+@pytest.mark.parametrize("key", ["wan", "wan-grid", "hunyuan", "long4x"])
+def test_table_forward_equals_rule_forward_full_size(key):
+    """The full-size workloads (Wan 1-D and grid distance, HunyuanVideo, 4x long), every
+    head: many items per workgroup, both groups of every pair, every table entry in use
+    (up to 357,580 entries, 732 MB)."""
     wl = WORKLOADS[key]
-    ((o_rule, l_rule), (o_tab, l_tab)), _, _ = fwd_both(wl, gw=wl.grid_w)
+    ((o_rule, l_rule), (o_tab, l_tab)), _, _ = fwd_both(wl, gw=wl.grid_w, device_draw=True)
     assert torch.isfinite(l_tab).all()
     assert torch.equal(o_tab.view(torch.int16), o_rule.view(torch.int16))
     assert torch.equal(l_tab.view(torch.int32), l_rule.view(torch.int32))
