@@ -32,6 +32,7 @@ Work is counted on whole active 128x128 tiles: 4 * head_dim * 128^2 flops per ti
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -307,6 +308,9 @@ def main():
                     help="derive the block mask in the kernel from the rule (no CSR read)")
     ap.add_argument("--varlen", default="", metavar="F1,F2,...",
                     help="time a packed batch of videos with these frame counts")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="run the workload with this many heads instead of its own (e.g. one "
+                         "GPU's share when the heads are split across GPUs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale "
                          "HBM traffic counters against a kernel of known size")
@@ -336,6 +340,11 @@ def main():
         return
     radial.lib()
     wl = WORKLOADS[args.workload]
+    if args.heads:
+        if args.heads < 0:
+            print("--heads must be positive", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, heads=args.heads)
     dev = torch.device("cuda:0")
     if args.varlen:
         bench_varlen(args, wl, dev)
@@ -407,7 +416,7 @@ def main():
         cpu = cpu_baseline(wl, q, k, v, mask, args.cpu_seconds, args.element, do)
         log(f"cpu oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads; {cpu['sample']}")
 
-    traffic = None if args.backward or args.rule else traffic_bytes(
+    traffic = None if args.backward or args.rule or args.heads else traffic_bytes(
         wl.name + ("-element" if args.element else "")
         + ("-table" if table_ms is not None else ""))
     line = result_line(args, tflops, tm, {
@@ -429,7 +438,7 @@ def main():
         line["element_table_build_ms"] = round(table_ms, 3)
         line["element_table_bytes"] = mdev.element_table.numel() * 8
 
-    plain = not (args.backward or args.element or args.rule or args.no_extra)
+    plain = not (args.backward or args.element or args.rule or args.no_extra or args.heads)
     if plain and args.workload == "wan":
         # The pages' other two workloads, on the same kernel: the same line carries their
         # sparse and dense times (no CPU leg), with the ceiling that block skipping allows.
