@@ -314,3 +314,29 @@ def test_varlen_table_equals_varlen_rule(frames, S, w0, gw, H, D):
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(zip(*results)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), i
+
+
+def test_table_forward_with_random_pair_tables():
+    """Random pair tables, some rows alone (the other group of such a workgroup has no
+    row): each group counts its own row's entries, so every table gives the bits of the
+    rule path."""
+    def random_table(nb, rng, singles):
+        perm = rng.permutation(nb)
+        alone, rest = list(perm[:singles]), perm[singles:]
+        rows = [tuple(sorted(int(x) for x in rest[i:i + 2])) for i in range(0, len(rest) - 1, 2)]
+        if len(rest) % 2:
+            alone.append(rest[-1])
+        rows = sorted(rows + [(int(a), -1) for a in alone])
+        return torch.tensor(rows, dtype=torch.int32)
+
+    wl = Workload("narrow", 1, 3, 128, 6, 300, 40, 1.0)
+    q, k, v = (x.cuda() for x in draw_qkv(wl, seed=31))
+    host = radial.build_mask(6, 300, 40, pairs=False)
+    ref = radial.attn_fwd(q, k, v, host.to("cuda"), element=True)
+    rng = np.random.default_rng(5)
+    for singles in (0, 3, host.nb):
+        t = random_table(host.nb, rng, singles)
+        m = radial.Mask(host.row_ptr, host.col_idx, 6, 300, 40, t).to("cuda").with_element_table()
+        o = radial.attn_fwd(q, k, v, m, element=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16)), singles
