@@ -363,7 +363,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
       if constexpr (E == 3)
         ew = *reinterpret_cast<const uint32_t*>(words + h * 1024 + wi * 256 + lane * 4);
       // S^T = K Q^T and dP^T = V dO^T for keys 64h .. 64h + 63 (keys on M, this wave's
-      // queries on N).
+      // queries on N), at raised wave priority: the SIMD's other dQ wave (from the other
+      // workgroup) then issues its VALU work around these MFMAs rather than ahead of them.
+      __builtin_amdgcn_s_setprio(1);
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -382,6 +384,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void radial_bwd_dq_kernel(const Bwd
               vf[g], __builtin_bit_cast(bf16x8, gf[s]), s == 0 ? f32x16{} : pacc[g], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       const int key0 = kb * kBlock + 64 * h;
       if (n_eff - key0 < 64) pad_mask_tile<2>(key0, n_eff, lane, sacc);
       if constexpr (E == 3) {
