@@ -129,8 +129,9 @@ class Mask:
     or the width of the latent grid a frame is stored as (rows of grid_w tokens; the
     spatial distance is then the Manhattan distance on the grid). `element_table`
     (optional, int64 [nnz, 256], from `with_element_table()`) holds the element rule's
-    decisions for every active block; the forward's element masking then reads them
-    instead of evaluating the rule, with the same result bit for bit.
+    decisions for every active block; element masking in the forward (and, for a
+    symmetric mask, the backward) then reads them instead of evaluating the rule, with
+    the same result bit for bit.
     """
 
     row_ptr: torch.Tensor
