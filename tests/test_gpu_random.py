@@ -54,7 +54,7 @@ def draw_case(seed):
                 bnhd=bool(rng.integers(2)))
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_case_against_oracle(seed):
     c = draw_case(1000 + seed)
     wl = Workload(f"random{seed}", c["B"], c["H"], c["D"], c["F"], c["S"], c["w0"], 1.0,
